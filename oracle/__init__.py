@@ -1,0 +1,40 @@
+"""Float64 CPU oracle for draft-tree verification — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import anything under ``oracle/``. The product path (the HIP
+library and its Python binding in ``tree_attention_draft_tv_amd``) never
+imports, links or calls it, and the oracle imports nothing from the product
+path: the two share no code. Inputs come from the seeded generators in
+``workloads/``.
+
+What it computes, and where the method is defined (all on the EmbodiInfer
+pull-request page "perf(activevln): grammar-trie speculation and lossless
+throughput" unless noted):
+
+* ``tree.build_tree_mask`` — the ancestor-or-self visibility of each draft
+  node, found by following parent links (commit "feat(activevln): grammar-trie
+  tree speculation with exact acceptance": the N most likely trie nodes are
+  verified in one tree-attention forward, so each node may only see its own
+  ancestors).
+* ``attention.tree_attention`` — the plain softmax-attention definition over
+  the committed context plus the node's ancestors, with grouped-query heads
+  (commit "perf(activevln): lossless batched replay throughput options",
+  item attention_kernel="gqa"), never touching cache slots past the live
+  extent (commit "fix(attention): never read KV slots past a row's live
+  queries").
+* ``accept.accept_greedy`` — keep the argmax path (commit "feat(activevln):
+  grammar-trie tree speculation with exact acceptance").
+* ``accept.accept_sample`` — SpecInfer-style rejection sampling against the
+  draft with a residual resample (same commit; "exact SpecInfer-style
+  acceptance" in the page's summary).
+
+Every function works in float64 after decoding its inputs exactly from their
+stored float32 / bfloat16 values. Every result is pinned by tests against
+closed forms, textbook special cases and brute force (tests/test_oracle_*.py).
+"""
+
+from .accept import accept_greedy, accept_sample, sample_probs  # noqa: F401
+from .attention import tree_attention  # noqa: F401
+from .decode import decode  # noqa: F401
+from .tree import ROW_BAD_PARENT, ROW_BAD_TOKEN, ROW_CTX_BOUND, ROW_NNODES, ROW_OK  # noqa: F401
+from .tree import ancestors, build_tree_mask  # noqa: F401

@@ -1,0 +1,90 @@
+"""Tree-masked grouped-query attention, plain definition (oracle).
+
+Test infrastructure only. Follows the EmbodiInfer page "perf(activevln):
+grammar-trie speculation and lossless throughput":
+
+* commit "feat(activevln): grammar-trie tree speculation with exact
+  acceptance" — every draft node of the tree is verified in one attention
+  forward; a node sees the committed context and its own ancestors (itself
+  included), never its siblings or other branches;
+* commit "perf(activevln): lossless batched replay throughput options", item
+  attention_kernel="gqa" — query heads that share a KV head read the same
+  keys and values; here query head h reads KV head h // (Hq / Hkv);
+* commit "fix(attention): never read KV slots past a row's live queries" —
+  slots at or past ctx_len + n_nodes are never read (they may hold NaN).
+
+Split-KV with a log-sum-exp combine reaches this same result up to rounding
+order, so the oracle is the definition itself: for each live (b, i, h) the
+scores s = scale * q . k over the visible keys, o = softmax(s) @ v and
+lse = ln sum exp(s) (natural log), evaluated as max + ln sum exp(s - max).
+"""
+
+import numpy as np
+
+from .decode import decode
+from .tree import ROW_CTX_BOUND, ROW_NNODES, ROW_OK, ancestors, parents_valid
+
+
+def tree_attention(q, k, v, dtype, ctx_len, n_nodes, parent, scale,
+                   max_ctx=None, kv_capacity=None):
+    """Exact float64 tree attention.
+
+    q: [B, T, Hq, D] stored values; k, v: [B, Hkv, Lcap, D] stored values;
+    ``dtype`` is their storage type ("f32" or "bf16"); ctx_len, n_nodes:
+    int [B]; parent: int [B, T]; scale: the float32 softmax scale (used as its
+    exact float64 value). ``max_ctx`` and ``kv_capacity`` are the launch
+    bounds; a row with ctx_len > max_ctx, ctx_len < 0 or
+    ctx_len + n_nodes > kv_capacity is reported as ROW_CTX_BOUND and a row
+    with n_nodes outside [0, T] as ROW_NNODES.
+
+    Returns (out float64 [B, T, Hq, D], lse float64 [B, T, Hq], status int32
+    [B]). Padding rows (i >= n_nodes[b]) and rows whose status is not OK get
+    out = 0 and lse = -inf.
+    """
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    Lcap = k.shape[2]
+    if kv_capacity is None:
+        kv_capacity = Lcap
+    if max_ctx is None:
+        max_ctx = kv_capacity
+    G = Hq // Hkv
+    sc = np.float64(np.float32(scale))
+    out = np.zeros((B, T, Hq, D), dtype=np.float64)
+    lse = np.full((B, T, Hq), -np.inf, dtype=np.float64)
+    status = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        n = int(n_nodes[b])
+        L = int(ctx_len[b])
+        if n < 0 or n > T:
+            status[b] = ROW_NNODES
+            continue
+        if n == 0:
+            continue
+        if L < 0 or L > max_ctx or L + n > kv_capacity:
+            status[b] = ROW_CTX_BOUND
+            continue
+        if not parents_valid(parent[b], n):
+            raise ValueError("row %d: parent links are not a topologically ordered tree" % b)
+        # Visible keys of node i: the whole committed context, then the tree
+        # keys of its ancestors-or-self (tree node j lives in slot L + j).
+        visible = np.zeros((n, L + n), dtype=bool)
+        visible[:, :L] = True
+        for i in range(n):
+            for j in ancestors(parent[b], i):
+                visible[i, L + j] = True
+        for kv in range(Hkv):
+            K = decode(k[b, kv, : L + n], dtype)
+            Vv = decode(v[b, kv, : L + n], dtype)
+            for g in range(G):
+                h = kv * G + g
+                qh = decode(q[b, :n, h, :], dtype)
+                s = sc * (qh @ K.T)
+                s = np.where(visible, s, -np.inf)
+                m = s.max(axis=1, keepdims=True)
+                w = np.exp(s - m)
+                z = w.sum(axis=1)
+                out[b, :n, h, :] = (w @ Vv) / z[:, None]
+                lse[b, :n, h] = m[:, 0] + np.log(z)
+        status[b] = ROW_OK
+    return out, lse, status
