@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Benchmark of one draft-tree verification step on one MI355X.
+
+A step is the whole hot path over one batch: ancestor-mask build,
+tree-masked split-KV GQA attention (one layer) and greedy acceptance, at the
+headline workload (8 sequences of which 6 live, 28/4 heads, head_dim 128,
+bf16, contexts 4096-8192, 32-node trees, vocabulary 152064). Inputs are
+seeded synthetic tensors resident in HBM before timing starts. The timed
+loop rotates over several copies of the inputs so that the 256 MB Infinity
+Cache cannot serve a step from the previous one (cold timing).
+
+Prints one JSON line. ``value`` is verified draft nodes per second for the
+whole step; ``roofline`` reports the attention call's algorithmic HBM
+bandwidth against the 8 TB/s peak, from HIP events recorded on the stream
+the kernels run on; ``cpu_baseline`` times the float64 oracle on a bounded
+sample of the same workload on the host.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "verified draft nodes/sec + achieved HBM GB/s (B=8, 8k ctx, N=32 tree)"
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "tree_attention_draft_tv_amd", "csrc", "tv_attention.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C3", help="workload (C1..C5); C3 is the headline")
+    ap.add_argument("--sets", type=int, default=4, help="input copies rotated for cold timing")
+    ap.add_argument("--chunk", type=int, default=0, help="attention chunk_keys (0 = auto)")
+    ap.add_argument("--parts", type=int, default=1, help="probability_parts")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target host time of the oracle baseline sample")
+    ap.add_argument("--no-sampling", action="store_true",
+                    help="skip the secondary sampling-acceptance measurement")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def attention_alg_bytes(w):
+    """Bytes the attention must move: live committed + tree K and V, live
+    queries, fp32 outputs and LSE, and the mask words."""
+    elt = 2 if w.dtype == "bf16" else 4
+    tot = 0
+    for b in range(w.B):
+        n = int(w.n_nodes[b])
+        if n == 0:
+            continue
+        L = int(w.ctx_len[b])
+        tot += 2 * (L + n) * w.Hkv * w.D * elt        # K and V
+        tot += n * w.Hq * w.D * elt                   # Q
+        tot += n * w.Hq * w.D * 4 + n * w.Hq * 4      # out + lse
+        tot += n * ((w.T + 31) // 32) * 4             # mask
+    return tot
+
+
+def attention_flops(w):
+    tot = 0
+    for b in range(w.B):
+        n = int(w.n_nodes[b])
+        if n:
+            tot += 4 * w.D * w.G * n * (int(w.ctx_len[b]) + n) * w.Hkv
+    return tot
+
+
+def accept_alg_bytes(w):
+    tot = 0
+    for b in range(w.B):
+        n = int(w.n_nodes[b])
+        tot += n * w.V * 4 + n * 8 * 4  # logits rows + parent/token/outputs
+        if w.qdraft is not None:
+            tot += max(n - 1, 0) * 4  # u
+    return tot
+
+
+def kernel_source_hash():
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter runs, if the
+    kernel source is unchanged since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds):
+    """Time the float64 oracle (mask, attention, greedy acceptance) one live
+    sequence at a time until about `seconds` of host time have passed."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    live = [b for b in range(w.B) if w.n_nodes[b] > 0]
+    nodes = 0
+    seqs = 0
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        b = live[i % len(live)]
+        sl = slice(b, b + 1)
+        oracle.build_tree_mask(w.parent[sl], w.n_nodes[sl], w.T)
+        oracle.tree_attention(w.q[sl], w.k[sl], w.v[sl], w.dtype, w.ctx_len[sl], w.n_nodes[sl],
+                              w.parent[sl], w.scale)
+        if w.mode == "greedy":
+            oracle.accept_greedy(w.logits[sl], w.tokens[sl], w.parent[sl], w.n_nodes[sl])
+        else:
+            oracle.accept_sample(w.logits[sl], w.temperature, w.qdraft[sl], w.u[sl],
+                                 w.tokens[sl], w.parent[sl], w.n_nodes[sl])
+        nodes += int(w.n_nodes[b]) - 1
+        seqs += 1
+        i += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or seqs >= 4 * len(live):
+            break
+    return {"value": nodes / el, "unit": "verified draft nodes/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "%d sequence(s) of workload %s (mask + float64 attention over all "
+                      "%d KV heads + acceptance), %.1f s" % (seqs, w.name, w.Hkv, el)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import tree_attention_draft_tv_amd as tv
+    from workloads import make_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    tv.load()
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return
+
+    w = make_config(args.config)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32))
+
+    host = {
+        "q": bf(w.q) if w.dtype == "bf16" else torch.from_numpy(w.q),
+        "k": bf(w.k) if w.dtype == "bf16" else torch.from_numpy(w.k),
+        "v": bf(w.v) if w.dtype == "bf16" else torch.from_numpy(w.v),
+        "ctx": i32(w.ctx_len), "n": i32(w.n_nodes), "parent": i32(w.parent),
+        "tokens": i32(w.tokens), "logits": torch.from_numpy(w.logits),
+    }
+    if w.mode == "sample":
+        host["qd"] = torch.from_numpy(w.qdraft)
+        host["u"] = torch.from_numpy(w.u)
+    sets = [{k: t.to(dev) for k, t in host.items()} for _ in range(max(1, args.sets))]
+    B, T = w.B, w.T
+    W = (T + 31) // 32
+    bufs = []
+    for _ in sets:
+        bufs.append({
+            "mask": (torch.empty((B, T, W), dtype=torch.int32, device=dev),
+                     torch.empty((B, T), dtype=torch.int32, device=dev),
+                     torch.empty((B,), dtype=torch.int32, device=dev)),
+            "out": torch.empty((B, T, w.Hq, w.D), dtype=torch.float32, device=dev),
+            "lse": torch.empty((B, T, w.Hq), dtype=torch.float32, device=dev),
+            "ast": torch.empty((B,), dtype=torch.int32, device=dev),
+        })
+    ws_attn = torch.empty(max(1, tv.attention_workspace_size(B, T, w.Hq, w.Hkv, w.D, w.max_ctx,
+                                                               args.chunk)),
+                          dtype=torch.uint8, device=dev)
+    mode = 0 if w.mode == "greedy" else 1
+    ws_acc = torch.empty(tv.accept_workspace_size(B, T, w.V, mode), dtype=torch.uint8, device=dev)
+    acc_out = (torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B, T), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B, T), dtype=torch.uint8, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev))
+    dec = torch.empty((B, T), dtype=torch.int8, device=dev)
+
+    def step(i, ev=None):
+        s = sets[i % len(sets)]
+        bb = bufs[i % len(bufs)]
+        if ev is not None:
+            ev[0].record()
+        mask, _, _ = tv.build_tree_mask(s["parent"], s["n"], out=bb["mask"])
+        if ev is not None:
+            ev[1].record()
+        tv.tree_attention(s["q"], s["k"], s["v"], s["ctx"], s["n"], mask, w.max_ctx,
+                          scale=float(w.scale), probability_parts=args.parts,
+                          chunk_keys=args.chunk, out=bb["out"], lse=bb["lse"],
+                          row_status=bb["ast"], workspace=ws_attn)
+        if ev is not None:
+            ev[2].record()
+        if mode == 0:
+            tv.accept_greedy(s["logits"], s["tokens"], s["parent"], s["n"], outputs=acc_out,
+                             workspace=ws_acc)
+        else:
+            tv.accept_sample(s["logits"], float(w.temperature), s["qd"], s["u"], s["tokens"],
+                             s["parent"], s["n"], outputs=acc_out[:4] + (dec, acc_out[4]),
+                             workspace=ws_acc)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region 1: whole steps, wall clock between two synchronisations.
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # Timed region 2: the same steps with HIP events between the calls, on the
+    # stream the kernels are launched on.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t_mask = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    t_attn = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    t_acc = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
+
+    ms_per_step = wall / args.steps * 1e3
+    nodes = w.draft_nodes
+    value = nodes / (wall / args.steps)
+    a_bytes = attention_alg_bytes(w)
+    a_flops = attention_flops(w)
+    acc_bytes = accept_alg_bytes(w)
+    achieved = a_bytes / t_attn / 1e9
+    traffic = measured_traffic()
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "verified draft nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; cold: %d rotating input copies)" % len(sets),
+        "config": {
+            "workload": "%s: B=%d (%d live), Hq/Hkv=%d/%d, D=%d, ctx %d..%d, N=%d draft nodes "
+                        "(T=%d), V=%d, %s acceptance" % (
+                            w.name, w.B, w.live_rows, w.Hq, w.Hkv, w.D, int(w.ctx_len.min()),
+                            int(w.ctx_len.max()), w.T - 1, w.T, w.V, w.mode),
+            "draft_nodes_per_step": nodes,
+            "chunk_keys": args.chunk if args.chunk else tv.auto_chunk(B, T, w.Hq, w.Hkv,
+                                                                      w.max_ctx),
+            "probability_parts": args.parts,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "tv_tree_attention (split + combine)",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": a_bytes,
+            "avg_launch_us": round(t_attn * 1e6, 3),
+        },
+        "kernels": {
+            "mask_us": round(t_mask * 1e6, 3),
+            "attention_us": round(t_attn * 1e6, 3),
+            "attention_GBps": round(achieved, 1),
+            "attention_TFLOPs": round(a_flops / t_attn / 1e12, 2),
+            "accept_us": round(t_acc * 1e6, 3),
+            "accept_GBps": round(acc_bytes / t_acc / 1e9, 1),
+            "accept_alg_bytes": acc_bytes,
+            "nodes_per_s_attention_only": round(nodes / t_attn, 1),
+        },
+    }
+
+    if not args.no_sampling and w.mode == "greedy":
+        res["sampling"] = sampling_secondary(tv, torch, dev, args)
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def sampling_secondary(tv, torch, dev, args):
+    """Sampling acceptance at its own workload (8 sequences, V=32000), warm."""
+    from workloads import make_config
+
+    w = make_config("C5")
+    lg = torch.from_numpy(w.logits).to(dev)
+    qd = torch.from_numpy(w.qdraft).to(dev)
+    u = torch.from_numpy(w.u).to(dev)
+    tok = torch.from_numpy(w.tokens).to(dev)
+    par = torch.from_numpy(w.parent).to(dev)
+    n = torch.from_numpy(w.n_nodes).to(dev)
+    ws = torch.empty(tv.accept_workspace_size(w.B, w.T, w.V, 1), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        tv.accept_sample(lg, float(w.temperature), qd, u, tok, par, n, workspace=ws)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = max(5, args.steps)
+    e0.record()
+    for _ in range(reps):
+        tv.accept_sample(lg, float(w.temperature), qd, u, tok, par, n, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    by = accept_alg_bytes(w)
+    return {"workload": "C5: B=8, V=32000, N=32, temperature 0.7", "accept_us": round(t * 1e6, 3),
+            "alg_bytes": by, "GBps_warm": round(by / t / 1e9, 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+/*
+ * tv.h — tree-draft verification on AMD MI355X (gfx950): C ABI.
+ *
+ * Verifies a speculative draft token tree in one forward pass, the method of
+ * the EmbodiInfer pull-request page "perf(activevln): grammar-trie
+ * speculation and lossless throughput":
+ *   - commit "feat(activevln): grammar-trie tree speculation with exact
+ *     acceptance": the N most likely trie nodes are verified in one
+ *     tree-attention forward; greedy decoding keeps the argmax path; sampling
+ *     runs standard rejection sampling against the draft;
+ *   - commit "perf(activevln): lossless batched replay throughput options",
+ *     item attention_kernel="gqa": a split-KV kernel that packs the query
+ *     heads sharing a KV head into one program; items probability_parts and
+ *     skip_padded_queries;
+ *   - commit "fix(attention): never read KV slots past a row's live queries".
+ * The acceptance-mask output follows the vectorised accepted-token mask of
+ * the IluvatarLabs/vllm page "Introduce SCV vectorized masking with
+ * graph/adaptive modes".
+ *
+ * Tree conventions (all entry points):
+ *   A sequence b has T tree rows. Row 0 is the root (the last accepted token);
+ *   rows 1..n-1 are draft nodes with 0 <= parent[i] < i; n = n_nodes[b] is
+ *   0 (a fully padded sequence: no work, padding outputs) or 1..T. Rows
+ *   i >= n are padding. parent[b][0] is ignored.
+ *
+ * Memory: every pointer argument is a DEVICE pointer owned by the caller,
+ * unless stated otherwise. The library allocates nothing, keeps no global
+ * mutable state, never synchronises the stream and never reads device memory
+ * from the host; every call only enqueues kernels on `stream`, so it can be
+ * captured in a HIP graph. Grid sizes depend only on host integers.
+ *
+ * Errors: a call first validates its host-visible arguments and returns a
+ * negative tv_status (nothing enqueued) on failure. Problems that only the
+ * device can see (a bad parent link, a context over its bound) are written to
+ * row_status[b] (tv_row_status) and that sequence's outputs are set to the
+ * padding values. TV_ERR_HIP means a kernel launch failed.
+ */
+#ifndef TV_H_
+#define TV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tv_status {
+  TV_OK = 0,
+  TV_ERR_NULL = -1,        /* a required pointer is NULL */
+  TV_ERR_SHAPE = -2,       /* a size or stride is out of range */
+  TV_ERR_DTYPE = -3,       /* unknown element type */
+  TV_ERR_ALIGN = -4,       /* pointer or stride misaligned */
+  TV_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+  TV_ERR_UNSUPPORTED = -6, /* a valid but unsupported configuration (head_dim) */
+  TV_ERR_HIP = -7          /* the HIP runtime reported an error */
+} tv_status;
+
+typedef enum tv_row_status {
+  TV_ROW_OK = 0,
+  TV_ROW_BAD_PARENT = 1, /* some live node i has parent outside [0, i) */
+  TV_ROW_CTX_BOUND = 2,  /* ctx_len < 0, ctx_len > max_ctx or ctx_len + n > kv_capacity */
+  TV_ROW_NNODES = 3,     /* n_nodes outside [0, T] */
+  TV_ROW_BAD_TOKEN = 4   /* some live draft token outside [0, V) */
+} tv_row_status;
+
+typedef enum tv_dtype { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
+
+/* Largest tree the kernels accept (rows per sequence, root included). */
+#define TV_MAX_TREE 128
+/* Largest number of query heads sharing one KV head. */
+#define TV_MAX_GROUP 16
+
+/*
+ * tv_build_tree_mask — ancestor-or-self visibility of every tree row.
+ * (Page 1, commit "feat(activevln): grammar-trie tree speculation with exact
+ * acceptance": a node is verified against the committed context plus its
+ * own ancestors in one tree-attention forward.)
+ *
+ *   parent   int32 [B][T]   parent links (row-major, contiguous)
+ *   n_nodes  int32 [B]      live rows per sequence
+ *   mask     uint32 [B][T][W], W = ceil(T / 32): bit j of word j/32 of
+ *            mask[b][i] is set iff node j is node i or one of its ancestors
+ *   depth    int32 [B][T]   root 0, node i: depth[parent[i]] + 1; -1 on
+ *            padding rows and on every row of a sequence whose status is not OK
+ *   row_status int32 [B]    TV_ROW_OK, TV_ROW_BAD_PARENT or TV_ROW_NNODES
+ *
+ * The mask is built once per verification step and reused by every layer's
+ * tv_tree_attention call. 1 <= T <= TV_MAX_TREE; B >= 0 (B == 0 enqueues
+ * nothing). Errors: TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_HIP.
+ */
+int tv_build_tree_mask(const int32_t* parent, const int32_t* n_nodes, int B, int T,
+                       uint32_t* mask, int32_t* depth, int32_t* row_status,
+                       hipStream_t stream);
+
+/*
+ * Workspace (bytes) tv_tree_attention needs for these sizes and chunk choice
+ * (chunk_keys == 0: the automatic choice tv_tree_attention makes). Returns 0
+ * when no workspace is needed (a single key chunk per sequence) and
+ * (size_t)-1 for invalid sizes.
+ */
+size_t tv_tree_attention_workspace_size(int B, int T, int Hq, int Hkv, int D, int max_ctx,
+                                        int chunk_keys);
+
+/* The key-chunk size tv_tree_attention uses for chunk_keys == 0. */
+int tv_tree_attention_auto_chunk(int B, int T, int Hq, int Hkv, int max_ctx);
+
+/*
+ * tv_tree_attention — tree-masked, split-KV, grouped-query attention.
+ * (Page 1, commit "perf(activevln): lossless batched replay throughput
+ * options", items attention_kernel="gqa", probability_parts and
+ * skip_padded_queries; commit "fix(attention): never read KV slots past a
+ * row's live queries".)
+ *
+ * For each sequence b with n = n_nodes[b] > 0 and L = ctx_len[b], each live
+ * node i < n and query head h (KV head h / (Hq / Hkv)):
+ *   visible keys: cache slots [0, L) (the committed context) and slots L + j
+ *                 for every j with bit j of mask[b][i] set (j < n);
+ *   out[b][i][h] = softmax(scale * q . k) @ v over the visible keys;
+ *   lse[b][i][h] = natural log of sum over visible keys of exp(scale * q . k).
+ * Padding rows (i >= n), padded sequences (n == 0) and sequences with a bad
+ * status get out = 0 and lse = -inf. Cache slots >= L + n are never read, so
+ * they may hold anything (NaN included). A padded sequence reads no KV.
+ *
+ *   q        [B][T][Hq][D] elements of in_dtype; element (b,i,h,d) at
+ *            q + b*q_sb + i*q_st + h*q_sh + d (strides in elements)
+ *   k, v     [B][Hkv][kv_capacity][D] caches; element (b,g,s,d) at
+ *            base + b*kv_sb + g*kv_sh + s*kv_ss + d
+ *   ctx_len  int32 [B]; n_nodes int32 [B]; mask from tv_build_tree_mask
+ *   max_ctx  host bound on every ctx_len (sizes the grid); kv_capacity slots
+ *   scale    softmax scale (1/sqrt(D) is the usual choice)
+ *   in_dtype TV_F32 (fp32-faithful arithmetic) or TV_BF16 (bf16 matrix cores,
+ *            fp32 accumulation)
+ *   probability_parts  1..3 (bf16 only): the probabilities enter the P.V
+ *            product as a sum of that many bf16 terms (3 = fp32-faithful P)
+ *   chunk_keys  keys per split-KV partition (multiple of 64, 64..65536) or 0
+ *            for the automatic choice; results are bitwise independent of the
+ *            other sequences of the batch for a fixed chunk_keys
+ *   out      float32 [B][T][Hq][D] contiguous; lse float32 [B][T][Hq]
+ *   workspace/ws_bytes  device scratch of at least
+ *            tv_tree_attention_workspace_size(...) bytes, 256-byte aligned
+ *            (may be NULL when that size is 0); contents need no initialisation
+ *   row_status int32 [B]: TV_ROW_OK, TV_ROW_NNODES or TV_ROW_CTX_BOUND
+ *
+ * Constraints: D in {64, 128} (else TV_ERR_UNSUPPORTED); 1 <= T <= TV_MAX_TREE;
+ * Hq % Hkv == 0 and Hq / Hkv <= TV_MAX_GROUP; q, k, v 16-byte aligned with
+ * every stride a multiple of 16 bytes; out, lse 16-byte aligned.
+ */
+int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
+                      const void* k, const void* v, int64_t kv_sb, int64_t kv_sh,
+                      int64_t kv_ss, const int32_t* ctx_len, const int32_t* n_nodes,
+                      const uint32_t* mask, int B, int T, int Hq, int Hkv, int D,
+                      int max_ctx, int kv_capacity, float scale, int in_dtype,
+                      int probability_parts, int chunk_keys, float* out, float* lse,
+                      void* workspace, size_t ws_bytes, int32_t* row_status,
+                      hipStream_t stream);
+
+/*
+ * Workspace (bytes) of tv_accept_greedy (mode 0) or tv_accept_sample
+ * (mode 1); (size_t)-1 for invalid sizes.
+ */
+size_t tv_accept_workspace_size(int B, int T, int V, int mode);
+
+/*
+ * tv_accept_greedy — exact greedy acceptance of a verified tree.
+ * (Page 1, commit "feat(activevln): grammar-trie tree speculation with exact
+ * acceptance": greedy decoding keeps the argmax path.)
+ *
+ * For each live sequence: a_j = argmax_v logits[b][j][v] (the lowest index
+ * among equal maxima; -0.0 equals +0.0; logits must be finite). From the
+ * root, move to the lowest-index child c of the current node with
+ * tokens[b][c] == a_cur; when no child matches, a_cur is the bonus token.
+ *
+ *   logits   float32, row (b, j) at logits + (b*T + j) * logits_row_stride,
+ *            V contiguous values; only rows j < n_nodes[b] are read
+ *   tokens, parent  int32 [B][T]; tokens[b][0] is ignored
+ *   accept_len int32 [B]  accepted draft nodes (0 on padding)
+ *   path     int32 [B][T] root then accepted nodes in depth order, -1 after
+ *   bonus    int32 [B]    token after the accepted path (-1 on padding)
+ *   accept_mask uint8 [B][T] 1 on the nodes of path, else 0
+ *   row_status int32 [B]: OK, BAD_PARENT, NNODES or BAD_TOKEN
+ *
+ * Constraints: 1 <= T <= TV_MAX_TREE; V >= 1; logits 16-byte aligned and
+ * logits_row_stride >= V, a multiple of 4. Workspace as sized above,
+ * 256-byte aligned, no initialisation needed.
+ */
+int tv_accept_greedy(const float* logits, int64_t logits_row_stride, const int32_t* tokens,
+                     const int32_t* parent, const int32_t* n_nodes, int B, int T, int V,
+                     int32_t* accept_len, int32_t* path, int32_t* bonus, uint8_t* accept_mask,
+                     void* workspace, size_t ws_bytes, int32_t* row_status,
+                     hipStream_t stream);
+
+/*
+ * tv_accept_sample — SpecInfer-style rejection sampling on the tree.
+ * (Page 1, commit "feat(activevln): grammar-trie tree speculation with exact
+ * acceptance": standard rejection sampling against the draft keeps the
+ * output distribution unchanged; summary: "exact SpecInfer-style
+ * acceptance".)
+ *
+ * Target p_j(x) = exp((l_j(x) - max l_j) / tau) / sum, computed in float64
+ * with tau the float64 value of `temperature`. Walk from the root with
+ * r = p_root; test the children c of the current node in ascending index:
+ * x = tokens[b][c], ratio = r(x) / q_c(x) (0 when r(x) = 0, +inf when
+ * q_c(x) = 0 < r(x)); accept iff u[b][c] < ratio (then move to c and set
+ * r = p_c), else r = max(r - q_c, 0) renormalised. When no child of the
+ * current node is accepted, the bonus token is the smallest x with
+ * sum_{y<=x} r(y) > u[b][0] * sum_y r(y).
+ *
+ *   logits   as in tv_accept_greedy (float32 target logits)
+ *   q        float32 draft distributions, row (b, c) at
+ *            q + (b*T + c) * q_row_stride; row 0 is never read
+ *   u        float32 [B][T] uniforms in [0, 1): u[b][c] tests node c,
+ *            u[b][0] is the single final draw
+ *   decision int8 [B][T]  +1 accepted, 0 rejected, -1 never tested
+ *   other outputs as in tv_accept_greedy
+ *
+ * Constraints as tv_accept_greedy, plus q 16-byte aligned with
+ * q_row_stride >= V, a multiple of 4, and temperature > 0.
+ */
+int tv_accept_sample(const float* logits, int64_t logits_row_stride, float temperature,
+                     const float* q, int64_t q_row_stride, const float* u,
+                     const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
+                     int B, int T, int V, int32_t* accept_len, int32_t* path, int32_t* bonus,
+                     uint8_t* accept_mask, int8_t* decision, void* workspace, size_t ws_bytes,
+                     int32_t* row_status, hipStream_t stream);
+
+/* Static, human-readable name of a tv_status or tv_row_status value. */
+const char* tv_status_string(int code);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int tv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TV_H_ */

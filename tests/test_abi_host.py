@@ -1,0 +1,154 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/tv.h declares, and rejects bad arguments with the
+documented status codes before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_attention_draft_tv_amd as tv
+from tree_attention_draft_tv_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tv.h")
+
+# Non-null, 256-byte aligned fake addresses: validation must fail before use.
+P = ctypes.c_void_p(0x100000)
+P2 = ctypes.c_void_p(0x200000)
+NULL = None
+STREAM = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tv_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tv.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(binding.SIGNATURES) == names
+
+
+def test_version_and_status_strings(lib):
+    assert lib.tv_version() == 100
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, 1, 2, 3, 4):
+        s = lib.tv_status_string(code).decode()
+        assert s and s != "unknown status", code
+    assert lib.tv_status_string(99).decode() == "unknown status"
+
+
+def test_mask_validation(lib):
+    assert lib.tv_build_tree_mask(NULL, P, 1, 4, P, P, P, STREAM) == -1
+    assert lib.tv_build_tree_mask(P, P, 1, 0, P, P, P, STREAM) == -2
+    assert lib.tv_build_tree_mask(P, P, 1, 129, P, P, P, STREAM) == -2
+    assert lib.tv_build_tree_mask(P, P, -1, 4, P, P, P, STREAM) == -2
+    assert lib.tv_build_tree_mask(P, P, 0, 4, P, P, P, STREAM) == 0  # nothing to do
+
+
+def _attn(lib, **kw):
+    a = dict(q=P, q_sb=8 * 33 * 28 * 128, q_st=28 * 128, q_sh=128, k=P, v=P2,
+             kv_sb=4 * 4096 * 128, kv_sh=4096 * 128, kv_ss=128, ctx=P, n=P, mask=P,
+             B=2, T=33, Hq=28, Hkv=4, D=128, max_ctx=4000, cap=4096, scale=0.088,
+             dtype=1, parts=1, chunk=0, out=P, lse=P, ws=P, ws_bytes=1 << 40, st=P)
+    a.update(kw)
+    return lib.tv_tree_attention(a["q"], a["q_sb"], a["q_st"], a["q_sh"], a["k"], a["v"],
+                                 a["kv_sb"], a["kv_sh"], a["kv_ss"], a["ctx"], a["n"], a["mask"],
+                                 a["B"], a["T"], a["Hq"], a["Hkv"], a["D"], a["max_ctx"],
+                                 a["cap"], a["scale"], a["dtype"], a["parts"], a["chunk"],
+                                 a["out"], a["lse"], a["ws"], a["ws_bytes"], a["st"], STREAM)
+
+
+def test_attention_validation(lib):
+    assert _attn(lib, q=NULL) == -1
+    assert _attn(lib, mask=NULL) == -1
+    assert _attn(lib, st=NULL) == -1
+    assert _attn(lib, dtype=5) == -3
+    assert _attn(lib, T=0) == -2
+    assert _attn(lib, T=129) == -2
+    assert _attn(lib, Hq=27) == -2                  # not a multiple of Hkv
+    assert _attn(lib, Hq=68) == -2                  # group of 17 > 16
+    assert _attn(lib, parts=4) == -2
+    assert _attn(lib, chunk=100) == -2              # not a multiple of 64
+    assert _attn(lib, chunk=32) == -2
+    assert _attn(lib, cap=0) == -2
+    assert _attn(lib, D=96) == -6
+    assert _attn(lib, q=ctypes.c_void_p(0x100008)) == -4
+    assert _attn(lib, kv_ss=132) == -4               # bf16 stride not a multiple of 8
+    assert _attn(lib, ws=NULL, ws_bytes=0) == -5
+    assert _attn(lib, ws_bytes=16) == -5
+    assert _attn(lib, ws=ctypes.c_void_p(0x100010)) == -5  # not 256-byte aligned
+    assert _attn(lib, B=0) == 0
+
+
+def test_attention_workspace_size(lib):
+    f = lib.tv_tree_attention_workspace_size
+    assert f(8, 33, 28, 4, 128, 256, 256) == 0          # one chunk: no workspace
+    assert f(1, 9, 8, 2, 64, 256, 0) == 0
+    big = f(8, 33, 28, 4, 128, 7650, 512)
+    rows = 8 * 4 * 15 * 231
+    assert big >= rows * (128 * 4 + 8)
+    assert f(8, 33, 28, 4, 128, 7650, 100) == ctypes.c_size_t(-1).value
+    assert lib.tv_tree_attention_auto_chunk(8, 33, 28, 4, 7650) % 64 == 0
+
+
+def test_accept_validation(lib):
+    g = lib.tv_accept_greedy
+    ok = dict(lg=P, stride=152064, tok=P, par=P, n=P, B=2, T=33, V=152064, al=P, path=P,
+              bonus=P, am=P, ws=P, wsb=1 << 40, st=P)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return g(a["lg"], a["stride"], a["tok"], a["par"], a["n"], a["B"], a["T"], a["V"],
+                 a["al"], a["path"], a["bonus"], a["am"], a["ws"], a["wsb"], a["st"], STREAM)
+
+    assert call(lg=NULL) == -1
+    assert call(bonus=NULL) == -1
+    assert call(T=0) == -2 and call(T=200) == -2 and call(V=0) == -2
+    assert call(stride=100) == -2
+    assert call(stride=152066) == -4
+    assert call(lg=ctypes.c_void_p(0x100004)) == -4
+    assert call(ws=NULL) == -5 and call(wsb=8) == -5
+    assert call(B=0) == 0
+    s = lib.tv_accept_sample
+
+    def scall(**kw):
+        a = dict(lg=P, stride=32000, temp=0.7, q=P2, qs=32000, u=P, tok=P, par=P, n=P, B=2,
+                 T=33, V=32000, al=P, path=P, bonus=P, am=P, dec=P, ws=P, wsb=1 << 40, st=P)
+        a.update(kw)
+        return s(a["lg"], a["stride"], a["temp"], a["q"], a["qs"], a["u"], a["tok"], a["par"],
+                 a["n"], a["B"], a["T"], a["V"], a["al"], a["path"], a["bonus"], a["am"],
+                 a["dec"], a["ws"], a["wsb"], a["st"], STREAM)
+
+    assert scall(q=NULL) == -1 and scall(dec=NULL) == -1 and scall(u=NULL) == -1
+    assert scall(temp=0.0) == -2 and scall(temp=-1.0) == -2
+    assert scall(qs=10) == -2
+    assert scall(qs=32002) == -4
+    assert scall(wsb=100) == -5
+    assert scall(B=0) == 0
+
+
+def test_accept_workspace_size(lib):
+    f = lib.tv_accept_workspace_size
+    assert f(8, 33, 152064, 0) >= 8 * 33 * 10 * 8
+    assert f(8, 33, 32000, 1) >= 8 * 2 * 32000 * 8
+    assert f(8, 33, 32000, 2) == ctypes.c_size_t(-1).value
+    assert f(8, 0, 32000, 0) == ctypes.c_size_t(-1).value
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    parent = torch.zeros((1, 4), dtype=torch.int32)
+    with pytest.raises(tv.TVError):
+        tv.build_tree_mask(parent, torch.ones(1, dtype=torch.int32))

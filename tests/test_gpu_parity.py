@@ -1,0 +1,354 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Attention: max |out - oracle| <= 2e-3 and max |lse - oracle| <= 1e-4 over
+live rows; padding rows exactly 0 / -inf; no NaN although every dead cache
+slot, padding query, logits row and draft row holds NaN. Mask and greedy
+outputs: bit-exact. Sampling: bit-exact decisions except within 1e-6 of a
+threshold.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import make_config, make_custom
+
+from gpu_util import (check_attention, check_greedy, check_sample, oracle_attention,
+                      run_attention, run_greedy, run_mask, run_sample, upload)
+import tree_attention_draft_tv_amd as tv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X")
+    tv.load()
+
+
+def _mask_check(w, d):
+    mask, depth, st = run_mask(d, w.T)
+    torch.cuda.synchronize()
+    m_ref, dep_ref, st_ref = oracle.build_tree_mask(w.parent, w.n_nodes, w.T)
+    assert np.array_equal(st.cpu().numpy(), st_ref)
+    assert np.array_equal(mask.cpu().numpy().view(np.uint32), m_ref)
+    assert np.array_equal(depth.cpu().numpy(), dep_ref)
+    return mask
+
+
+# ------------------------------------------------------------------ mask ---
+
+@pytest.mark.parametrize("T", [1, 2, 9, 33, 64, 65, 100, 128])
+def test_mask_random_trees(T):
+    rng = np.random.default_rng(T)
+    B = 6
+    parent = np.full((B, T), -1, np.int32)
+    n_nodes = np.array([T, T, max(T - 3, 0), 0, T, T], np.int32)
+    for b in range(B):
+        for i in range(1, T):
+            if b == 4:
+                parent[b, i] = i - 1                # chain
+            elif b == 5:
+                parent[b, i] = 0                    # star
+            else:
+                parent[b, i] = rng.integers(0, i)
+    d = {"parent": torch.from_numpy(parent).cuda(), "n_nodes": torch.from_numpy(n_nodes).cuda()}
+
+    class W:
+        pass
+    w = W()
+    w.parent, w.n_nodes, w.T = parent, n_nodes, T
+    _mask_check(w, d)
+
+
+def test_mask_status_codes():
+    T = 8
+    parent = np.tile(np.arange(-1, T - 1, dtype=np.int32), (4, 1))
+    parent[1, 5] = 5          # not < 5
+    parent[2, 3] = -2
+    n_nodes = np.array([8, 8, 8, 9], np.int32)
+    d = {"parent": torch.from_numpy(parent).cuda(), "n_nodes": torch.from_numpy(n_nodes).cuda()}
+
+    class W:
+        pass
+    w = W()
+    w.parent, w.n_nodes, w.T = parent, n_nodes, T
+    _mask_check(w, d)
+
+
+# ------------------------------------------------------------- attention ---
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C5"])
+def test_attention_configs(name):
+    w = make_config(name)
+    d = upload(w)
+    mask = _mask_check(w, d)
+    got = run_attention(w, d, mask)
+    err = check_attention(w, got, oracle_attention(w))
+    print(name, "max abs err out %.3g lse %.3g" % err)
+
+
+def test_attention_long_context_c4():
+    w = make_config("C4")
+    d = upload(w)
+    mask = _mask_check(w, d)
+    got = run_attention(w, d, mask)
+    err = check_attention(w, got, oracle_attention(w))
+    print("C4 max abs err out %.3g lse %.3g" % err)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("chunk", [64, 128, 0])
+def test_attention_multichunk_ragged(dtype, D, chunk):
+    # Ragged contexts (not multiples of the chunk or the 64-key tile), an empty
+    # context, a partial tree, a padded sequence, G = 3 so rows straddle tiles.
+    w = make_custom(31 + D + chunk, 5, 9, 3, D, 50, dtype, [300, 0, 77, 1000, 129], 20,
+                    n_nodes=[21, 21, 13, 0, 1], trie_tokens=False)
+    d = upload(w)
+    mask = _mask_check(w, d)
+    got = run_attention(w, d, mask, chunk_keys=chunk)
+    check_attention(w, got, oracle_attention(w))
+
+
+@pytest.mark.parametrize("parts", [1, 2, 3])
+def test_attention_probability_parts(parts):
+    w = make_custom(41, 2, 16, 2, 128, 50, "bf16", [37, 700], 40, max_depth=10,
+                    trie_tokens=False)
+    d = upload(w)
+    mask = _mask_check(w, d)
+    got = run_attention(w, d, mask, chunk_keys=256, parts=parts)
+    want = oracle_attention(w)
+    err_o, err_l = check_attention(w, got, want)
+    if parts == 3:  # probabilities fp32-faithful: only fp32 accumulation error remains
+        assert err_o < 2e-5 and err_l < 2e-5, (err_o, err_l)
+
+
+def test_attention_many_rows_two_row_groups():
+    # R = 16 heads per KV head x 65 rows = 1040 packed rows: five row groups.
+    w = make_custom(51, 1, 16, 1, 128, 50, "bf16", [333], 64, max_depth=12, max_children=6,
+                    trie_tokens=False)
+    d = upload(w)
+    mask = _mask_check(w, d)
+    for chunk in (64, 0):
+        got = run_attention(w, d, mask, chunk_keys=chunk)
+        check_attention(w, got, oracle_attention(w))
+
+
+def test_attention_context_bound_status():
+    w = make_custom(61, 3, 4, 2, 64, 50, "bf16", [100, 200, 50], 8, trie_tokens=False,
+                    max_ctx=150, kv_capacity=256)
+    d = upload(w)
+    mask = _mask_check(w, d)
+    got = run_attention(w, d, mask, chunk_keys=64)
+    want = oracle.tree_attention(w.q, w.k, w.v, w.dtype, w.ctx_len, w.n_nodes, w.parent,
+                                 w.scale, max_ctx=150, kv_capacity=256)
+    assert want[2].tolist() == [0, oracle.ROW_CTX_BOUND, 0]
+    check_attention(w, got, want)
+
+
+def test_attention_batch_invariance_and_determinism():
+    w = make_custom(71, 4, 14, 2, 128, 50, "bf16", [900, 2000, 64, 1500], 32,
+                    trie_tokens=False, n_nodes=[33, 33, 20, 33])
+    d = upload(w)
+    mask = _mask_check(w, d)
+    a = run_attention(w, d, mask, chunk_keys=256, max_ctx=2048)
+    b2 = run_attention(w, d, mask, chunk_keys=256, max_ctx=2048)
+    assert np.array_equal(a[0], b2[0]) and np.array_equal(a[1], b2[1])
+    for b in range(w.B):
+        sl = slice(b, b + 1)
+        one = {k: (v[sl] if v.dim() > 0 else v) for k, v in d.items()}
+        m1 = mask[sl].contiguous()
+        o1, l1, _ = tv.tree_attention(one["q"], one["k"], one["v"], one["ctx_len"],
+                                      one["n_nodes"], m1, 2048, scale=float(w.scale),
+                                      chunk_keys=256)
+        torch.cuda.synchronize()
+        assert np.array_equal(o1.cpu().numpy()[0], a[0][b])
+        assert np.array_equal(l1.cpu().numpy()[0], a[1][b])
+
+
+def test_attention_chunk_size_invariance_fp32_faithful():
+    w = make_custom(81, 2, 7, 1, 128, 50, "bf16", [1000, 3000], 32, trie_tokens=False)
+    d = upload(w)
+    mask = _mask_check(w, d)
+    ref = run_attention(w, d, mask, chunk_keys=64, parts=3)
+    for chunk in (128, 512, 4096):
+        got = run_attention(w, d, mask, chunk_keys=chunk, parts=3)
+        assert np.abs(got[0] - ref[0]).max() < 1e-5
+        assert np.abs(got[1] - ref[1]).max() < 1e-5
+
+
+def test_attention_strided_nhd_cache():
+    # Cache laid out [B][capacity][Hkv][D] (NHD) and viewed through strides.
+    w = make_custom(91, 2, 8, 2, 128, 50, "bf16", [200, 90], 12, trie_tokens=False)
+    d = upload(w)
+    mask = _mask_check(w, d)
+    k_nhd = d["k"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    v_nhd = d["v"].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    out, lse, st = tv.tree_attention(d["q"], k_nhd, v_nhd, d["ctx_len"], d["n_nodes"], mask,
+                                     w.max_ctx, scale=float(w.scale), chunk_keys=64)
+    torch.cuda.synchronize()
+    check_attention(w, (out.cpu().numpy(), lse.cpu().numpy(), st.cpu().numpy()),
+                    oracle_attention(w))
+
+
+def test_attention_all_padded_batch():
+    w = make_custom(95, 3, 4, 1, 64, 50, "bf16", [10, 20, 30], 5, trie_tokens=False,
+                    padded_rows=[0, 1, 2])
+    d = upload(w)
+    mask = _mask_check(w, d)
+    got = run_attention(w, d, mask, chunk_keys=64)
+    check_attention(w, got, oracle_attention(w))
+
+
+# ---------------------------------------------------------------- greedy ---
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4"])
+def test_greedy_configs(name):
+    w = make_config(name)
+    d = upload(w)
+    got = run_greedy(d)
+    want = oracle.accept_greedy(w.logits, w.tokens, w.parent, w.n_nodes)
+    check_greedy(got, want)
+    for b in w.planted:
+        assert got[0][b] == 4 and list(got[1][b, :5]) == w.planted[b]
+
+
+@pytest.mark.parametrize("V", [1, 3, 4, 5, 1000, 16387, 40000])
+def test_greedy_ties_and_odd_vocab(V):
+    rng = np.random.default_rng(V)
+    w = make_custom(V, 4, 2, 1, 64, V, "bf16", [4, 4, 4, 4], 12, trie_tokens=False,
+                    padded_rows=[2])
+    logits = w.logits.copy()
+    for b in range(4):
+        for j in range(int(w.n_nodes[b])):
+            row = logits[b, j]
+            m = row.max()
+            # plant exact ties of the maximum at several positions, and signed zeros
+            k = rng.integers(1, 4)
+            pos = rng.choice(V, size=min(k, V), replace=False)
+            row[pos] = m + 1.0
+            if j % 3 == 0:
+                row[:] = np.where(rng.random(V) < 0.5, np.float32(-0.0), np.float32(0.0))
+                row[rng.integers(0, V, size=max(1, V // 4))] = -1.0
+    # make some draft tokens match so the walk goes deeper
+    for b in range(4):
+        for c in range(1, int(w.n_nodes[b])):
+            if rng.random() < 0.6:
+                row = logits[b, w.parent[b, c]].astype(np.float64)
+                w.tokens[b, c] = int(np.flatnonzero(row == row.max())[0])
+    w.logits = logits
+    d = upload(w)
+    got = run_greedy(d)
+    check_greedy(got, oracle.accept_greedy(w.logits, w.tokens, w.parent, w.n_nodes))
+
+
+def test_greedy_status_codes():
+    w = make_custom(5, 4, 2, 1, 64, 100, "bf16", [4] * 4, 6, trie_tokens=False)
+    w.parent[1, 3] = 4
+    w.tokens[2, 2] = 100
+    w.n_nodes[3] = 9
+    d = upload(w)
+    got = run_greedy(d)
+    want = oracle.accept_greedy(w.logits, w.tokens, w.parent, w.n_nodes)
+    assert want[4].tolist() == [0, oracle.ROW_BAD_PARENT, oracle.ROW_BAD_TOKEN, oracle.ROW_NNODES]
+    check_greedy(got, want)
+
+
+# -------------------------------------------------------------- sampling ---
+
+def test_sample_config_c5():
+    w = make_config("C5")
+    d = upload(w)
+    got = run_sample(w, d)
+    want = oracle.accept_sample(w.logits, w.temperature, w.qdraft, w.u, w.tokens, w.parent,
+                                w.n_nodes)
+    exempt = check_sample(w, got, want)
+    print("C5 sampling: exempt rows", exempt)
+    assert exempt <= 1
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_sample_small_vocab_many_rows(seed):
+    w = make_custom(200 + seed, 16, 2, 1, 64, 7, "bf16", [4] * 16, 10, mode="sample",
+                    temperature=0.9 + 0.3 * seed, padded_rows=[3])
+    # make some draft probabilities exactly zero and some rows one-hot
+    rng = np.random.default_rng(seed)
+    for b in range(16):
+        for c in range(1, 11):
+            if rng.random() < 0.3:
+                z = rng.integers(0, 7)
+                if z != w.tokens[b, c]:
+                    w.qdraft[b, c, z] = 0.0
+            if rng.random() < 0.15:
+                w.qdraft[b, c] = 0.0
+                w.qdraft[b, c, w.tokens[b, c]] = 1.0
+    d = upload(w)
+    got = run_sample(w, d)
+    want = oracle.accept_sample(w.logits, w.temperature, w.qdraft, w.u, w.tokens, w.parent,
+                                w.n_nodes)
+    assert check_sample(w, got, want) <= 1
+
+
+def test_sample_draws_follow_target():
+    """Statistical check of the GPU sampler itself: the first emitted token
+    over many independent rows follows p_root (chi-square)."""
+    import scipy.stats
+    rng = np.random.default_rng(9)
+    V, rows, k = 5, 4096, 3
+    T = k + 1
+    root = np.log(rng.dirichlet(np.ones(V))).astype(np.float32)
+    logits = np.tile(root, (rows, T, 1)).astype(np.float32)
+    q = np.full((rows, T, V), np.nan, np.float32)
+    tokens = np.zeros((rows, T), np.int32)
+    drafts = [rng.dirichlet(np.ones(V)).astype(np.float32) for _ in range(k)]
+    for c in range(1, T):
+        q[:, c] = drafts[c - 1]
+        qq = drafts[c - 1].astype(np.float64)
+        tokens[:, c] = rng.choice(V, size=rows, p=qq / qq.sum())
+    parent = np.tile(np.array([-1] + [0] * k, np.int32), (rows, 1))
+    u = rng.random((rows, T), dtype=np.float32)
+    n = np.full(rows, T, np.int32)
+    res = tv.accept_sample(torch.from_numpy(logits).cuda(), 1.0, torch.from_numpy(q).cuda(),
+                           torch.from_numpy(u).cuda(), torch.from_numpy(tokens).cuda(),
+                           torch.from_numpy(parent).cuda(), torch.from_numpy(n).cuda())
+    al, path, bonus = (r.cpu().numpy() for r in res[:3])
+    first = np.where(al >= 1, tokens[np.arange(rows), np.maximum(path[:, 1], 0)], bonus)
+    p = oracle.sample_probs(root, np.float32(1.0))
+    pval = scipy.stats.chisquare(np.bincount(first, minlength=V), p * rows).pvalue
+    assert pval > 1e-3
+
+
+# ----------------------------------------------------------- HIP graphs ---
+
+def test_graph_capture_replays_match_eager():
+    w = make_config("C2")
+    d = upload(w)
+    mask_e, _, _ = tv.build_tree_mask(d["parent"], d["n_nodes"])
+    out_e, lse_e, _ = tv.tree_attention(d["q"], d["k"], d["v"], d["ctx_len"], d["n_nodes"],
+                                        mask_e, w.max_ctx, scale=float(w.scale))
+    acc_e = tv.accept_greedy(d["logits"], d["tokens"], d["parent"], d["n_nodes"])
+    torch.cuda.synchronize()
+    ref = [out_e.cpu(), lse_e.cpu()] + [a.cpu() for a in acc_e]
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g):
+            mask, _, _ = tv.build_tree_mask(d["parent"], d["n_nodes"])
+            out, lse, _ = tv.tree_attention(d["q"], d["k"], d["v"], d["ctx_len"], d["n_nodes"],
+                                            mask, w.max_ctx, scale=float(w.scale))
+            acc = tv.accept_greedy(d["logits"], d["tokens"], d["parent"], d["n_nodes"])
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        out.fill_(7.0)
+        acc[0].fill_(-5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [out.cpu(), lse.cpu()] + [a.cpu() for a in acc]
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), rep

@@ -1,0 +1,26 @@
+"""Tree-draft verification for AMD MI355X (gfx950).
+
+Verifies a speculative draft token tree in one forward pass: ancestor masks
+(:func:`build_tree_mask`), tree-masked split-KV grouped-query attention
+(:func:`tree_attention`) and exact acceptance (:func:`accept_greedy`,
+:func:`accept_sample`). The compute runs in the HIP kernels of the in-tree
+``libtv.so`` (C ABI in ``include/tv.h``); this package only marshals
+arguments.
+"""
+
+from .binding import (  # noqa: F401
+    LIB_PATH,
+    TV_BF16,
+    TV_F32,
+    TV_MAX_GROUP,
+    TV_MAX_TREE,
+    TVError,
+    accept_greedy,
+    accept_sample,
+    accept_workspace_size,
+    attention_workspace_size,
+    auto_chunk,
+    build_tree_mask,
+    load,
+    tree_attention,
+)

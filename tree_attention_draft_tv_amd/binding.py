@@ -1,0 +1,294 @@
+"""Thin Python binding of the tree-verification C ABI (``include/tv.h``).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libtv.so``. PyTorch provides device memory and the current HIP stream;
+the functions take and return torch tensors on an MI355X device. There is
+no fallback: if ``libtv.so`` is missing or a call fails, an exception is
+raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtv.so")
+
+TV_F32 = 0
+TV_BF16 = 1
+TV_MAX_TREE = 128
+TV_MAX_GROUP = 16
+
+STATUS = {
+    0: "TV_OK", -1: "TV_ERR_NULL", -2: "TV_ERR_SHAPE", -3: "TV_ERR_DTYPE",
+    -4: "TV_ERR_ALIGN", -5: "TV_ERR_WORKSPACE", -6: "TV_ERR_UNSUPPORTED", -7: "TV_ERR_HIP",
+}
+ROW_STATUS = {0: "TV_ROW_OK", 1: "TV_ROW_BAD_PARENT", 2: "TV_ROW_CTX_BOUND",
+              3: "TV_ROW_NNODES", 4: "TV_ROW_BAD_TOKEN"}
+
+# Every exported symbol of include/tv.h with its (restype, argtypes).
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_L = ctypes.c_int64
+_S = ctypes.c_size_t
+_F = ctypes.c_float
+SIGNATURES = {
+    "tv_build_tree_mask": (_I, [_P, _P, _I, _I, _P, _P, _P, _P]),
+    "tv_tree_attention_workspace_size": (_S, [_I, _I, _I, _I, _I, _I, _I]),
+    "tv_tree_attention_auto_chunk": (_I, [_I, _I, _I, _I, _I]),
+    "tv_tree_attention": (_I, [_P, _L, _L, _L, _P, _P, _L, _L, _L, _P, _P, _P,
+                               _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
+                               _P, _P, _P, _S, _P, _P]),
+    "tv_accept_workspace_size": (_S, [_I, _I, _I, _I]),
+    "tv_accept_greedy": (_I, [_P, _L, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _S, _P, _P]),
+    "tv_accept_sample": (_I, [_P, _L, _F, _P, _L, _P, _P, _P, _P, _I, _I, _I,
+                              _P, _P, _P, _P, _P, _P, _S, _P, _P]),
+    "tv_status_string": (ctypes.c_char_p, [_I]),
+    "tv_version": (_I, []),
+}
+
+_lib = None
+
+
+class TVError(RuntimeError):
+    pass
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load ``libtv.so`` once and declare every signature."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise TVError("libtv.so is not built (%s); run __graft_entry__.build() or "
+                      "python -m tree_attention_draft_tv_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        msg = load().tv_status_string(code).decode()
+        raise TVError("%s failed: %s (%s)" % (what, STATUS.get(code, code), msg))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise TVError("%s must live on the GPU (got %s)" % (name, t.device))
+    if device is not None and t.device != device:
+        raise TVError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise TVError("workspace too small: %d < %d bytes" %
+                          (workspace.numel() * workspace.element_size(), nbytes))
+        return workspace, workspace.numel() * workspace.element_size()
+    # The caching allocator returns 256-byte aligned blocks.
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+# ----------------------------------------------------------------- mask ---
+
+def build_tree_mask(parent: torch.Tensor, n_nodes: torch.Tensor,
+                    out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Ancestor bitmasks (int32 storage of uint32 words), depths, row status."""
+    lib = load()
+    dev = parent.device
+    _need(parent, "parent", torch.int32)
+    _need(n_nodes, "n_nodes", torch.int32, dev)
+    if parent.dim() != 2 or not parent.is_contiguous():
+        raise TVError("parent must be a contiguous [B, T] tensor")
+    B, T = parent.shape
+    W = (T + 31) // 32
+    if out is None:
+        mask = torch.empty((B, T, W), dtype=torch.int32, device=dev)
+        depth = torch.empty((B, T), dtype=torch.int32, device=dev)
+        status = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        mask, depth, status = out
+    _check(lib.tv_build_tree_mask(_ptr(parent), _ptr(n_nodes), B, T, _ptr(mask), _ptr(depth),
+                                  _ptr(status), _stream(dev)), "tv_build_tree_mask")
+    return mask, depth, status
+
+
+# ------------------------------------------------------------ attention ---
+
+def attention_workspace_size(B, T, Hq, Hkv, D, max_ctx, chunk_keys=0) -> int:
+    n = load().tv_tree_attention_workspace_size(B, T, Hq, Hkv, D, max_ctx, chunk_keys)
+    if n == ctypes.c_size_t(-1).value:
+        raise TVError("invalid attention sizes")
+    return int(n)
+
+
+def auto_chunk(B, T, Hq, Hkv, max_ctx) -> int:
+    return int(load().tv_tree_attention_auto_chunk(B, T, Hq, Hkv, max_ctx))
+
+
+def tree_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ctx_len: torch.Tensor,
+                   n_nodes: torch.Tensor, mask: torch.Tensor, max_ctx: int,
+                   scale: Optional[float] = None, probability_parts: int = 1,
+                   chunk_keys: int = 0, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, row_status: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None):
+    """Tree-masked split-KV GQA attention.
+
+    q: [B, T, Hq, D]; k, v: [B, Hkv, kv_capacity, D] (float32 or bfloat16,
+    D contiguous, any other strides); ctx_len, n_nodes: int32 [B];
+    mask: from :func:`build_tree_mask`. Returns (out float32 [B, T, Hq, D],
+    lse float32 [B, T, Hq], row_status int32 [B]).
+    """
+    lib = load()
+    dev = q.device
+    if q.dtype == torch.bfloat16:
+        dt = TV_BF16
+    elif q.dtype == torch.float32:
+        dt = TV_F32
+    else:
+        raise TypeError("q must be float32 or bfloat16")
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    _need(ctx_len, "ctx_len", torch.int32, dev)
+    _need(n_nodes, "n_nodes", torch.int32, dev)
+    _need(mask, "mask", torch.int32, dev)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise TVError("q must be [B, T, Hq, D] and k, v [B, Hkv, capacity, D]")
+    B, T, Hq, D = q.shape
+    _, Hkv, cap, Dk = k.shape
+    if Dk != D or k.shape[0] != B:
+        raise TVError("q and k disagree on B or D")
+    if q.stride(3) != 1 or k.stride(3) != 1 or v.stride(3) != 1:
+        raise TVError("the head dimension must be contiguous")
+    if k.stride() != v.stride():
+        raise TVError("k and v must share strides")
+    if not mask.is_contiguous() or tuple(mask.shape) != (B, T, (T + 31) // 32):
+        raise TVError("mask must be a contiguous [B, T, ceil(T/32)] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+    if row_status is None:
+        row_status = torch.empty((B,), dtype=torch.int32, device=dev)
+    if not out.is_contiguous() or not lse.is_contiguous():
+        raise TVError("out and lse must be contiguous")
+    nbytes = attention_workspace_size(B, T, Hq, Hkv, D, max_ctx, chunk_keys)
+    ws, ws_bytes = _workspace(nbytes, dev, workspace)
+    _check(lib.tv_tree_attention(
+        _ptr(q), q.stride(0), q.stride(1), q.stride(2),
+        _ptr(k), _ptr(v), k.stride(0), k.stride(1), k.stride(2),
+        _ptr(ctx_len), _ptr(n_nodes), _ptr(mask),
+        B, T, Hq, Hkv, D, int(max_ctx), cap, float(scale), dt, int(probability_parts),
+        int(chunk_keys), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _ptr(row_status),
+        _stream(dev)), "tv_tree_attention")
+    return out, lse, row_status
+
+
+# ----------------------------------------------------------- acceptance ---
+
+def accept_workspace_size(B, T, V, mode) -> int:
+    n = load().tv_accept_workspace_size(B, T, V, mode)
+    if n == ctypes.c_size_t(-1).value:
+        raise TVError("invalid acceptance sizes")
+    return int(n)
+
+
+def _accept_outputs(B, T, dev):
+    return (torch.empty((B,), dtype=torch.int32, device=dev),
+            torch.empty((B, T), dtype=torch.int32, device=dev),
+            torch.empty((B,), dtype=torch.int32, device=dev),
+            torch.empty((B, T), dtype=torch.uint8, device=dev),
+            torch.empty((B,), dtype=torch.int32, device=dev))
+
+
+def _check_logits(logits, name, dev):
+    _need(logits, name, torch.float32, dev)
+    if logits.dim() != 3 or logits.stride(2) != 1 or logits.stride(0) != logits.shape[1] * logits.stride(1):
+        raise TVError("%s must be [B, T, V] with V contiguous and rows evenly strided" % name)
+    return logits.stride(1)
+
+
+def accept_greedy(logits: torch.Tensor, tokens: torch.Tensor, parent: torch.Tensor,
+                  n_nodes: torch.Tensor, outputs=None, workspace: Optional[torch.Tensor] = None):
+    """Greedy acceptance. Returns (accept_len, path, bonus, accept_mask, row_status)."""
+    lib = load()
+    dev = logits.device
+    stride = _check_logits(logits, "logits", dev)
+    B, T, V = logits.shape
+    for t, nm in ((tokens, "tokens"), (parent, "parent")):
+        _need(t, nm, torch.int32, dev)
+        if tuple(t.shape) != (B, T) or not t.is_contiguous():
+            raise TVError("%s must be a contiguous [B, T] tensor" % nm)
+    _need(n_nodes, "n_nodes", torch.int32, dev)
+    outs = outputs if outputs is not None else _accept_outputs(B, T, dev)
+    acc_len, path, bonus, amask, status = outs
+    nbytes = accept_workspace_size(B, T, V, 0)
+    ws, ws_bytes = _workspace(nbytes, dev, workspace)
+    _check(lib.tv_accept_greedy(_ptr(logits), stride, _ptr(tokens), _ptr(parent), _ptr(n_nodes),
+                                B, T, V, _ptr(acc_len), _ptr(path), _ptr(bonus), _ptr(amask),
+                                _ptr(ws), ws_bytes, _ptr(status), _stream(dev)),
+           "tv_accept_greedy")
+    return outs
+
+
+def accept_sample(logits: torch.Tensor, temperature: float, q: torch.Tensor, u: torch.Tensor,
+                  tokens: torch.Tensor, parent: torch.Tensor, n_nodes: torch.Tensor,
+                  outputs=None, workspace: Optional[torch.Tensor] = None):
+    """SpecInfer-style sampling acceptance.
+
+    Returns (accept_len, path, bonus, accept_mask, decision, row_status).
+    """
+    lib = load()
+    dev = logits.device
+    stride = _check_logits(logits, "logits", dev)
+    qstride = _check_logits(q, "q", dev)
+    B, T, V = logits.shape
+    if tuple(q.shape) != (B, T, V):
+        raise TVError("q must match logits' shape")
+    _need(u, "u", torch.float32, dev)
+    if tuple(u.shape) != (B, T) or not u.is_contiguous():
+        raise TVError("u must be a contiguous [B, T] tensor")
+    for t, nm in ((tokens, "tokens"), (parent, "parent")):
+        _need(t, nm, torch.int32, dev)
+        if tuple(t.shape) != (B, T) or not t.is_contiguous():
+            raise TVError("%s must be a contiguous [B, T] tensor" % nm)
+    _need(n_nodes, "n_nodes", torch.int32, dev)
+    if outputs is None:
+        acc_len, path, bonus, amask, status = _accept_outputs(B, T, dev)
+        decision = torch.empty((B, T), dtype=torch.int8, device=dev)
+    else:
+        acc_len, path, bonus, amask, decision, status = outputs
+    nbytes = accept_workspace_size(B, T, V, 1)
+    ws, ws_bytes = _workspace(nbytes, dev, workspace)
+    _check(lib.tv_accept_sample(_ptr(logits), stride, float(temperature), _ptr(q), qstride,
+                                _ptr(u), _ptr(tokens), _ptr(parent), _ptr(n_nodes), B, T, V,
+                                _ptr(acc_len), _ptr(path), _ptr(bonus), _ptr(amask),
+                                _ptr(decision), _ptr(ws), ws_bytes, _ptr(status), _stream(dev)),
+           "tv_accept_sample")
+    return acc_len, path, bonus, amask, decision, status
