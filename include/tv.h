@@ -182,8 +182,8 @@ size_t tv_accept_workspace_size(int B, int T, int V, int mode);
  *   accept_mask uint8 [B][T] 1 on the nodes of path, else 0
  *   row_status int32 [B]: OK, BAD_PARENT, NNODES or BAD_TOKEN
  *
- * Constraints: 1 <= T <= TV_MAX_TREE; V >= 1; logits 16-byte aligned and
- * logits_row_stride >= V, a multiple of 4. Workspace as sized above,
+ * Constraints: 1 <= T <= TV_MAX_TREE; V >= 1; logits_row_stride >= V (any
+ * value: rows need not be 16-byte aligned). Workspace as sized above,
  * 256-byte aligned, no initialisation needed.
  */
 int tv_accept_greedy(const float* logits, int64_t logits_row_stride, const int32_t* tokens,
@@ -216,8 +216,8 @@ int tv_accept_greedy(const float* logits, int64_t logits_row_stride, const int32
  *   decision int8 [B][T]  +1 accepted, 0 rejected, -1 never tested
  *   other outputs as in tv_accept_greedy
  *
- * Constraints as tv_accept_greedy, plus q 16-byte aligned with
- * q_row_stride >= V, a multiple of 4, and temperature > 0.
+ * Constraints as tv_accept_greedy, plus q_row_stride >= V and
+ * temperature > 0.
  */
 int tv_accept_sample(const float* logits, int64_t logits_row_stride, float temperature,
                      const float* q, int64_t q_row_stride, const float* u,

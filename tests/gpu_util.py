@@ -68,6 +68,22 @@ def oracle_attention(w):
                                  w.scale, max_ctx=w.max_ctx, kv_capacity=w.kv_capacity)
 
 
+def bf16_p_bound(w):
+    """Worst-case output error of one-part bf16 probabilities: each P is
+    rounded with relative error <= 2^-9, so |out - exact| <= 2^-9 max|v|
+    over the visible values (plus fp32 accumulation slack). Used for the
+    tiny-context edge cases, where few keys carry all the weight; the
+    measured workloads meet 2e-3 directly."""
+    from oracle import decode
+    vmax = 0.0
+    for b in range(w.B):
+        n = int(w.n_nodes[b])
+        if n:
+            live = decode(w.v[b, :, : int(w.ctx_len[b]) + n], w.dtype)
+            vmax = max(vmax, float(np.abs(live).max()))
+    return max(ATOL_OUT, 2.0 ** -9 * vmax + 1e-5)
+
+
 def check_attention(w, got, want, atol_out=ATOL_OUT, atol_lse=ATOL_LSE):
     out, lse, st = got
     o_ref, l_ref, st_ref = want
@@ -77,8 +93,8 @@ def check_attention(w, got, want, atol_out=ATOL_OUT, atol_lse=ATOL_LSE):
     for b in range(w.B):
         if st_ref[b] == 0:
             live[b, : int(w.n_nodes[b])] = True
-    err_o = np.abs(out - o_ref)[live].max(initial=0.0)
-    err_l = np.abs(lse - l_ref)[live].max(initial=0.0)
+    err_o = np.abs(out[live] - o_ref[live]).max(initial=0.0)
+    err_l = np.abs(lse[live] - l_ref[live]).max(initial=0.0)
     assert err_o <= atol_out, "max |out - oracle| = %g" % err_o
     assert err_l <= atol_lse, "max |lse - oracle| = %g" % err_l
     assert np.all(out[~live] == 0.0)

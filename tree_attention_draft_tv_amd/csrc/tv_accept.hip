@@ -40,7 +40,7 @@ int num_splits(int V) {
   return s;
 }
 
-// Slice [lo, hi) of split s; lo is a multiple of 4.
+// Slice [lo, hi) of split s.
 __device__ __forceinline__ void slice_bounds(int V, int S, int s, int& lo, int& hi) {
   int span = (V + S - 1) / S;
   span = (span + 3) & ~3;
@@ -70,10 +70,19 @@ __global__ __launch_bounds__(kThreads) void argmax_slices_kernel(
   float bv = -INFINITY;
   int bi = INT_MAX;
   const int tid = threadIdx.x;
-  // Each thread walks its elements in increasing index order, so a strict
-  // comparison keeps the lowest index among its equal maxima.
-  int v0 = lo + 4 * tid;
-  const int hi4 = lo + ((hi - lo) & ~3);
+  // Rows need not be 16-byte aligned: up to 3 leading elements are read as
+  // scalars, the body with 16-byte loads, the last < 4 elements as scalars.
+  // Every thread sees its elements in increasing index order (head, body,
+  // tail), so a strict comparison keeps the lowest index among its equal
+  // maxima.
+  const int mis = static_cast<int>((reinterpret_cast<uintptr_t>(row + lo) >> 2) & 3);
+  const int lo_al = min(hi, lo + ((4 - mis) & 3));
+  if (lo + tid < lo_al) {
+    bv = row[lo + tid];
+    bi = lo + tid;
+  }
+  int v0 = lo_al + 4 * tid;
+  const int hi4 = lo_al + ((hi - lo_al) & ~3);
   for (; v0 + 4 * kThreads * 3 < hi4; v0 += 4 * kThreads * 4) {
     float4 x[4];
 #pragma unroll
@@ -81,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void argmax_slices_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int base = v0 + 4 * kThreads * u;
-      if (x[u].x > bv) { bv = x[u].x; bi = base; }
+      if (x[u].x > bv || bi == INT_MAX) { bv = x[u].x; bi = base; }
       if (x[u].y > bv) { bv = x[u].y; bi = base + 1; }
       if (x[u].z > bv) { bv = x[u].z; bi = base + 2; }
       if (x[u].w > bv) { bv = x[u].w; bi = base + 3; }
@@ -89,14 +98,11 @@ __global__ __launch_bounds__(kThreads) void argmax_slices_kernel(
   }
   for (; v0 < hi4; v0 += 4 * kThreads) {
     const float4 x = *reinterpret_cast<const float4*>(row + v0);
-    if (x.x > bv) { bv = x.x; bi = v0; }
+    if (x.x > bv || bi == INT_MAX) { bv = x.x; bi = v0; }
     if (x.y > bv) { bv = x.y; bi = v0 + 1; }
     if (x.z > bv) { bv = x.z; bi = v0 + 2; }
     if (x.w > bv) { bv = x.w; bi = v0 + 3; }
   }
-  // Tail (fewer than 4 elements, only in the last slice when V % 4 != 0):
-  // the elements come after every other one of this slice, so a strict
-  // comparison is still right.
   const int tv = hi4 + tid;
   if (tv < hi) {
     const float x = row[tv];
@@ -480,7 +486,7 @@ extern "C" int tv_accept_greedy(const float* logits, int64_t logits_row_stride,
       !accept_mask || !row_status)
     return TV_ERR_NULL;
   if (!accept_sizes_ok(B, T, V) || logits_row_stride < V) return TV_ERR_SHAPE;
-  if (!tvh::aligned16(logits) || logits_row_stride % 4) return TV_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(logits) & 3u) return TV_ERR_ALIGN;
   if (B == 0) return TV_OK;
   if (!workspace || ws_bytes < greedy_ws(B, T, V) || !tvh::aligned256(workspace))
     return TV_ERR_WORKSPACE;
@@ -506,8 +512,7 @@ extern "C" int tv_accept_sample(const float* logits, int64_t logits_row_stride,
   if (!accept_sizes_ok(B, T, V) || logits_row_stride < V || q_row_stride < V)
     return TV_ERR_SHAPE;
   if (!(temperature > 0.f)) return TV_ERR_SHAPE;
-  if (!tvh::aligned16(logits) || !tvh::aligned16(q) || logits_row_stride % 4 ||
-      q_row_stride % 4)
+  if ((reinterpret_cast<uintptr_t>(logits) & 3u) || (reinterpret_cast<uintptr_t>(q) & 3u))
     return TV_ERR_ALIGN;
   if (B == 0) return TV_OK;
   if (!workspace || ws_bytes < sample_ws(B, T, V) || !tvh::aligned256(workspace))
