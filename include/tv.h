@@ -130,7 +130,7 @@ int tv_tree_attention_auto_chunk(int B, int T, int Hq, int Hkv, int max_ctx);
  *            base + b*kv_sb + g*kv_sh + s*kv_ss + d
  *   ctx_len  int32 [B]; n_nodes int32 [B]; mask from tv_build_tree_mask
  *   max_ctx  host bound on every ctx_len (sizes the grid); kv_capacity slots
- *   scale    softmax scale (1/sqrt(D) is the usual choice)
+ *   scale    softmax scale, finite and > 0 (1/sqrt(D) is the usual choice)
  *   in_dtype TV_F32 (fp32-faithful arithmetic) or TV_BF16 (bf16 matrix cores,
  *            fp32 accumulation)
  *   probability_parts  1..3 (bf16 only): the probabilities enter the P.V

@@ -36,6 +36,8 @@
 //   * Online softmax in the log2 domain with a lazy rescale: the running
 //     max only moves when a row's block max exceeds it by more than 8, so
 //     P stays below 2^8 and the O rescale is rare.
+#include <type_traits>
+
 #include "tv_common.h"
 
 namespace {
@@ -49,12 +51,11 @@ constexpr int kThreads = 256;      // 4 waves
 constexpr int kRowsWave = 64;      // packed rows per wave (4 tiles of 16)
 constexpr int kRT = 4;             // row tiles per wave
 constexpr int kRowsWG = kRowsWave * (kThreads / tv::kWave);
-constexpr int kVtStride = kKB + 8; // bf16 per V^T row: 144 bytes
 constexpr int kRowsWGf32 = 64;     // packed rows per fp32 workgroup (4 lanes each)
 constexpr int kKBf32 = 32;         // keys per fp32 LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescale = 8.0f;   // lazy-rescale threshold (log2 units)
+constexpr float kRefSlack = 32.0f; // P may reach 2^32 above a row's reference max
 
 struct AttnParams {
   const void* q;
@@ -128,23 +129,51 @@ __device__ __forceinline__ bool tree_visible(const uint32_t* s_mask, int W, int 
 
 // ------------------------------------------------------------ bf16 MFMA ---
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+constexpr int kStages = 3;  // LDS ring depth (tiles in flight)
+
+// LDS tiles hold 64 keys of K and V in [key][d] order, rows unpadded, with an
+// XOR swizzle that depends only on the key's low bits:
+//   K: 16-byte chunk c of key k sits at chunk c ^ (k mod D/8);
+//   V: 32-byte chunk c of key k sits at chunk c ^ (k mod D/16 (max 8)).
+// The S^T = K Q^T operand reads 16 consecutive keys at one chunk (distinct
+// bank groups), the transposing V reads take 8 consecutive keys at one
+// chunk (distinct 32-byte groups), and every lane's read addresses differ
+// only by compile-time offsets from a few per-lane bases.
 template <int D>
 __device__ __forceinline__ int k_swz(int key) {
-  constexpr int DCH = D / 8;
-  return ((key & 3) | (((key >> 3) & 3) << 2)) & (DCH - 1);
+  return key & (D / 8 - 1);
 }
+template <int D>
+__device__ __forceinline__ int v_swz(int key) {
+  return key & (D / 16 - 1);
+}
+
+// s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding).
+#define TV_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14))
+
+template <int V>
+using IC = std::integral_constant<int, V>;
 
 template <int D, int PARTS>
 __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p) {
-  constexpr int DCH = D / 8;               // 16-byte chunks per key row
-  constexpr int KS = D / 32;               // MFMA k-steps along D
-  constexpr int DT = D / 16;               // 16-wide d tiles of O
-  constexpr int KLOADS = kKB * DCH / kThreads;   // K chunks per thread per tile
-  constexpr int VITEMS = (kKB / 4) * DCH;        // V (4 keys x 8 d) items per tile
+  constexpr int CH16 = D / 8;                    // 16-byte chunks per key row
+  constexpr int KS = D / 32;                     // MFMA k-steps along D
+  constexpr int DT = D / 16;                     // 16-wide d tiles of O
+  constexpr int LOADS = kKB * CH16 / kThreads;   // 16-byte loads per thread per tensor
+  constexpr int KEYS_PER_LOAD = kThreads / CH16; // keys covered by one load round
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKB * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[2][D * kVtStride];
+  // One LDS object per pipeline stage: the block loop below is unrolled by
+  // the stage count, so every access names its buffer statically and the
+  // compiler can tell the in-flight HBM->LDS copies from the LDS reads.
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[kKB * D], sK1[kKB * D], sK2[kKB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[kKB * D], sV1[kKB * D], sV2[kKB * D];
   __shared__ uint32_t sMask[TV_MAX_TREE * (TV_MAX_TREE / 32)];
+  __shared__ int sOvf;
 
   const int c = blockIdx.x;
   const int rg = blockIdx.y;
@@ -153,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   const int kvh = bk - b * p.Hkv;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   int n, L;
   const int st = seq_check(p, b, n, L);
@@ -163,242 +192,252 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   const bool last = (c == nch - 1);
   const int kbeg = c * p.chunk;
   const int kend = last ? L + n : min(kbeg + p.chunk, L);
+  const int nblk = (kend - kbeg + kKB - 1) / kKB;
+  const int kv_ss = static_cast<int>(p.kv_ss);  // host checks capacity * stride < 2^31
 
-  if (last) {
-    const uint32_t* mrow = p.mask + static_cast<int64_t>(b) * p.T * p.W;
-    for (int idx = tid; idx < n * p.W; idx += kThreads) sMask[idx] = mrow[idx];
-  }
-
-  const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + b * p.kv_sb + kvh * p.kv_sh;
-  const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + b * p.kv_sb + kvh * p.kv_sh;
-
-  // ---- Q fragments (MFMA B operand of S^T = K Q^T) ----
+  // ---- Q fragments (MFMA B operand of S^T = K Q^T), loaded first ----
   const int g = lane >> 4;
   const int l16 = lane & 15;
   const int row0 = rg * kRowsWG + wave * kRowsWave;
-  const int rows_here = min(p.R - row0, kRowsWave);
-  const int ntile = rows_here <= 0 ? 0 : (rows_here + 15) / 16;
+  const bool wave_active = row0 < p.R;
   bf16x8_t qf[kRT][KS];
   int node_rt[kRT];
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     const int r = row0 + rt * 16 + l16;
-    int node = -1;
-    if (r < p.R) {
-      const int i = r / p.G;
-      if (i < n) node = i;
-    }
+    const int i = r / p.G;
+    const int node = (r < p.R && i < n) ? i : -1;
     node_rt[rt] = node;
-    if (node >= 0) {
-      const int h = kvh * p.G + (r - node * p.G);
-      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + b * p.q_sb + node * p.q_st +
-                             h * p.q_sh;
+    const int h = kvh * p.G + (r - i * p.G);
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + b * p.q_sb +
+                           (node < 0 ? 0 : node) * p.q_st + (node < 0 ? 0 : h) * p.q_sh;
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        qf[rt][s] = __builtin_bit_cast(bf16x8_t,
-                                       *reinterpret_cast<const u16x8_t*>(qrow + 32 * s + 8 * g));
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) qf[rt][s] = __builtin_bit_cast(bf16x8_t, u16x8_t(0));
+    for (int s = 0; s < KS; ++s) {
+      const u16x8_t v = *reinterpret_cast<const u16x8_t*>(qrow + 32 * s + 8 * g);
+      qf[rt][s] = __builtin_bit_cast(bf16x8_t, node < 0 ? u16x8_t(0) : v);
     }
   }
+  if (last) {
+    const uint32_t* mrow = p.mask + static_cast<int64_t>(b) * p.T * p.W;
+    for (int idx = tid; idx < n * p.W; idx += kThreads) sMask[idx] = mrow[idx];
+  }
+
+  // ---- tile loads: HBM -> LDS directly (16 bytes per lane; lane i's bytes
+  // land at base + 16 i). The swizzle is applied on the global side: the
+  // lane filling LDS slot (key, chunk) fetches the chunk that belongs there.
+  // A thread's chunk is the same in every load round. Keys at or past kend
+  // are never read: their slots re-read key kend - 1 (finite data that the
+  // softmax gives probability 0). ----
+  const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + b * p.kv_sb + kvh * p.kv_sh;
+  const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + b * p.kv_sb + kvh * p.kv_sh;
+  const int ld_key = tid / CH16;
+  const int ld_pch = tid - ld_key * CH16;
+  const int ld_kch = ld_pch ^ k_swz<D>(ld_key);
+  const int ld_vch = 2 * ((ld_pch >> 1) ^ v_swz<D>(ld_key)) + (ld_pch & 1);
+  auto issue_tile = [&](uint16_t* dK, uint16_t* dV, int blk) __attribute__((always_inline)) {
+    const int key0 = kbeg + blk * kKB + ld_key;
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int row = min(key0 + it * KEYS_PER_LOAD, kend - 1) * kv_ss;
+      const int lds_off = (it * kThreads + wave * tv::kWave) * 8;
+      __builtin_amdgcn_global_load_lds(kbase + row + ld_kch * 8, (lds_void_t*)(dK + lds_off),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + row + ld_vch * 8, (lds_void_t*)(dV + lds_off),
+                                       16, 0, 0);
+    }
+  };
 
   f32x4_t o[DT][kRT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) o[dt][rt] = f32x4_t(0.f);
-  float m_run[kRT], l_run[kRT];
+  float m_run[kRT], m_seen[kRT], l_run[kRT];
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     m_run[rt] = -INFINITY;
-    l_run[rt] = 0.f;
+    m_seen[rt] = -INFINITY;
   }
-
-  // ---- tile loads: global -> registers -> LDS ----
-  u16x8_t kreg[KLOADS];
-  u16x8_t vreg[4];
-  const int vkq = tid & 15;       // V item: keys 4*vkq .. 4*vkq+3
-  const int vdq = tid >> 4;       //         d   8*vdq .. 8*vdq+7
-  const bool v_item = tid < VITEMS;
-
-  auto load_tile = [&](int key0) {
-#pragma unroll
-    for (int it = 0; it < KLOADS; ++it) {
-      const int idx = it * kThreads + tid;
-      const int key = idx / DCH;
-      const int ch = idx - key * DCH;
-      const int s = key0 + key;
-      kreg[it] = (s < kend)
-                     ? *reinterpret_cast<const u16x8_t*>(kbase + s * p.kv_ss + ch * 8)
-                     : u16x8_t(0);
-    }
-    if (v_item) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = key0 + 4 * vkq + j;
-        vreg[j] = (s < kend)
-                      ? *reinterpret_cast<const u16x8_t*>(vbase + s * p.kv_ss + vdq * 8)
-                      : u16x8_t(0);
-      }
-    }
-  };
-  auto store_tile = [&](int stg) {
-#pragma unroll
-    for (int it = 0; it < KLOADS; ++it) {
-      const int idx = it * kThreads + tid;
-      const int key = idx / DCH;
-      const int ch = idx - key * DCH;
-      *reinterpret_cast<u16x8_t*>(&sK[stg][key * D + ((ch ^ k_swz<D>(key)) * 8)]) = kreg[it];
-    }
-    if (v_item) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = static_cast<uint32_t>(vreg[0][e]) |
-                            (static_cast<uint32_t>(vreg[1][e]) << 16);
-        const uint32_t hi = static_cast<uint32_t>(vreg[2][e]) |
-                            (static_cast<uint32_t>(vreg[3][e]) << 16);
-        *reinterpret_cast<uint2*>(&sVt[stg][(8 * vdq + e) * kVtStride + 4 * vkq]) =
-            make_uint2(lo, hi);
-      }
-    }
-  };
-
-  const int nblk = (kend - kbeg + kKB - 1) / kKB;
+  const float cs = p.scale_log2;          // > 0
   const int vis_all_end = min(L, kend);  // keys below this are visible to every row
 
-  load_tile(kbeg);
-  store_tile(0);
-  __syncthreads();
+  // Per-lane LDS read offsets (elements); everything else is a compile-time
+  // offset. K operand: tile t row 16t + l16, chunk (4s + g) ^ swizzle.
+  int k_off[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) k_off[s] = l16 * D + (((4 * s + g) ^ k_swz<D>(l16)) * 8);
+  // V^T operand: key 16hh + 4g + l16/4 (+32 sb), d 16 dt + 4 (l16 % 4).
+  const int vkey = 4 * g + (l16 >> 2);
+  int v_off[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    v_off[dt] = vkey * D + ((dt ^ v_swz<D>(vkey)) * 16) + 4 * (l16 & 3);
 
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int stg = blk & 1;
-    const int key0 = kbeg + blk * kKB;
-    if (blk + 1 < nblk) load_tile(key0 + kKB);
-
-    if (ntile > 0) {
+  // ---- one 64-key tile from LDS buffers (tK, tV) ----
+  auto compute_tile = [&](const uint16_t* tK, const uint16_t* tV, int key0)
+                          __attribute__((always_inline)) {
 #pragma unroll
-      for (int sb = 0; sb < kKB / 32; ++sb) {
-        const int skey0 = key0 + 32 * sb;
-        if (skey0 >= kend) break;
-        // S^T for 32 keys: two 16-key tiles; tile t row m holds key
-        // 8*(m/4) + 4*t + m%4 so that lane group g ends up with keys 8g..8g+7.
-        f32x4_t sacc[2][kRT];
+    for (int sb = 0; sb < kKB / 32; ++sb) {
+      const int skey0 = key0 + 32 * sb;
+      if (skey0 >= kend) break;
+      // S^T for 32 keys: two tiles of 16 consecutive keys. Lane (g, l16)
+      // ends up with S for packed row l16 and keys 16t + 4g + (0..3): the
+      // P^T B-operand k-slot 4t + e of lane group g is key 16t + 4g + e.
+      f32x4_t sacc[2][kRT];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) sacc[t][rt] = f32x4_t(0.f);
-          const int krow = 32 * sb + 8 * (l16 >> 2) + 4 * t + (l16 & 3);
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8_t a = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u16x8_t*>(tK + (32 * sb + 16 * t) * D + k_off[s]));
 #pragma unroll
-          for (int s = 0; s < KS; ++s) {
-            const int ch = 4 * s + g;
-            const bf16x8_t a = __builtin_bit_cast(
-                bf16x8_t,
-                *reinterpret_cast<const u16x8_t*>(&sK[stg][krow * D + ((ch ^ k_swz<D>(krow)) * 8)]));
-#pragma unroll
-            for (int rt = 0; rt < kRT; ++rt)
-              if (rt < ntile)
-                sacc[t][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rt][s], sacc[t][rt], 0,
-                                                                      0, 0);
-          }
+          for (int rt = 0; rt < kRT; ++rt)
+            sacc[t][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a, qf[rt][s], s == 0 ? f32x4_t(0.f) : sacc[t][rt], 0, 0, 0);
         }
-        // ---- scale, mask, online softmax ----
-        const bool full = (skey0 + 32 <= vis_all_end);
-        float x[kRT][8];
+      }
+      // ---- tail sub-blocks: mask invisible keys (tree block, chunk end) ----
+      if (skey0 + 32 > vis_all_end) {
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
+          const int node = node_rt[rt] < 0 ? 0 : node_rt[rt];
 #pragma unroll
           for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              float v = sacc[t][rt][e] * p.scale_log2;
-              if (!full) {
-                const int key = skey0 + 8 * g + 4 * t + e;
-                bool vis = key < vis_all_end;
-                if (!vis && key >= L && key < kend) {
-                  const int node = node_rt[rt];
-                  vis = node >= 0 && tree_visible(sMask, p.W, node, key - L);
-                }
-                if (!vis) v = -INFINITY;
-              }
-              x[rt][4 * t + e] = v;
+              const int key = skey0 + 16 * t + 4 * g + e;
+              const int j = key - L;
+              const uint32_t in_tree = static_cast<uint32_t>(j >= 0) &
+                                       static_cast<uint32_t>(key < kend) &
+                                       static_cast<uint32_t>(node_rt[rt] >= 0);
+              const int jj = in_tree ? j : 0;
+              const uint32_t w = sMask[node * p.W + (jj >> 5)];
+              const uint32_t vis = static_cast<uint32_t>(key < vis_all_end) |
+                                   (in_tree & (w >> (jj & 31)));
+              sacc[t][rt][e] = (vis & 1u) ? sacc[t][rt][e] : -INFINITY;
             }
         }
-        float mx[kRT];
-        bool need_any = false;
+      }
+      // ---- row max against the fixed reference ----
+      // A row's reference max is its first visible block max; afterwards O
+      // is only ever touched by MFMA. A block max more than kRefSlack above
+      // the reference flags the chunk for one recomputation with the exact
+      // chunk max as reference (the running max over the chunk is tracked).
+      bool ovf = false;
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-          float m = x[rt][0];
+      for (int rt = 0; rt < kRT; ++rt) {
+        float m = fmaxf(fmaxf(fmaxf(sacc[0][rt][0], sacc[0][rt][1]),
+                              fmaxf(sacc[0][rt][2], sacc[0][rt][3])),
+                        fmaxf(fmaxf(sacc[1][rt][0], sacc[1][rt][1]),
+                              fmaxf(sacc[1][rt][2], sacc[1][rt][3])));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const float mu = m * cs;  // block max in log2 units
+        m_seen[rt] = fmaxf(m_seen[rt], mu);
+        m_run[rt] = (m_run[rt] == -INFINITY) ? mu : m_run[rt];
+        ovf |= mu > m_run[rt] + kRefSlack;
+      }
+      if (__any(ovf) && lane == 0) sOvf = 1;
+      // ---- P = 2^(s*cs - m), as bf16 parts: the MFMA B operand P^T ----
+      bf16x8_t pb[kRT], pb2[kRT], pb3[kRT];
 #pragma unroll
-          for (int e = 1; e < 8; ++e) m = fmaxf(m, x[rt][e]);
-          m = fmaxf(m, __shfl_xor(m, 16));
-          m = fmaxf(m, __shfl_xor(m, 32));
-          mx[rt] = m;
-          need_any |= (m > m_run[rt] + kRescale);
-        }
-        if (__any(need_any)) {
+      for (int rt = 0; rt < kRT; ++rt) {
+        const float neg_m = (m_run[rt] == -INFINITY) ? 0.f : -m_run[rt];
+        float pr[8];
 #pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) {
-            const bool need = mx[rt] > m_run[rt] + kRescale;
-            const float m_new = need ? mx[rt] : m_run[rt];
-            const float alpha = need ? exp2f(m_run[rt] - m_new) : 1.f;
-            l_run[rt] *= alpha;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
-            m_run[rt] = m_new;
-          }
-        }
-        bf16x8_t pb[kRT], pb2[kRT], pb3[kRT];
+          for (int e = 0; e < 4; ++e)
+            pr[4 * t + e] = __builtin_amdgcn_exp2f(fmaf(sacc[t][rt][e], cs, neg_m));
+        l_run[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+        bf16x8_t h1;
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-          const float mu = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt];
-          u16x8_t h1, h2, h3;
-          float lsum = 0.f;
+        for (int e = 0; e < 8; ++e) h1[e] = static_cast<__bf16>(pr[e]);
+        pb[rt] = h1;
+        if (PARTS > 1) {
+          bf16x8_t h2, h3;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float pr = exp2f(x[rt][e] - mu);
-            lsum += pr;
-            const uint16_t b1 = tv::f32_to_bf16_rne(pr);
-            h1[e] = b1;
-            if (PARTS > 1) {
-              const float r1 = pr - tv::bf16_to_f32(b1);
-              const uint16_t b2 = tv::f32_to_bf16_rne(r1);
-              h2[e] = b2;
-              h3[e] = tv::f32_to_bf16_rne(r1 - tv::bf16_to_f32(b2));
-            }
+            const float r1 = pr[e] - static_cast<float>(h1[e]);
+            h2[e] = static_cast<__bf16>(r1);
+            h3[e] = static_cast<__bf16>(r1 - static_cast<float>(h2[e]));
           }
-          l_run[rt] += lsum;
-          pb[rt] = __builtin_bit_cast(bf16x8_t, h1);
-          if (PARTS > 1) {
-            pb2[rt] = __builtin_bit_cast(bf16x8_t, h2);
-            pb3[rt] = __builtin_bit_cast(bf16x8_t, h3);
-          }
+          pb2[rt] = h2;
+          pb3[rt] = h3;
         }
-        // ---- O^T += V^T P^T over these 32 keys ----
+      }
+      // ---- O^T += V^T P^T over these 32 keys. The V^T A operand needs,
+      // in lane (g, j), V[key of k-slot 4hh + kk][d0 + j]; within each group
+      // of 16 lanes the transposing read hands lane j element j%4 of the
+      // 8 bytes fetched by lanes 4kk + j/4, so lane (g, L) fetches d
+      // d0 + 4(L%4) .. +3 of key 32sb + 16hh + 4g + L/4. ----
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u16x8_t*>(
-                            &sVt[stg][(16 * dt + l16) * kVtStride + 32 * sb + 8 * g]));
+      for (int dt = 0; dt < DT; ++dt) {
+        const s16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(tV + (32 * sb) * D + v_off[dt]));
+        const s16x4_t h1v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(tV + (32 * sb + 16) * D + v_off[dt]));
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(h0, h1v, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) {
-            if (rt < ntile) {
-              o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt], o[dt][rt], 0, 0, 0);
-              if (PARTS > 1)
-                o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb2[rt], o[dt][rt], 0, 0, 0);
-              if (PARTS > 2)
-                o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb3[rt], o[dt][rt], 0, 0, 0);
-            }
-          }
+        for (int rt = 0; rt < kRT; ++rt) {
+          o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt], o[dt][rt], 0, 0, 0);
+          if (PARTS > 1)
+            o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb2[rt], o[dt][rt], 0, 0, 0);
+          if (PARTS > 2)
+            o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb3[rt], o[dt][rt], 0, 0, 0);
         }
       }
     }
+  };
 
-    if (blk + 1 < nblk) store_tile(stg ^ 1);
+  // ---- 3-stage ring: tile blk lives in buffer blk % 3. A second pass runs
+  // only if some row's scores rose more than kRefSlack above its reference.
+#pragma unroll 1
+  for (int attempt = 0; attempt < 2; ++attempt) {
+  if (attempt == 1) {
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) m_run[rt] = m_seen[rt];
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) o[dt][rt] = f32x4_t(0.f);
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) l_run[rt] = 0.f;
+  if (tid == 0) sOvf = 0;
+  issue_tile(sK0, sV0, 0);
+  if (nblk > 1) issue_tile(sK1, sV1, 1);
+  auto step = [&](auto stage, int blk) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
+    // Tile blk has landed once at most one younger tile's loads are pending.
+    if (blk + 1 < nblk)
+      TV_WAIT_VMCNT(2 * LOADS);
+    else
+      TV_WAIT_VMCNT(0);
     __syncthreads();
+    // Tile blk + 2 goes to the buffer tile blk - 1 used; every wave has
+    // finished reading it (barrier above).
+    if (blk + 2 < nblk) {
+      if (S == 0) issue_tile(sK2, sV2, blk + 2);
+      if (S == 1) issue_tile(sK0, sV0, blk + 2);
+      if (S == 2) issue_tile(sK1, sV1, blk + 2);
+    }
+    if (wave_active) {
+      if (S == 0) compute_tile(sK0, sV0, kbeg + blk * kKB);
+      if (S == 1) compute_tile(sK1, sV1, kbeg + blk * kKB);
+      if (S == 2) compute_tile(sK2, sV2, kbeg + blk * kKB);
+    }
+  };
+  for (int blk = 0; blk < nblk; blk += kStages) {
+    step(IC<0>(), blk);
+    if (blk + 1 < nblk) step(IC<1>(), blk + 1);
+    if (blk + 2 < nblk) step(IC<2>(), blk + 2);
+  }
+  __syncthreads();
+  const int again = sOvf;
+  __syncthreads();
+  if (!again) break;
   }
 
   // ---- epilogue ----
+  if (!wave_active) return;
   float l_tot[kRT];
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
@@ -410,7 +449,6 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   const bool direct = (nch == 1);
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
-    if (rt >= ntile) continue;
     const int r = row0 + rt * 16 + l16;
     if (r >= p.R) continue;
     if (direct) {
@@ -681,6 +719,7 @@ extern "C" int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int6
   if (!valid_sizes(B, T, Hq, Hkv, D, max_ctx, chunk_keys) || kv_capacity < 1)
     return TV_ERR_SHAPE;
   if (probability_parts < 1 || probability_parts > 3) return TV_ERR_SHAPE;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return TV_ERR_SHAPE;
   if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
   const int64_t elem_align = in_dtype == TV_BF16 ? 8 : 4;  // 16 bytes
   if (!tvh::aligned16(q) || !tvh::aligned16(k) || !tvh::aligned16(v) || !tvh::aligned16(out) ||
@@ -689,6 +728,7 @@ extern "C" int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int6
   if (q_sb % elem_align || q_st % elem_align || q_sh % elem_align || kv_sb % elem_align ||
       kv_sh % elem_align || kv_ss % elem_align)
     return TV_ERR_ALIGN;
+  if (kv_ss < 0 || static_cast<int64_t>(kv_capacity) * kv_ss + D > INT32_MAX) return TV_ERR_SHAPE;
   if (B == 0) return TV_OK;
   const int chunk = chunk_keys ? chunk_keys : auto_chunk(B, T, Hq, Hkv, max_ctx);
   const size_t need = workspace_bytes(B, T, Hq, Hkv, D, max_ctx, chunk);
