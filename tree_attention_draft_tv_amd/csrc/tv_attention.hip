@@ -47,10 +47,12 @@ typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kKB = 64;            // keys per LDS stage
-constexpr int kThreads = 256;      // 4 waves
-constexpr int kRowsWave = 64;      // packed rows per wave (4 tiles of 16)
-constexpr int kRT = 4;             // row tiles per wave
+constexpr int kThreads = 512;      // 8 waves, two per SIMD
+constexpr int kRowsWave = 32;      // packed rows per wave (2 tiles of 16)
+constexpr int kRT = 2;             // row tiles per wave
 constexpr int kRowsWG = kRowsWave * (kThreads / tv::kWave);
+constexpr int kThreadsF32 = 256;   // fp32 kernel: 4 lanes per packed row
+constexpr int kThreadsCombine = 256;
 constexpr int kRowsWGf32 = 64;     // packed rows per fp32 workgroup (4 lanes each)
 constexpr int kKBf32 = 32;         // keys per fp32 LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
@@ -156,8 +158,52 @@ __device__ __forceinline__ int v_swz(int key) {
 #define TV_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14))
 
+// Workgroup barrier for the LDS ring: waits for this wave's LDS operations
+// only (lgkmcnt(0)), then s_barrier. __syncthreads() would also wait for
+// every outstanding global load (vmcnt(0)), which drains the HBM->LDS copies
+// of the tiles still in flight; the ring's explicit TV_WAIT_VMCNT waits
+// already guarantee that the tile about to be read has landed.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16-byte HBM -> LDS copy per lane (global_load_lds_dwordx4): lane i's bytes
+// land at lds_base + 16 i. Issued as inline assembly so that the compiler
+// does not serialise it against unrelated LDS reads of other ring stages;
+// completion is awaited explicitly with TV_WAIT_VMCNT before the barrier
+// that publishes the tile.
+__device__ __forceinline__ void lds_copy16(const void* gptr, const void* lds_base) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)lds_base));
+  asm volatile(
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gptr), "{m0}"(lds)
+      : "memory");
+}
+
 template <int V>
 using IC = std::integral_constant<int, V>;
+
+// Max over the four lanes l, l^16, l^32, l^48 (the four lane groups that
+// hold the same packed row), with the gfx950 row-swap permutes (no LDS).
+__device__ __forceinline__ float row_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 template <int D, int PARTS>
 __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p) {
@@ -240,10 +286,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
     for (int it = 0; it < LOADS; ++it) {
       const int row = min(key0 + it * KEYS_PER_LOAD, kend - 1) * kv_ss;
       const int lds_off = (it * kThreads + wave * tv::kWave) * 8;
-      __builtin_amdgcn_global_load_lds(kbase + row + ld_kch * 8, (lds_void_t*)(dK + lds_off),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + row + ld_vch * 8, (lds_void_t*)(dV + lds_off),
-                                       16, 0, 0);
+      lds_copy16(kbase + row + ld_kch * 8, dK + lds_off);
+      lds_copy16(vbase + row + ld_vch * 8, dV + lds_off);
     }
   };
 
@@ -269,13 +313,16 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   for (int dt = 0; dt < DT; ++dt)
     v_off[dt] = vkey * D + ((dt ^ v_swz<D>(vkey)) * 16) + 4 * (l16 & 3);
 
+  bool ovf = false;  // some row's block max exceeded its reference by kRefSlack
+
   // ---- one 64-key tile from LDS buffers (tK, tV) ----
-  auto compute_tile = [&](const uint16_t* tK, const uint16_t* tV, int key0)
+  auto compute_tile = [&](auto masked, const uint16_t* tK, const uint16_t* tV, int key0)
                           __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
     for (int sb = 0; sb < kKB / 32; ++sb) {
       const int skey0 = key0 + 32 * sb;
-      if (skey0 >= kend) break;
+      if (MASKED && skey0 >= kend) break;
       // S^T for 32 keys: two tiles of 16 consecutive keys. Lane (g, l16)
       // ends up with S for packed row l16 and keys 16t + 4g + (0..3): the
       // P^T B-operand k-slot 4t + e of lane group g is key 16t + 4g + e.
@@ -293,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
         }
       }
       // ---- tail sub-blocks: mask invisible keys (tree block, chunk end) ----
-      if (skey0 + 32 > vis_all_end) {
+      if (MASKED && skey0 + 32 > vis_all_end) {
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
           const int node = node_rt[rt] < 0 ? 0 : node_rt[rt];
@@ -319,21 +366,18 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
       // is only ever touched by MFMA. A block max more than kRefSlack above
       // the reference flags the chunk for one recomputation with the exact
       // chunk max as reference (the running max over the chunk is tracked).
-      bool ovf = false;
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
         float m = fmaxf(fmaxf(fmaxf(sacc[0][rt][0], sacc[0][rt][1]),
                               fmaxf(sacc[0][rt][2], sacc[0][rt][3])),
                         fmaxf(fmaxf(sacc[1][rt][0], sacc[1][rt][1]),
                               fmaxf(sacc[1][rt][2], sacc[1][rt][3])));
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
+        m = row_max4(m);
         const float mu = m * cs;  // block max in log2 units
         m_seen[rt] = fmaxf(m_seen[rt], mu);
         m_run[rt] = (m_run[rt] == -INFINITY) ? mu : m_run[rt];
         ovf |= mu > m_run[rt] + kRefSlack;
       }
-      if (__any(ovf) && lane == 0) sOvf = 1;
       // ---- P = 2^(s*cs - m), as bf16 parts: the MFMA B operand P^T ----
       bf16x8_t pb[kRT], pb2[kRT], pb3[kRT];
 #pragma unroll
@@ -402,6 +446,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) l_run[rt] = 0.f;
   if (tid == 0) sOvf = 0;
+  ovf = false;
   issue_tile(sK0, sV0, 0);
   if (nblk > 1) issue_tile(sK1, sV1, 1);
   auto step = [&](auto stage, int blk) __attribute__((always_inline)) {
@@ -411,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
       TV_WAIT_VMCNT(2 * LOADS);
     else
       TV_WAIT_VMCNT(0);
-    __syncthreads();
+    lds_barrier();
     // Tile blk + 2 goes to the buffer tile blk - 1 used; every wave has
     // finished reading it (barrier above).
     if (blk + 2 < nblk) {
@@ -420,19 +465,43 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
       if (S == 2) issue_tile(sK1, sV1, blk + 2);
     }
     if (wave_active) {
-      if (S == 0) compute_tile(sK0, sV0, kbeg + blk * kKB);
-      if (S == 1) compute_tile(sK1, sV1, kbeg + blk * kKB);
-      if (S == 2) compute_tile(sK2, sV2, kbeg + blk * kKB);
+      if (S == 0) compute_tile(std::false_type(), sK0, sV0, kbeg + blk * kKB);
+      if (S == 1) compute_tile(std::false_type(), sK1, sV1, kbeg + blk * kKB);
+      if (S == 2) compute_tile(std::false_type(), sK2, sV2, kbeg + blk * kKB);
     }
   };
-  for (int blk = 0; blk < nblk; blk += kStages) {
+  // Blocks whose 64 keys are all visible to every row run unmasked with a
+  // static buffer per stage; the few tail blocks (chunk end, tree block)
+  // follow with masking.
+  const int nfull = max(0, (vis_all_end - kbeg) / kKB);
+  int blk = 0;
+  for (; blk + kStages <= nfull; blk += kStages) {
     step(IC<0>(), blk);
-    if (blk + 1 < nblk) step(IC<1>(), blk + 1);
-    if (blk + 2 < nblk) step(IC<2>(), blk + 2);
+    step(IC<1>(), blk + 1);
+    step(IC<2>(), blk + 2);
   }
-  __syncthreads();
+  if (blk < nfull) step(IC<0>(), blk++);
+  if (blk < nfull) step(IC<1>(), blk++);
+  for (; blk < nblk; ++blk) {
+    const int stg = blk % kStages;
+    TV_WAIT_VMCNT(0);
+    lds_barrier();
+    if (blk + 2 < nblk) {
+      if (stg == 0) issue_tile(sK2, sV2, blk + 2);
+      if (stg == 1) issue_tile(sK0, sV0, blk + 2);
+      if (stg == 2) issue_tile(sK1, sV1, blk + 2);
+    }
+    if (wave_active) {
+      const uint16_t* tK = stg == 0 ? sK0 : (stg == 1 ? sK1 : sK2);
+      const uint16_t* tV = stg == 0 ? sV0 : (stg == 1 ? sV1 : sV2);
+      compute_tile(std::true_type(), tK, tV, kbeg + blk * kKB);
+    }
+  }
+  if (__any(ovf) && lane == 0) sOvf = 1;
+  TV_WAIT_VMCNT(0);
+  lds_barrier();
   const int again = sOvf;
-  __syncthreads();
+  lds_barrier();
   if (!again) break;
   }
 
@@ -440,12 +509,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   if (!wave_active) return;
   float l_tot[kRT];
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
-    float l = l_run[rt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    l_tot[rt] = l;
-  }
+  for (int rt = 0; rt < kRT; ++rt) l_tot[rt] = row_sum4(l_run[rt]);
   const bool direct = (nch == 1);
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
@@ -483,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
 // each holding a quarter of D; keys are staged through LDS 32 at a time.
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_split_f32_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams p) {
   constexpr int DQ = D / 4;
   constexpr int D4 = D / 4;  // float4 per key row
   __shared__ __attribute__((aligned(16))) float sK[kKBf32 * D];
@@ -499,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32_kernel(AttnParams p) 
 
   int n, L;
   const int st = seq_check(p, b, n, L);
-  if (handle_non_live<D>(p, st, b, kvh, c, rg, kRowsWGf32, tid, kThreads)) return;
+  if (handle_non_live<D>(p, st, b, kvh, c, rg, kRowsWGf32, tid, kThreadsF32)) return;
   const int nch = num_chunks(L, p.chunk);
   if (c >= nch) return;
   const bool last = (c == nch - 1);
@@ -507,7 +571,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32_kernel(AttnParams p) 
   const int kend = last ? L + n : min(kbeg + p.chunk, L);
   if (last) {
     const uint32_t* mrow = p.mask + static_cast<int64_t>(b) * p.T * p.W;
-    for (int idx = tid; idx < n * p.W; idx += kThreads) sMask[idx] = mrow[idx];
+    for (int idx = tid; idx < n * p.W; idx += kThreadsF32) sMask[idx] = mrow[idx];
   }
 
   const float* kbase = static_cast<const float*>(p.k) + b * p.kv_sb + kvh * p.kv_sh;
@@ -539,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32_kernel(AttnParams p) 
 
   for (int key0 = kbeg; key0 < kend; key0 += kKBf32) {
     __syncthreads();
-    for (int idx = tid; idx < kKBf32 * D4; idx += kThreads) {
+    for (int idx = tid; idx < kKBf32 * D4; idx += kThreadsF32) {
       const int key = idx / D4;
       const int d4 = idx - key * D4;
       const int s = key0 + key;
@@ -599,13 +663,13 @@ __global__ __launch_bounds__(kThreads) void attn_split_f32_kernel(AttnParams p) 
 // O = sum O_c 2^(m_c - m*) / l*, lse = (m* + log2 l*) ln 2.
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParams p) {
   constexpr int PER = D / tv::kWave;
   const int bk = blockIdx.y;
   const int b = bk / p.Hkv;
   const int kvh = bk - b * p.Hkv;
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * (kThreads / tv::kWave) + (threadIdx.x >> 6);
+  const int r = blockIdx.x * (kThreadsCombine / tv::kWave) + (threadIdx.x >> 6);
   if (r >= p.R) return;
   int n, L;
   if (seq_check(p, b, n, L) != TV_ROW_OK) return;
@@ -684,10 +748,10 @@ void launch_all(const AttnParams& p, int in_dtype, int rowgroups, hipStream_t st
     else
       hipLaunchKernelGGL((attn_split_bf16_kernel<D, 3>), grid, dim3(kThreads), 0, stream, p);
   } else
-    hipLaunchKernelGGL(attn_split_f32_kernel<D>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(attn_split_f32_kernel<D>, grid, dim3(kThreadsF32), 0, stream, p);
   if (p.nchunk > 1) {
     const dim3 cgrid((p.R + 3) / 4, p.B * p.Hkv);
-    hipLaunchKernelGGL(attn_combine_kernel<D>, cgrid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(attn_combine_kernel<D>, cgrid, dim3(kThreadsCombine), 0, stream, p);
   }
 }
 
