@@ -14,28 +14,33 @@
 //     queries": slots at or past ctx_len + n_nodes are never loaded.
 //
 // MI355X design (gfx950, wave64, 160 KB LDS, bf16 MFMA):
-//   * One workgroup (4 waves) per (key chunk, row group, sequence, KV head).
-//     The G query heads of a KV head times the T tree rows form R = G*T
-//     packed rows (row r = node * G + head-in-group); a workgroup holds up
-//     to 256 of them, 64 per wave, so every key and value read from HBM is
-//     used by all G heads and all T nodes at once: the contraction over D
-//     and over keys is dense, so it runs on MFMA (v_mfma_f32_16x16x32_bf16).
+//   * One workgroup (8 waves, two per SIMD) per (key chunk, row group,
+//     sequence, KV head). The G query heads of a KV head times the T tree
+//     rows form R = G*T packed rows (row r = node * G + head-in-group); a
+//     workgroup holds up to 256 of them, 32 per wave, so every key and value
+//     read from HBM is used by all G heads and all T nodes at once: the
+//     contraction over D and over keys is dense, so it runs on MFMA
+//     (v_mfma_f32_16x16x32_bf16).
 //   * Keys are cut into fixed chunks of C keys (split-KV). The last chunk of
 //     a sequence also covers the tree block [L, L + n), so tree masking
 //     only happens there; partial (m, l, O) go to a workspace and a second
 //     kernel merges them with a log-sum-exp combine. A sequence with one
 //     chunk is written directly.
-//   * K and V tiles of 64 keys are double-buffered through LDS: registers
-//     hold the next tile's loads while the waves compute on the current one.
-//     K is stored row-major with an XOR swizzle of its 16-byte chunks; V is
-//     stored transposed (V^T, padded rows) so that the P.V operand reads
-//     eight consecutive keys per lane with one 16-byte LDS load.
+//   * K and V tiles of 64 keys are copied HBM -> LDS with
+//     global_load_lds_dwordx4 (no register staging) into a ring of four
+//     stages, two tiles ahead of the one being read. K is stored with an
+//     XOR swizzle of its 16-byte chunks; V is read transposed with
+//     ds_read_b64_tr_b16, so P.V needs no shuffle.
 //   * S^T = K Q^T is computed so that a lane's accumulators always belong to
-//     one packed row: the per-row softmax max needs only two cross-lane
-//     steps, and P^T lands directly in the MFMA B-operand layout.
-//   * Online softmax in the log2 domain with a lazy rescale: the running
-//     max only moves when a row's block max exceeds it by more than 8, so
-//     P stays below 2^8 and the O rescale is rare.
+//     one packed row and P^T lands directly in the MFMA B-operand layout.
+//   * Softmax in the log2 domain against a fixed per-row reference (the
+//     max of the chunk's first 32 scores): O is never rescaled, the per-key
+//     work is one FMA, one exp2, one add and a max3 per pair, and a pass
+//     whose scores rise more than 2^32 above the reference is redone with
+//     the exact chunk max.
+//   * The loop is software-pipelined over 32-key sub-blocks: the S^T MFMAs
+//     of sub-block j+1 are issued together with the softmax of sub-block j,
+//     so matrix cores and VALU work side by side within a wave.
 #include <type_traits>
 
 #include "tv_common.h"
@@ -46,10 +51,11 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kKB = 64;            // keys per LDS stage
+constexpr int kKB = 64;            // keys per LDS tile
 constexpr int kThreads = 512;      // 8 waves, two per SIMD
 constexpr int kRowsWave = 32;      // packed rows per wave (2 tiles of 16)
 constexpr int kRT = 2;             // row tiles per wave
+constexpr int kRing = 4;           // LDS tiles: one finishing, one current, two in flight
 constexpr int kRowsWG = kRowsWave * (kThreads / tv::kWave);
 constexpr int kThreadsF32 = 256;   // fp32 kernel: 4 lanes per packed row
 constexpr int kThreadsCombine = 256;
@@ -135,8 +141,6 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-constexpr int kStages = 3;  // LDS ring depth (tiles in flight)
-
 // LDS tiles hold 64 keys of K and V in [key][d] order, rows unpadded, with an
 // XOR swizzle that depends only on the key's low bits:
 //   K: 16-byte chunk c of key k sits at chunk c ^ (k mod D/8);
@@ -205,19 +209,26 @@ __device__ __forceinline__ float row_sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// max(a, b, c) in one v_max3_f32. fmaxf on MFMA results makes the compiler
+// quieten each input first (one extra v_max per value); the scores here are
+// never NaN, so that step is not needed.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 template <int D, int PARTS>
 __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p) {
   constexpr int CH16 = D / 8;                    // 16-byte chunks per key row
   constexpr int KS = D / 32;                     // MFMA k-steps along D
   constexpr int DT = D / 16;                     // 16-wide d tiles of O
+  constexpr int TILE = kKB * D;                  // elements per tensor per LDS tile
   constexpr int LOADS = kKB * CH16 / kThreads;   // 16-byte loads per thread per tensor
   constexpr int KEYS_PER_LOAD = kThreads / CH16; // keys covered by one load round
 
-  // One LDS object per pipeline stage: the block loop below is unrolled by
-  // the stage count, so every access names its buffer statically and the
-  // compiler can tell the in-flight HBM->LDS copies from the LDS reads.
-  __shared__ __attribute__((aligned(16))) uint16_t sK0[kKB * D], sK1[kKB * D], sK2[kKB * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV0[kKB * D], sV1[kKB * D], sV2[kKB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kRing * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kRing * TILE];
   __shared__ uint32_t sMask[TV_MAX_TREE * (TV_MAX_TREE / 32)];
   __shared__ int sOvf;
 
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   const bool last = (c == nch - 1);
   const int kbeg = c * p.chunk;
   const int kend = last ? L + n : min(kbeg + p.chunk, L);
-  const int nblk = (kend - kbeg + kKB - 1) / kKB;
+  const int ntile = (kend - kbeg + kKB - 1) / kKB;
   const int kv_ss = static_cast<int>(p.kv_ss);  // host checks capacity * stride < 2^31
 
   // ---- Q fragments (MFMA B operand of S^T = K Q^T), loaded first ----
@@ -273,15 +284,17 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   // lane filling LDS slot (key, chunk) fetches the chunk that belongs there.
   // A thread's chunk is the same in every load round. Keys at or past kend
   // are never read: their slots re-read key kend - 1 (finite data that the
-  // softmax gives probability 0). ----
+  // softmax gives probability 0). Tile t lives in ring stage t mod kRing. ----
   const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + b * p.kv_sb + kvh * p.kv_sh;
   const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + b * p.kv_sb + kvh * p.kv_sh;
   const int ld_key = tid / CH16;
   const int ld_pch = tid - ld_key * CH16;
   const int ld_kch = ld_pch ^ k_swz<D>(ld_key);
   const int ld_vch = 2 * ((ld_pch >> 1) ^ v_swz<D>(ld_key)) + (ld_pch & 1);
-  auto issue_tile = [&](uint16_t* dK, uint16_t* dV, int blk) __attribute__((always_inline)) {
-    const int key0 = kbeg + blk * kKB + ld_key;
+  auto issue_tile = [&](int t) __attribute__((always_inline)) {
+    const int key0 = kbeg + t * kKB + ld_key;
+    uint16_t* dK = sK + (t & (kRing - 1)) * TILE;
+    uint16_t* dV = sV + (t & (kRing - 1)) * TILE;
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
       const int row = min(key0 + it * KEYS_PER_LOAD, kend - 1) * kv_ss;
@@ -290,219 +303,235 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
       lds_copy16(vbase + row + ld_vch * 8, dV + lds_off);
     }
   };
+  // Tile t becomes readable: wait for this thread's copies of it (the next
+  // tile's may stay in flight), publish with a barrier, then reuse the stage
+  // of tile t - 2, which every wave has finished reading, for tile t + 2.
+  auto enter_tile = [&](int t) __attribute__((always_inline)) {
+    if (t + 1 < ntile)
+      TV_WAIT_VMCNT(2 * LOADS);
+    else
+      TV_WAIT_VMCNT(0);
+    lds_barrier();
+    if (t + 2 < ntile) issue_tile(t + 2);
+  };
 
   f32x4_t o[DT][kRT];
-  float m_run[kRT], m_seen[kRT], l_run[kRT];
+  // Per row: mref = the reference max (log2 units) that P = 2^(s cs - mref)
+  // is taken against, m_seen = the exact chunk max once a pass has run;
+  // per lane: lmax = the largest raw score seen, l_run = the partial sum.
+  float mref[kRT], neg_m[kRT], m_seen[kRT], l_run[kRT], lmax[kRT];
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
-    m_run[rt] = -INFINITY;
-    m_seen[rt] = -INFINITY;
-  }
+  for (int rt = 0; rt < kRT; ++rt) mref[rt] = m_seen[rt] = 0.f;
   const float cs = p.scale_log2;          // > 0
   const int vis_all_end = min(L, kend);  // keys below this are visible to every row
 
-  // Per-lane LDS read offsets (elements); everything else is a compile-time
-  // offset. K operand: tile t row 16t + l16, chunk (4s + g) ^ swizzle.
+  // Per-lane LDS read offsets (elements) within a stage. K operand: key
+  // 16t + l16 of the sub-block, chunk (4s + g) ^ swizzle. V^T operand: key
+  // 16hh + 4g + l16/4 of the sub-block, d 16 dt + 4 (l16 % 4).
   int k_off[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) k_off[s] = l16 * D + (((4 * s + g) ^ k_swz<D>(l16)) * 8);
-  // V^T operand: key 16hh + 4g + l16/4 (+32 sb), d 16 dt + 4 (l16 % 4).
   const int vkey = 4 * g + (l16 >> 2);
   int v_off[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
     v_off[dt] = vkey * D + ((dt ^ v_swz<D>(vkey)) * 16) + 4 * (l16 & 3);
 
-  bool ovf = false;  // some row's block max exceeded its reference by kRefSlack
-
-  // ---- one 64-key tile from LDS buffers (tK, tV) ----
-  auto compute_tile = [&](auto masked, const uint16_t* tK, const uint16_t* tV, int key0)
-                          __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked)::value;
+  // S^T for the 32 keys of sub-block sb of tile t: two MFMA tiles of 16
+  // consecutive keys. Lane (g, l16) ends up with S for packed row l16 and
+  // keys 16u + 4g + (0..3): the P^T B-operand k-slot 4u + e of lane group g
+  // is key 16u + 4g + e.
+  auto s_block = [&](int t, int sb, f32x4_t (&sacc)[2][kRT]) __attribute__((always_inline)) {
+    const uint16_t* tK = sK + (t & (kRing - 1)) * TILE + 32 * sb * D;
 #pragma unroll
-    for (int sb = 0; sb < kKB / 32; ++sb) {
-      const int skey0 = key0 + 32 * sb;
-      if (MASKED && skey0 >= kend) break;
-      // S^T for 32 keys: two tiles of 16 consecutive keys. Lane (g, l16)
-      // ends up with S for packed row l16 and keys 16t + 4g + (0..3): the
-      // P^T B-operand k-slot 4t + e of lane group g is key 16t + 4g + e.
-      f32x4_t sacc[2][kRT];
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u16x8_t*>(tK + (32 * sb + 16 * t) * D + k_off[s]));
-#pragma unroll
-          for (int rt = 0; rt < kRT; ++rt)
-            sacc[t][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                a, qf[rt][s], s == 0 ? f32x4_t(0.f) : sacc[t][rt], 0, 0, 0);
-        }
-      }
-      // ---- tail sub-blocks: mask invisible keys (tree block, chunk end) ----
-      if (MASKED && skey0 + 32 > vis_all_end) {
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-          const int node = node_rt[rt] < 0 ? 0 : node_rt[rt];
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int key = skey0 + 16 * t + 4 * g + e;
-              const int j = key - L;
-              const uint32_t in_tree = static_cast<uint32_t>(j >= 0) &
-                                       static_cast<uint32_t>(key < kend) &
-                                       static_cast<uint32_t>(node_rt[rt] >= 0);
-              const int jj = in_tree ? j : 0;
-              const uint32_t w = sMask[node * p.W + (jj >> 5)];
-              const uint32_t vis = static_cast<uint32_t>(key < vis_all_end) |
-                                   (in_tree & (w >> (jj & 31)));
-              sacc[t][rt][e] = (vis & 1u) ? sacc[t][rt][e] : -INFINITY;
-            }
-        }
-      }
-      // ---- row max against the fixed reference ----
-      // A row's reference max is its first visible block max; afterwards O
-      // is only ever touched by MFMA. A block max more than kRefSlack above
-      // the reference flags the chunk for one recomputation with the exact
-      // chunk max as reference (the running max over the chunk is tracked).
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) {
-        float m = fmaxf(fmaxf(fmaxf(sacc[0][rt][0], sacc[0][rt][1]),
-                              fmaxf(sacc[0][rt][2], sacc[0][rt][3])),
-                        fmaxf(fmaxf(sacc[1][rt][0], sacc[1][rt][1]),
-                              fmaxf(sacc[1][rt][2], sacc[1][rt][3])));
-        m = row_max4(m);
-        const float mu = m * cs;  // block max in log2 units
-        m_seen[rt] = fmaxf(m_seen[rt], mu);
-        m_run[rt] = (m_run[rt] == -INFINITY) ? mu : m_run[rt];
-        ovf |= mu > m_run[rt] + kRefSlack;
-      }
-      // ---- P = 2^(s*cs - m), as bf16 parts: the MFMA B operand P^T ----
-      bf16x8_t pb[kRT], pb2[kRT], pb3[kRT];
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) {
-        const float neg_m = (m_run[rt] == -INFINITY) ? 0.f : -m_run[rt];
-        float pr[8];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            pr[4 * t + e] = __builtin_amdgcn_exp2f(fmaf(sacc[t][rt][e], cs, neg_m));
-        l_run[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-        bf16x8_t h1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h1[e] = static_cast<__bf16>(pr[e]);
-        pb[rt] = h1;
-        if (PARTS > 1) {
-          bf16x8_t h2, h3;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float r1 = pr[e] - static_cast<float>(h1[e]);
-            h2[e] = static_cast<__bf16>(r1);
-            h3[e] = static_cast<__bf16>(r1 - static_cast<float>(h2[e]));
-          }
-          pb2[rt] = h2;
-          pb3[rt] = h3;
-        }
-      }
-      // ---- O^T += V^T P^T over these 32 keys. The V^T A operand needs,
-      // in lane (g, j), V[key of k-slot 4hh + kk][d0 + j]; within each group
-      // of 16 lanes the transposing read hands lane j element j%4 of the
-      // 8 bytes fetched by lanes 4kk + j/4, so lane (g, L) fetches d
-      // d0 + 4(L%4) .. +3 of key 32sb + 16hh + 4g + L/4. ----
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const s16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(tV + (32 * sb) * D + v_off[dt]));
-        const s16x4_t h1v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(tV + (32 * sb + 16) * D + v_off[dt]));
+      for (int s = 0; s < KS; ++s) {
         const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, __builtin_shufflevector(h0, h1v, 0, 1, 2, 3, 4, 5, 6, 7));
+            bf16x8_t, *reinterpret_cast<const u16x8_t*>(tK + 16 * u * D + k_off[s]));
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-          o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt], o[dt][rt], 0, 0, 0);
-          if (PARTS > 1)
-            o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb2[rt], o[dt][rt], 0, 0, 0);
-          if (PARTS > 2)
-            o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb3[rt], o[dt][rt], 0, 0, 0);
-        }
+        for (int rt = 0; rt < kRT; ++rt)
+          sacc[u][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a, qf[rt][s], s == 0 ? f32x4_t(0.f) : sacc[u][rt], 0, 0, 0);
       }
     }
   };
+  // Tail sub-blocks: keys a row may not see (tree block, past the chunk end)
+  // become -inf.
+  auto mask_block = [&](int skey0, f32x4_t (&sacc)[2][kRT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      const int node = node_rt[rt] < 0 ? 0 : node_rt[rt];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = skey0 + 16 * u + 4 * g + e;
+          const int j = key - L;
+          const uint32_t in_tree = static_cast<uint32_t>(j >= 0) &
+                                   static_cast<uint32_t>(key < kend) &
+                                   static_cast<uint32_t>(node_rt[rt] >= 0);
+          const int jj = in_tree ? j : 0;
+          const uint32_t w = sMask[node * p.W + (jj >> 5)];
+          const uint32_t vis = static_cast<uint32_t>(key < vis_all_end) |
+                               (in_tree & (w >> (jj & 31)));
+          sacc[u][rt][e] = (vis & 1u) ? sacc[u][rt][e] : -INFINITY;
+        }
+    }
+  };
+  // Row reference from the first scores of the chunk (one cross-lane max).
+  auto take_reference = [&](const f32x4_t (&sacc)[2][kRT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      const float m = max3f(max3f(sacc[0][rt][0], sacc[0][rt][1], sacc[0][rt][2]),
+                            max3f(sacc[0][rt][3], sacc[1][rt][0], sacc[1][rt][1]),
+                            fmaxf(sacc[1][rt][2], sacc[1][rt][3]));
+      mref[rt] = row_max4(m) * cs;
+      neg_m[rt] = (mref[rt] == -INFINITY) ? 0.f : -mref[rt];
+    }
+  };
+  // P = 2^(s cs - mref) as bf16 parts (the MFMA B operand P^T). The lane
+  // max only feeds the end-of-pass overflow test, so no cross-lane step is
+  // needed here.
+  auto softmax_block = [&](const f32x4_t (&sacc)[2][kRT], bf16x8_t (&pb)[PARTS][kRT])
+                           __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      lmax[rt] = max3f(lmax[rt], max3f(sacc[0][rt][0], sacc[0][rt][1], sacc[0][rt][2]),
+                       max3f(sacc[0][rt][3], sacc[1][rt][0], sacc[1][rt][1]));
+      lmax[rt] = max3f(lmax[rt], sacc[1][rt][2], sacc[1][rt][3]);
+      float pr[8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pr[4 * u + e] = __builtin_amdgcn_exp2f(fmaf(sacc[u][rt][e], cs, neg_m[rt]));
+      l_run[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+      bf16x8_t h1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h1[e] = static_cast<__bf16>(pr[e]);
+      pb[0][rt] = h1;
+      if constexpr (PARTS > 1) {
+        bf16x8_t h2, h3;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float r1 = pr[e] - static_cast<float>(h1[e]);
+          h2[e] = static_cast<__bf16>(r1);
+          h3[e] = static_cast<__bf16>(r1 - static_cast<float>(h2[e]));
+        }
+        pb[1][rt] = h2;
+        if constexpr (PARTS > 2) pb[2][rt] = h3;
+      }
+    }
+  };
+  // O^T += V^T P^T over sub-block sb of tile t. The V^T A operand needs, in
+  // lane (g, j), V[key of k-slot 4hh + kk][d0 + j]; within each group of 16
+  // lanes the transposing read hands lane j element j%4 of the 8 bytes
+  // fetched by lanes 4kk + j/4, so lane (g, L) fetches d d0 + 4(L%4) .. +3
+  // of key 16hh + 4g + L/4 of the sub-block.
+  auto pv_block = [&](int t, int sb, const bf16x8_t (&pb)[PARTS][kRT])
+                      __attribute__((always_inline)) {
+    const uint16_t* tV = sV + (t & (kRing - 1)) * TILE + 32 * sb * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const s16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tV + v_off[dt]));
+      const s16x4_t h1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tV + 16 * D + v_off[dt]));
+      const bf16x8_t a =
+          __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+        for (int q = 0; q < PARTS; ++q)
+          o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[q][rt], o[dt][rt], 0, 0, 0);
+    }
+  };
 
-  // ---- 3-stage ring: tile blk lives in buffer blk % 3. A second pass runs
-  // only if some row's scores rose more than kRefSlack above its reference.
+  // ---- passes over the chunk. The first takes each row's reference from
+  // the chunk's first 32 keys; a second runs only if some row's scores rose
+  // more than kRefSlack above it, with the exact chunk max as reference.
+  // Leading tiles whose keys every row sees run software-pipelined: the
+  // S^T MFMAs of the next 32 keys are issued together with the softmax of
+  // the current ones, so the matrix cores and the VALU work side by side.
+  // The remaining tail tiles (tree block, chunk end) run masked, unpipelined.
+  const int nfull = max(0, (vis_all_end - kbeg) / kKB);
 #pragma unroll 1
   for (int attempt = 0; attempt < 2; ++attempt) {
-  if (attempt == 1) {
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) m_run[rt] = m_seen[rt];
-  }
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+      for (int rt = 0; rt < kRT; ++rt) o[dt][rt] = f32x4_t(0.f);
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) o[dt][rt] = f32x4_t(0.f);
-#pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) l_run[rt] = 0.f;
-  if (tid == 0) sOvf = 0;
-  ovf = false;
-  issue_tile(sK0, sV0, 0);
-  if (nblk > 1) issue_tile(sK1, sV1, 1);
-  auto step = [&](auto stage, int blk) __attribute__((always_inline)) {
-    constexpr int S = decltype(stage)::value;
-    // Tile blk has landed once at most one younger tile's loads are pending.
-    if (blk + 1 < nblk)
-      TV_WAIT_VMCNT(2 * LOADS);
-    else
-      TV_WAIT_VMCNT(0);
-    lds_barrier();
-    // Tile blk + 2 goes to the buffer tile blk - 1 used; every wave has
-    // finished reading it (barrier above).
-    if (blk + 2 < nblk) {
-      if (S == 0) issue_tile(sK2, sV2, blk + 2);
-      if (S == 1) issue_tile(sK0, sV0, blk + 2);
-      if (S == 2) issue_tile(sK1, sV1, blk + 2);
+    for (int rt = 0; rt < kRT; ++rt) {
+      l_run[rt] = 0.f;
+      lmax[rt] = -INFINITY;
+      neg_m[rt] = (mref[rt] == -INFINITY) ? 0.f : -mref[rt];
     }
-    if (wave_active) {
-      if (S == 0) compute_tile(std::false_type(), sK0, sV0, kbeg + blk * kKB);
-      if (S == 1) compute_tile(std::false_type(), sK1, sV1, kbeg + blk * kKB);
-      if (S == 2) compute_tile(std::false_type(), sK2, sV2, kbeg + blk * kKB);
+    if (tid == 0) sOvf = 0;
+    bool need_ref = (attempt == 0);
+    issue_tile(0);
+    if (ntile > 1) issue_tile(1);
+    if (nfull > 0) {
+      // Waves without live rows compute on zero queries here rather than
+      // branch: the loop body stays one straight-line block.
+      enter_tile(0);
+      f32x4_t sa[2][kRT], sb[2][kRT];
+      bf16x8_t pb[PARTS][kRT];
+      s_block(0, 0, sa);
+      if (need_ref) take_reference(sa);
+      need_ref = false;
+      int t = 0;
+#pragma unroll 1
+      for (; t + 1 < nfull; ++t) {
+        s_block(t, 1, sb);
+        softmax_block(sa, pb);
+        pv_block(t, 0, pb);
+        enter_tile(t + 1);
+        s_block(t + 1, 0, sa);
+        softmax_block(sb, pb);
+        pv_block(t, 1, pb);
+      }
+      s_block(t, 1, sb);
+      softmax_block(sa, pb);
+      pv_block(t, 0, pb);
+      softmax_block(sb, pb);
+      pv_block(t, 1, pb);
     }
-  };
-  // Blocks whose 64 keys are all visible to every row run unmasked with a
-  // static buffer per stage; the few tail blocks (chunk end, tree block)
-  // follow with masking.
-  const int nfull = max(0, (vis_all_end - kbeg) / kKB);
-  int blk = 0;
-  for (; blk + kStages <= nfull; blk += kStages) {
-    step(IC<0>(), blk);
-    step(IC<1>(), blk + 1);
-    step(IC<2>(), blk + 2);
-  }
-  if (blk < nfull) step(IC<0>(), blk++);
-  if (blk < nfull) step(IC<1>(), blk++);
-  for (; blk < nblk; ++blk) {
-    const int stg = blk % kStages;
+#pragma unroll 1
+    for (int t = nfull; t < ntile; ++t) {
+      enter_tile(t);
+      if (wave_active) {
+#pragma unroll
+        for (int sbk = 0; sbk < 2; ++sbk) {
+          const int skey0 = kbeg + t * kKB + 32 * sbk;
+          if (skey0 < kend) {
+            f32x4_t sacc[2][kRT];
+            bf16x8_t pb[PARTS][kRT];
+            s_block(t, sbk, sacc);
+            if (skey0 + 32 > vis_all_end) mask_block(skey0, sacc);
+            if (need_ref) take_reference(sacc);
+            need_ref = false;
+            softmax_block(sacc, pb);
+            pv_block(t, sbk, pb);
+          }
+        }
+      }
+    }
+    // ---- end of pass: exact chunk max per row and the overflow test ----
+    bool ovf = false;
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      m_seen[rt] = row_max4(lmax[rt]) * cs;
+      ovf |= m_seen[rt] > mref[rt] + kRefSlack;
+    }
+    if (wave_active && __any(ovf) && lane == 0) sOvf = 1;
     TV_WAIT_VMCNT(0);
     lds_barrier();
-    if (blk + 2 < nblk) {
-      if (stg == 0) issue_tile(sK2, sV2, blk + 2);
-      if (stg == 1) issue_tile(sK0, sV0, blk + 2);
-      if (stg == 2) issue_tile(sK1, sV1, blk + 2);
-    }
-    if (wave_active) {
-      const uint16_t* tK = stg == 0 ? sK0 : (stg == 1 ? sK1 : sK2);
-      const uint16_t* tV = stg == 0 ? sV0 : (stg == 1 ? sV1 : sV2);
-      compute_tile(std::true_type(), tK, tV, kbeg + blk * kKB);
-    }
-  }
-  if (__any(ovf) && lane == 0) sOvf = 1;
-  TV_WAIT_VMCNT(0);
-  lds_barrier();
-  const int again = sOvf;
-  lds_barrier();
-  if (!again) break;
+    const int again = sOvf;
+    lds_barrier();
+    if (!again) break;
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) mref[rt] = m_seen[rt];
   }
 
   // ---- epilogue ----
@@ -527,7 +556,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
         const f32x4_t v = o[dt][rt] * inv;
         *reinterpret_cast<float4*>(dst + 16 * dt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
       }
-      if (g == 0) p.lse[orow] = live ? (m_run[rt] + __log2f(l_tot[rt])) * kLn2 : -INFINITY;
+      if (g == 0) p.lse[orow] = live ? (mref[rt] + __log2f(l_tot[rt])) * kLn2 : -INFINITY;
     } else {
       const int64_t prow = (static_cast<int64_t>(bk) * p.nchunk + c) * p.R + r;
       float* dst = p.part_o + prow * D;
@@ -536,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
         const f32x4_t v = o[dt][rt];
         *reinterpret_cast<float4*>(dst + 16 * dt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
       }
-      if (g == 0) p.part_ml[prow] = make_float2(m_run[rt], l_tot[rt]);
+      if (g == 0) p.part_ml[prow] = make_float2(mref[rt], l_tot[rt]);
     }
   }
 }
@@ -658,13 +687,19 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
 }
 
 // ----------------------------------------------------- log-sum-exp merge ---
-// One wave per packed row: merges the chunk partials of sequences with more
+// One wave per packed row merges the chunk partials of sequences with more
 // than one chunk: m* = max m_c, l* = sum l_c 2^(m_c - m*),
 // O = sum O_c 2^(m_c - m*) / l*, lse = (m* + log2 l*) ln 2.
+// Lane c holds chunk c's (m, l) and weight; the partial rows are fetched
+// eight chunks at a time with independent loads (clamped chunk index, zero
+// weight past the end), so the merge is bandwidth- rather than
+// latency-bound.
 
 template <int D>
 __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParams p) {
-  constexpr int PER = D / tv::kWave;
+  constexpr int PER = D / tv::kWave;  // floats per lane (2 at D = 128)
+  typedef float vecf __attribute__((ext_vector_type(PER)));
+  constexpr int U = 8;
   const int bk = blockIdx.y;
   const int b = bk / p.Hkv;
   const int kvh = bk - b * p.Hkv;
@@ -680,29 +715,46 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   const int64_t orow = (static_cast<int64_t>(b) * p.T + i) * p.Hq + h;
   float* dst = p.out + orow * D;
   if (i >= n) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) dst[lane + e * tv::kWave] = 0.f;
+    *reinterpret_cast<vecf*>(dst + PER * lane) = vecf(0.f);
     if (lane == 0) p.lse[orow] = -INFINITY;
     return;
   }
   const int64_t base = static_cast<int64_t>(bk) * p.nchunk * p.R + r;
   float mstar = -INFINITY;
-  for (int cc = 0; cc < nch; ++cc) mstar = fmaxf(mstar, p.part_ml[base + cc * p.R].x);
-  float lstar = 0.f;
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int cc = 0; cc < nch; ++cc) {
-    const float2 ml = p.part_ml[base + cc * p.R];
-    const float w = exp2f(ml.x - mstar);
-    lstar += ml.y * w;
-    const float* src = p.part_o + (base + cc * p.R) * D;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = fmaf(src[lane + e * tv::kWave], w, acc[e]);
+  for (int c0 = 0; c0 < nch; c0 += tv::kWave) {
+    const int cc = c0 + lane;
+    if (cc < nch) mstar = fmaxf(mstar, p.part_ml[base + static_cast<int64_t>(cc) * p.R].x);
   }
-  const float inv = 1.f / lstar;
+  mstar = tv::wave_max(mstar);
+  float lpart = 0.f;
+  vecf acc = vecf(0.f);
+  for (int c0 = 0; c0 < nch; c0 += tv::kWave) {
+    const int cc = c0 + lane;
+    float w = 0.f;
+    if (cc < nch) {
+      const float2 ml = p.part_ml[base + static_cast<int64_t>(cc) * p.R];
+      w = exp2f(ml.x - mstar);
+      lpart = fmaf(ml.y, w, lpart);
+    }
+    const int cnt = min(tv::kWave, nch - c0);
+    for (int k = 0; k < cnt; k += U) {
+      vecf v[U];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) dst[lane + e * tv::kWave] = acc[e] * inv;
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + min(k + u, cnt - 1);
+        v[u] = *reinterpret_cast<const vecf*>(p.part_o + (base + static_cast<int64_t>(c) * p.R) * D +
+                                             PER * lane);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(k + u, 63)));
+        acc += v[u] * (k + u < cnt ? wu : 0.f);
+      }
+    }
+  }
+  const float lstar = tv::wave_sum(lpart);
+  const float inv = 1.f / lstar;
+  *reinterpret_cast<vecf*>(dst + PER * lane) = acc * inv;
   if (lane == 0) p.lse[orow] = (mstar + __log2f(lstar)) * kLn2;
 }
 
