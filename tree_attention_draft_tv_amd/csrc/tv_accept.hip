@@ -150,6 +150,11 @@ __device__ int validate_seq(const int32_t* parent, const int32_t* tokens, int n,
   return TV_ROW_OK;
 }
 
+// One workgroup per sequence (one thread per tree row). Every global load is
+// issued up front (no load waits on another); the row argmaxes are merged
+// from their slice partials eight at a time; the walk itself runs in wave 0,
+// which finds the lowest-index child carrying the argmax token of the current
+// node with two ballots (rows lane and lane + 64) per step.
 __global__ __launch_bounds__(TV_MAX_TREE) void greedy_walk_kernel(
     const ArgBest* __restrict__ part, int S, const int32_t* __restrict__ tokens,
     const int32_t* __restrict__ parent, const int32_t* __restrict__ n_nodes, int T, int V,
@@ -164,11 +169,50 @@ __global__ __launch_bounds__(TV_MAX_TREE) void greedy_walk_kernel(
   __shared__ int s_len, s_bonus;
   const int b = blockIdx.x;
   const int i = threadIdx.x;
-  const int n = n_nodes[b];
-  const int st = validate_seq(parent, tokens, n, T, V, b, &s_flags);
   const int64_t row = static_cast<int64_t>(b) * T + i;
+  const bool in_t = i < T;
+  const int n = n_nodes[b];
+  const int pr = in_t ? parent[row] : -1;
+  const int tk = in_t ? tokens[row] : 0;
+  ArgBest best{-INFINITY, 0x7fffffff};
+  if (in_t) {
+    // Rows past n were never written by the slice pass: read (in bounds) but
+    // unused. Clamped duplicates of the last slice never win a strict test.
+    const ArgBest* pp = part + row * S;
+    best = pp[0];
+    for (int s0 = 1; s0 < S; s0 += 8) {
+      ArgBest o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] = pp[min(s0 + u, S - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (better(o[u].v, o[u].i, best.v, best.i)) best = o[u];
+    }
+  }
+  if (i == 0) s_flags = 0;
+  __syncthreads();
+  const bool n_ok = n >= 0 && n <= T;
+  const bool live = n_ok && i < n;
+  int f = 0;
+  if (live && i > 0) {
+    if (pr < 0 || pr >= i) f |= 1;
+    if (tk < 0 || tk >= V) f |= 2;
+  }
+  if (f) atomicOr(&s_flags, f);
+  if (in_t) {
+    s_arg[i] = best.i;
+    s_par[i] = (live && i > 0) ? pr : -1;
+    s_tok[i] = tk;
+    s_path[i] = -1;
+    s_on[i] = 0;
+  }
+  __syncthreads();
+  const int flags = s_flags;
+  const int st = !n_ok ? TV_ROW_NNODES
+                       : ((flags & 1) ? TV_ROW_BAD_PARENT
+                                      : ((flags & 2) ? TV_ROW_BAD_TOKEN : TV_ROW_OK));
   if (st != TV_ROW_OK || n == 0) {
-    if (i < T) {
+    if (in_t) {
       path[row] = -1;
       accept_mask[row] = 0;
     }
@@ -179,42 +223,34 @@ __global__ __launch_bounds__(TV_MAX_TREE) void greedy_walk_kernel(
     }
     return;
   }
-  if (i < n) {
-    ArgBest best = part[row * S];
-    for (int s = 1; s < S; ++s) {
-      const ArgBest o = part[row * S + s];
-      if (better(o.v, o.i, best.v, best.i)) best = o;
-    }
-    s_arg[i] = best.i;
-    s_par[i] = i == 0 ? -1 : parent[row];
-    s_tok[i] = tokens[row];
-  }
-  if (i < T) {
-    s_path[i] = -1;
-    s_on[i] = 0;
-  }
-  __syncthreads();
-  if (i == 0) {
+  if (i < tv::kWave) {
+    const int c1 = i, c2 = i + tv::kWave;  // candidate child rows of this lane
     int cur = 0, len = 0;
-    s_path[0] = 0;
-    s_on[0] = 1;
+    if (i == 0) {
+      s_path[0] = 0;
+      s_on[0] = 1;
+    }
     for (;;) {
       const int a = s_arg[cur];
-      int nxt = -1;
-      for (int c = cur + 1; c < n; ++c)
-        if (s_par[c] == cur && s_tok[c] == a) { nxt = c; break; }
-      if (nxt < 0) {
-        s_bonus = a;
+      const bool m1 = c1 > cur && c1 < n && s_par[c1] == cur && s_tok[c1] == a;
+      const bool m2 = c2 > cur && c2 < n && s_par[c2] == cur && s_tok[c2] == a;
+      const uint64_t b1 = __ballot(m1);
+      const uint64_t b2 = __ballot(m2);
+      if (b1 == 0 && b2 == 0) {
+        if (i == 0) s_bonus = a;
         break;
       }
-      s_path[++len] = nxt;
-      s_on[nxt] = 1;
-      cur = nxt;
+      cur = b1 ? __builtin_ctzll(b1) : tv::kWave + __builtin_ctzll(b2);
+      ++len;
+      if (i == 0) {
+        s_path[len] = cur;
+        s_on[cur] = 1;
+      }
     }
-    s_len = len;
+    if (i == 0) s_len = len;
   }
   __syncthreads();
-  if (i < T) {
+  if (in_t) {
     path[row] = s_path[i];
     accept_mask[row] = static_cast<uint8_t>(s_on[i]);
   }

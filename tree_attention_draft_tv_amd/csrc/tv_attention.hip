@@ -303,14 +303,15 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
       lds_copy16(vbase + row + ld_vch * 8, dV + lds_off);
     }
   };
-  // Tile t becomes readable: wait for this thread's copies of it (the next
-  // tile's may stay in flight), publish with a barrier, then reuse the stage
-  // of tile t - 2, which every wave has finished reading, for tile t + 2.
+  // Tile t becomes readable: wait for all of this thread's copies, publish
+  // with a barrier, then reuse the stage of tile t - 2, which every wave has
+  // finished reading, for tile t + 2. The wait is vmcnt(0), not a partial
+  // count that would leave tile t + 1 in flight: HBM->LDS copies are not
+  // relied on to complete in issue order (a partial count let a tile be
+  // read before all of it had landed). Tile t + 1 was issued a tile earlier,
+  // so it has usually landed by then anyway.
   auto enter_tile = [&](int t) __attribute__((always_inline)) {
-    if (t + 1 < ntile)
-      TV_WAIT_VMCNT(2 * LOADS);
-    else
-      TV_WAIT_VMCNT(0);
+    TV_WAIT_VMCNT(0);
     lds_barrier();
     if (t + 2 < ntile) issue_tile(t + 2);
   };

@@ -7,10 +7,10 @@
 // step and shared by every layer's attention call.
 //
 // One workgroup per sequence, one lane per tree row. Rows are topologically
-// ordered (parent[i] < i), so the masks are produced level by level with the
-// recurrence mask[i] = mask[parent[i]] | bit(i): every pass resolves every
-// row whose parent is already resolved; the number of passes is the tree
-// depth + 1 and is bounded by T.
+// ordered (parent[i] < i, checked), so row i's mask is the set of rows met
+// walking parent links from i to the root: each lane follows its own chain
+// through the parent array held in LDS (at most i steps), with no barrier
+// per tree level. depth[i] is the number of links walked.
 #include "tv_common.h"
 
 namespace {
@@ -20,64 +20,42 @@ constexpr int kMaxWords = TV_MAX_TREE / 32;
 __global__ __launch_bounds__(TV_MAX_TREE) void build_tree_mask_kernel(
     const int32_t* __restrict__ parent, const int32_t* __restrict__ n_nodes, int T, int W,
     uint32_t* __restrict__ mask, int32_t* __restrict__ depth, int32_t* __restrict__ row_status) {
-  __shared__ uint32_t s_mask[TV_MAX_TREE][kMaxWords];
-  __shared__ int32_t s_depth[TV_MAX_TREE];
-  __shared__ int s_bad;
-
+  __shared__ int32_t s_par[TV_MAX_TREE];
   const int b = blockIdx.x;
   const int i = threadIdx.x;
+  const int64_t row = static_cast<int64_t>(b) * T + i;
+  // Both loads are issued together; neither address depends on the other.
   const int n = n_nodes[b];
+  const int p = (i > 0 && i < T) ? parent[row] : -1;
   const bool nn_ok = (n >= 0 && n <= T);
-
-  if (i == 0) s_bad = nn_ok ? 0 : 1;
-  __syncthreads();
-
-  int p = -1;
   const bool live = nn_ok && i < n;
-  if (live && i > 0) {
-    p = parent[static_cast<int64_t>(b) * T + i];
-    if (p < 0 || p >= i) atomicOr(&s_bad, 2);
-  }
-  for (int w = 0; w < kMaxWords; ++w) s_mask[i][w] = 0u;
-  s_depth[i] = -1;
-  if (live && i == 0) {
-    s_mask[0][0] = 1u;
-    s_depth[0] = 0;
-  }
-  __syncthreads();
+  const bool bad = live && i > 0 && (p < 0 || p >= i);
+  s_par[i] = live ? p : -1;
+  const bool any_bad = __syncthreads_or(bad) != 0;
+  const bool ok = nn_ok && !any_bad;
 
-  if (s_bad == 0) {
-    // Level-synchronous resolution: a row resolves once its parent has. Each
-    // pass ends in a barrier that also reports whether any row is unresolved.
-    for (int pass = 0; pass < T; ++pass) {
-      const bool resolve = live && i > 0 && s_depth[i] < 0 && s_depth[p] >= 0;
-      uint32_t m[kMaxWords];
-      int d = 0;
-      if (resolve) {
-        for (int w = 0; w < kMaxWords; ++w) m[w] = s_mask[p][w];
-        m[i >> 5] |= 1u << (i & 31);
-        d = s_depth[p] + 1;
-      }
-      __syncthreads();
-      if (resolve) {
-        for (int w = 0; w < kMaxWords; ++w) s_mask[i][w] = m[w];
-        s_depth[i] = d;
-      }
-      const bool pending = live && i > 0 && !resolve && s_depth[i] < 0;
-      if (!__syncthreads_or(pending)) break;
+  uint32_t m[kMaxWords];
+#pragma unroll
+  for (int w = 0; w < kMaxWords; ++w) m[w] = 0u;
+  int d = -1;
+  if (ok && live) {
+    int cur = i;
+    d = 0;
+    for (;;) {
+#pragma unroll
+      for (int w = 0; w < kMaxWords; ++w) m[w] |= (cur >> 5) == w ? (1u << (cur & 31)) : 0u;
+      if (cur == 0) break;
+      cur = s_par[cur];
+      ++d;
     }
   }
-  __syncthreads();
-
-  const int64_t row = static_cast<int64_t>(b) * T + i;
   if (i < T) {
-    const bool ok = (s_bad == 0);
-    for (int w = 0; w < W; ++w) mask[row * W + w] = ok ? s_mask[i][w] : 0u;
-    depth[row] = ok ? s_depth[i] : -1;
+#pragma unroll
+    for (int w = 0; w < kMaxWords; ++w)
+      if (w < W) mask[row * W + w] = m[w];
+    depth[row] = d;
   }
-  if (i == 0) {
-    row_status[b] = (s_bad & 1) ? TV_ROW_NNODES : (s_bad ? TV_ROW_BAD_PARENT : TV_ROW_OK);
-  }
+  if (i == 0) row_status[b] = !nn_ok ? TV_ROW_NNODES : (any_bad ? TV_ROW_BAD_PARENT : TV_ROW_OK);
 }
 
 }  // namespace
