@@ -287,8 +287,7 @@ def main():
                             w.name, w.B, w.live_rows, w.Hq, w.Hkv, w.D, int(w.ctx_len.min()),
                             int(w.ctx_len.max()), w.T - 1, w.T, w.V, w.mode),
             "draft_nodes_per_step": nodes,
-            "chunk_keys": args.chunk if args.chunk else tv.auto_chunk(B, T, w.Hq, w.Hkv,
-                                                                      w.max_ctx),
+            "chunk_keys": args.chunk if args.chunk else "balanced on the device",
             "probability_parts": args.parts,
         },
         "roofline": {

@@ -41,6 +41,7 @@
 //   * The loop is software-pipelined over 32-key sub-blocks: the S^T MFMAs
 //     of sub-block j+1 are issued together with the softmax of sub-block j,
 //     so matrix cores and VALU work side by side within a wave.
+#include <algorithm>
 #include <type_traits>
 
 #include "tv_common.h"
@@ -74,12 +75,17 @@ struct AttnParams {
   const int32_t* ctx_len;
   const int32_t* n_nodes;
   const uint32_t* mask;
-  int B, T, Hq, Hkv, G, R, W, max_ctx, kv_capacity, chunk, nchunk, parts;
+  int B, T, Hq, Hkv, G, R, W, max_ctx, kv_capacity, parts;
+  int kunit;    // keys per unit if fixed by the caller, 0 = balanced on the device
+  int rows_wg;  // packed rows per workgroup (one row group)
+  int RG;       // row groups per (sequence, KV head)
+  int nw;       // workgroups launched (a multiple of 8)
   float scale_log2;
   float* out;
   float* lse;
-  float* part_o;    // [B*Hkv][nchunk][R][D], un-normalised
-  float2* part_ml;  // [B*Hkv][nchunk][R]: (running max in log2 units, sum)
+  int32_t* sched;   // [0] keys per unit, [1 + b] first unit of sequence b
+  float* part_o;    // [unit][rows_wg][D], un-normalised
+  float2* part_ml;  // [unit][rows_wg]: (reference max in log2 units, sum)
   int32_t* row_status;
 };
 
@@ -98,37 +104,168 @@ __device__ __forceinline__ int num_chunks(int L, int chunk) {
   return L == 0 ? 1 : (L + chunk - 1) / chunk;
 }
 
-// Output rows of (b, kvh) in [r_lo, r_hi) set to the padding values.
+// Padded (n == 0) and invalid sequences: every output row gets the padding
+// values (O = 0, lse = -inf) and every sequence its status, spread over the
+// whole grid after the units are done.
 template <int D>
-__device__ void zero_rows(const AttnParams& p, int b, int kvh, int r_lo, int r_hi, int tid,
-                          int nthreads) {
+__device__ void finish_non_live(const AttnParams& p) {
   constexpr int D4 = D / 4;
-  const int rows = r_hi - r_lo;
-  for (int idx = tid; idx < rows * D4; idx += nthreads) {
-    const int r = r_lo + idx / D4;
-    const int d4 = idx % D4;
-    const int i = r / p.G;
-    const int h = kvh * p.G + (r - i * p.G);
-    const int64_t orow = (static_cast<int64_t>(b) * p.T + i) * p.Hq + h;
-    reinterpret_cast<float4*>(p.out + orow * D)[d4] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (d4 == 0) p.lse[orow] = -INFINITY;
+  const int nthreads = gridDim.x * blockDim.x;
+  const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int per_seq = p.T * p.Hq * D4;
+  for (int b = 0; b < p.B; ++b) {
+    int n, L;
+    const int st = seq_check(p, b, n, L);
+    if (gtid == b % nthreads) p.row_status[b] = (st == -1) ? TV_ROW_OK : st;
+    if (st == TV_ROW_OK) continue;
+    float4* o = reinterpret_cast<float4*>(p.out + static_cast<int64_t>(b) * p.T * p.Hq * D);
+    float* l = p.lse + static_cast<int64_t>(b) * p.T * p.Hq;
+    for (int idx = gtid; idx < per_seq; idx += nthreads) {
+      o[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (idx % D4 == 0) l[idx / D4] = -INFINITY;
+    }
   }
 }
 
-// Handles sequences that are padded or invalid; returns true if the caller
-// must stop. Also publishes the per-sequence status exactly once.
-template <int D>
-__device__ bool handle_non_live(const AttnParams& p, int st, int b, int kvh, int c, int rg,
-                                int rows_wg, int tid, int nthreads) {
-  if (c == 0 && rg == 0 && kvh == 0 && tid == 0)
-    p.row_status[b] = (st == -1) ? TV_ROW_OK : st;
-  if (st == TV_ROW_OK) return false;
-  if (c == 0) {
-    const int r_lo = rg * rows_wg;
-    const int r_hi = min(p.R, r_lo + rows_wg);
-    zero_rows<D>(p, b, kvh, r_lo, r_hi, tid, nthreads);
+// ------------------------------------------------------------ schedule ---
+// The keys of every live (sequence, KV head, row group) pair are cut into
+// units of K keys (the last unit of a pair also holds the tree block); one
+// workgroup processes one unit at a time. Units are numbered by sequence,
+// then pair, then chunk, so the units of a pair are consecutive. Every wave
+// derives the schedule from ctx_len / n_nodes by itself (no host sync, no
+// inter-workgroup communication); the combine kernel reads K and the first
+// unit of each sequence from the table workgroup 0 writes.
+
+constexpr int kMinUnit = 256;  // smallest balanced unit (keys)
+
+// Committed length of sequence b if it is live, else -1.
+__device__ __forceinline__ int live_len(const AttnParams& p, int b) {
+  int n, L;
+  return seq_check(p, b, n, L) == TV_ROW_OK ? L : -1;
+}
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Every wave loads the committed lengths of the first 64 sequences once
+// (lane b holds sequence b, -1 if not live); longer batches re-read the rest
+// from memory (L2) in each pass.
+__device__ __forceinline__ int lane_len(const AttnParams& p) {
+  const int lane = threadIdx.x & 63;
+  return lane < p.B ? live_len(p, lane) : -1;
+}
+__device__ __forceinline__ int block_len(const AttnParams& p, int b0, int len0) {
+  const int b = b0 + (threadIdx.x & 63);
+  return b0 == 0 ? len0 : (b < p.B ? live_len(p, b) : -1);
+}
+__device__ __forceinline__ int units_of(const AttnParams& p, int L, int K) {
+  return L < 0 ? 0 : num_chunks(L, K) * p.Hkv * p.RG;
+}
+
+// Units of the whole launch (wave-uniform; every lane must call).
+__device__ int total_units(const AttnParams& p, int len0, int K) {
+  int acc = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) acc += units_of(p, block_len(p, b0, len0), K);
+  return wave_sum_i(acc);
+}
+
+// Keys per unit: the caller's fixed chunk, else the smallest multiple of 64
+// (at least kMinUnit) that cuts the launch into at most nw units, so that a
+// single pass of the nw workgroups covers it with the least work per unit.
+__device__ int choose_unit(const AttnParams& p, int len0) {
+  if (p.kunit > 0) return p.kunit;
+  int maxl = 0, keys = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int L = block_len(p, b0, len0);
+    maxl = max(maxl, L);
+    keys += max(L, 0);
   }
-  return true;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) maxl = max(maxl, __shfl_xor(maxl, o));
+  keys = wave_sum_i(keys);
+  const int hi = max(kMinUnit, (maxl + 63) / 64 * 64);  // one unit per pair
+  // Lower bound: the committed keys of all pairs spread evenly over nw
+  // units; rounding each pair up adds at most one unit per pair, so a few
+  // steps of 64 usually reach the answer.
+  const int64_t pair_keys = static_cast<int64_t>(keys) * p.Hkv * p.RG;
+  int lo = static_cast<int>((pair_keys + p.nw - 1) / p.nw);
+  lo = max(kMinUnit, (lo + 63) / 64 * 64);
+  if (lo >= hi) return hi;
+  for (int step = 0; step < 4 && lo < hi; ++step, lo += 64)
+    if (total_units(p, len0, lo) <= p.nw) return lo;
+  if (total_units(p, len0, hi) > p.nw) return hi;
+  int bad = lo - 64;  // units(bad) > nw >= units(hi)
+  int good = hi;
+  while (good - bad > 64) {
+    const int mid = (bad / 64 + good / 64) / 2 * 64;
+    if (total_units(p, len0, mid) <= p.nw)
+      good = mid;
+    else
+      bad = mid;
+  }
+  return good;
+}
+
+// Unit u -> (b, kvh, rg, c) and the pair's unit count nch; false past the
+// last unit (wave-uniform; every lane must call).
+__device__ bool decode_unit(const AttnParams& p, int len0, int K, int u, int& b, int& kvh, int& rg,
+                            int& c, int& nch) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int cnt = units_of(p, block_len(p, b0, len0), K);
+    int inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    const int tot = __shfl(inc, 63);
+    if (u < base + tot) {
+      const uint64_t hit = __ballot(base + inc > u);
+      const int l = __builtin_ctzll(hit);
+      b = b0 + l;
+      const int per_pair = __shfl(cnt, l) / (p.Hkv * p.RG);
+      const int local = u - base - (__shfl(inc, l) - __shfl(cnt, l));
+      nch = per_pair;
+      const int pair = local / per_pair;
+      c = local - pair * per_pair;
+      kvh = pair / p.RG;
+      rg = pair - kvh * p.RG;
+      return true;
+    }
+    base += tot;
+  }
+  return false;
+}
+
+// Table for the combine kernel: K, then the first unit of every sequence.
+__device__ void write_sched(const AttnParams& p, int len0, int K) {
+  const int lane = threadIdx.x & 63;
+  if (lane == 0) p.sched[0] = K;
+  int base = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int cnt = units_of(p, block_len(p, b0, len0), K);
+    int inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    if (b0 + lane < p.B) p.sched[1 + b0 + lane] = base + inc - cnt;
+    base += __shfl(inc, 63);
+  }
+}
+
+// First unit of workgroup w: the nw / 8 workgroups that share w mod 8 (the
+// XCD that hardware dispatch gives them) take one contiguous run of units,
+// so the units of a pair mostly share an L2.
+__device__ __forceinline__ int first_unit(const AttnParams& p) {
+  const int w = blockIdx.x;
+  return (w & 7) * (p.nw >> 3) + (w >> 3);
 }
 
 __device__ __forceinline__ bool tree_visible(const uint32_t* s_mask, int W, int node, int j) {
@@ -232,23 +369,21 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   __shared__ uint32_t sMask[TV_MAX_TREE * (TV_MAX_TREE / 32)];
   __shared__ int sOvf;
 
-  const int c = blockIdx.x;
-  const int rg = blockIdx.y;
-  const int bk = blockIdx.z;
-  const int b = bk / p.Hkv;
-  const int kvh = bk - b * p.Hkv;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int len0 = lane_len(p);
+  const int K = choose_unit(p, len0);
+  if (p.sched && blockIdx.x == 0 && wave == 0) write_sched(p, len0, K);
 
+  // ---- one unit: keys [c K, ...) of (b, kvh), packed rows of row group rg ----
+  auto run_unit = [&](int u, int b, int kvh, int rg, int c, int nch)
+                      __attribute__((always_inline)) {
   int n, L;
-  const int st = seq_check(p, b, n, L);
-  if (handle_non_live<D>(p, st, b, kvh, c, rg, kRowsWG, tid, kThreads)) return;
-  const int nch = num_chunks(L, p.chunk);
-  if (c >= nch) return;
+  seq_check(p, b, n, L);
   const bool last = (c == nch - 1);
-  const int kbeg = c * p.chunk;
-  const int kend = last ? L + n : min(kbeg + p.chunk, L);
+  const int kbeg = c * K;
+  const int kend = last ? L + n : min(kbeg + K, L);
   const int ntile = (kend - kbeg + kKB - 1) / kKB;
   const int kv_ss = static_cast<int>(p.kv_ss);  // host checks capacity * stride < 2^31
 
@@ -384,9 +519,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   auto take_reference = [&](const f32x4_t (&sacc)[2][kRT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
-      const float m = max3f(max3f(sacc[0][rt][0], sacc[0][rt][1], sacc[0][rt][2]),
-                            max3f(sacc[0][rt][3], sacc[1][rt][0], sacc[1][rt][1]),
-                            fmaxf(sacc[1][rt][2], sacc[1][rt][3]));
+      const float m = fmaxf(fmaxf(fmaxf(sacc[0][rt][0], sacc[0][rt][1]),
+                                  fmaxf(sacc[0][rt][2], sacc[0][rt][3])),
+                            fmaxf(fmaxf(sacc[1][rt][0], sacc[1][rt][1]),
+                                  fmaxf(sacc[1][rt][2], sacc[1][rt][3])));
       mref[rt] = row_max4(m) * cs;
       neg_m[rt] = (mref[rt] == -INFINITY) ? 0.f : -mref[rt];
     }
@@ -398,15 +534,15 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
                            __attribute__((always_inline)) {
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
-      lmax[rt] = max3f(lmax[rt], max3f(sacc[0][rt][0], sacc[0][rt][1], sacc[0][rt][2]),
-                       max3f(sacc[0][rt][3], sacc[1][rt][0], sacc[1][rt][1]));
-      lmax[rt] = max3f(lmax[rt], sacc[1][rt][2], sacc[1][rt][3]);
-      float pr[8];
+      float y[8], pr[8];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pr[4 * u + e] = __builtin_amdgcn_exp2f(fmaf(sacc[u][rt][e], cs, neg_m[rt]));
+        for (int e = 0; e < 4; ++e) y[4 * u + e] = fmaf(sacc[u][rt][e], cs, neg_m[rt]);
+      lmax[rt] = fmaxf(fmaxf(fmaxf(lmax[rt], y[0]), fmaxf(y[1], y[2])),
+                       fmaxf(fmaxf(y[3], y[4]), fmaxf(fmaxf(y[5], y[6]), y[7])));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(y[e]);
       l_run[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
       bf16x8_t h1;
 #pragma unroll
@@ -522,8 +658,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
     bool ovf = false;
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
-      m_seen[rt] = row_max4(lmax[rt]) * cs;
-      ovf |= m_seen[rt] > mref[rt] + kRefSlack;
+      const float ymax = row_max4(lmax[rt]);
+      m_seen[rt] = ymax - neg_m[rt];
+      ovf |= ymax > kRefSlack;
     }
     if (wave_active && __any(ovf) && lane == 0) sOvf = 1;
     TV_WAIT_VMCNT(0);
@@ -559,7 +696,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
       }
       if (g == 0) p.lse[orow] = live ? (mref[rt] + __log2f(l_tot[rt])) * kLn2 : -INFINITY;
     } else {
-      const int64_t prow = (static_cast<int64_t>(bk) * p.nchunk + c) * p.R + r;
+      const int64_t prow = static_cast<int64_t>(u) * p.rows_wg + (r - rg * kRowsWG);
       float* dst = p.part_o + prow * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -569,6 +706,16 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
       if (g == 0) p.part_ml[prow] = make_float2(mref[rt], l_tot[rt]);
     }
   }
+  };
+
+  const int u0 = first_unit(p);
+  for (int u = u0;; u += p.nw) {
+    int b, kvh, rg, c, nch;
+    if (!decode_unit(p, len0, K, u, b, kvh, rg, c, nch)) break;
+    if (u != u0) __syncthreads();  // the previous unit's LDS reads are done
+    run_unit(u, b, kvh, rg, c, nch);
+  }
+  finish_non_live<D>(p);
 }
 
 // ---------------------------------------------------------- fp32 (VALU) ---
@@ -584,21 +731,18 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
   __shared__ __attribute__((aligned(16))) float sV[kKBf32 * D];
   __shared__ uint32_t sMask[TV_MAX_TREE * (TV_MAX_TREE / 32)];
 
-  const int c = blockIdx.x;
-  const int rg = blockIdx.y;
-  const int bk = blockIdx.z;
-  const int b = bk / p.Hkv;
-  const int kvh = bk - b * p.Hkv;
   const int tid = threadIdx.x;
+  const int len0 = lane_len(p);
+  const int K = choose_unit(p, len0);
+  if (p.sched && blockIdx.x == 0 && tid < tv::kWave) write_sched(p, len0, K);
 
+  auto run_unit = [&](int u, int b, int kvh, int rg, int c, int nch)
+                      __attribute__((always_inline)) {
   int n, L;
-  const int st = seq_check(p, b, n, L);
-  if (handle_non_live<D>(p, st, b, kvh, c, rg, kRowsWGf32, tid, kThreadsF32)) return;
-  const int nch = num_chunks(L, p.chunk);
-  if (c >= nch) return;
+  seq_check(p, b, n, L);
   const bool last = (c == nch - 1);
-  const int kbeg = c * p.chunk;
-  const int kend = last ? L + n : min(kbeg + p.chunk, L);
+  const int kbeg = c * K;
+  const int kend = last ? L + n : min(kbeg + K, L);
   if (last) {
     const uint32_t* mrow = p.mask + static_cast<int64_t>(b) * p.T * p.W;
     for (int idx = tid; idx < n * p.W; idx += kThreadsF32) sMask[idx] = mrow[idx];
@@ -680,11 +824,21 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
     for (int d = 0; d < DQ; ++d) p.out[orow * D + quarter * DQ + d] = live ? ov[d] * inv : 0.f;
     if (quarter == 0) p.lse[orow] = live ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
   } else {
-    const int64_t prow = (static_cast<int64_t>(bk) * p.nchunk + c) * p.R + r;
+    const int64_t prow = static_cast<int64_t>(u) * p.rows_wg + (r - rg * kRowsWGf32);
 #pragma unroll
     for (int d = 0; d < DQ; ++d) p.part_o[prow * D + quarter * DQ + d] = ov[d];
     if (quarter == 0) p.part_ml[prow] = make_float2(m_run, l_run);
   }
+  };
+
+  const int u0 = first_unit(p);
+  for (int u = u0;; u += p.nw) {
+    int b, kvh, rg, c, nch;
+    if (!decode_unit(p, len0, K, u, b, kvh, rg, c, nch)) break;
+    if (u != u0) __syncthreads();  // the previous unit's LDS reads are done
+    run_unit(u, b, kvh, rg, c, nch);
+  }
+  finish_non_live<D>(p);
 }
 
 // ----------------------------------------------------- log-sum-exp merge ---
@@ -708,9 +862,9 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   const int r = blockIdx.x * (kThreadsCombine / tv::kWave) + (threadIdx.x >> 6);
   if (r >= p.R) return;
   int n, L;
-  if (seq_check(p, b, n, L) != TV_ROW_OK) return;
-  const int nch = num_chunks(L, p.chunk);
-  if (nch == 1) return;
+  if (seq_check(p, b, n, L) != TV_ROW_OK) return;  // padded / invalid: done by the split
+  const int nch = num_chunks(L, p.sched[0]);
+  if (nch == 1) return;                             // written directly by the split
   const int i = r / p.G;
   const int h = kvh * p.G + (r - i * p.G);
   const int64_t orow = (static_cast<int64_t>(b) * p.T + i) * p.Hq + h;
@@ -720,11 +874,15 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
     if (lane == 0) p.lse[orow] = -INFINITY;
     return;
   }
-  const int64_t base = static_cast<int64_t>(bk) * p.nchunk * p.R + r;
+  // Partial row of chunk cc: unit u0 + cc, row r - rg rows_wg of that unit.
+  const int rg = r / p.rows_wg;
+  const int64_t u0 = p.sched[1 + b] + static_cast<int64_t>(kvh * p.RG + rg) * nch;
+  const int64_t base = u0 * p.rows_wg + (r - rg * p.rows_wg);
+  const int64_t stride = p.rows_wg;
   float mstar = -INFINITY;
   for (int c0 = 0; c0 < nch; c0 += tv::kWave) {
     const int cc = c0 + lane;
-    if (cc < nch) mstar = fmaxf(mstar, p.part_ml[base + static_cast<int64_t>(cc) * p.R].x);
+    if (cc < nch) mstar = fmaxf(mstar, p.part_ml[base + cc * stride].x);
   }
   mstar = tv::wave_max(mstar);
   float lpart = 0.f;
@@ -733,7 +891,7 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
     const int cc = c0 + lane;
     float w = 0.f;
     if (cc < nch) {
-      const float2 ml = p.part_ml[base + static_cast<int64_t>(cc) * p.R];
+      const float2 ml = p.part_ml[base + cc * stride];
       w = exp2f(ml.x - mstar);
       lpart = fmaf(ml.y, w, lpart);
     }
@@ -743,8 +901,7 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = c0 + min(k + u, cnt - 1);
-        v[u] = *reinterpret_cast<const vecf*>(p.part_o + (base + static_cast<int64_t>(c) * p.R) * D +
-                                             PER * lane);
+        v[u] = *reinterpret_cast<const vecf*>(p.part_o + (base + c * stride) * D + PER * lane);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -759,17 +916,44 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   if (lane == 0) p.lse[orow] = (mstar + __log2f(lstar)) * kLn2;
 }
 
+// Workgroups per launch: one per compute unit (a multiple of 8), cached per
+// device. 256 (MI355X) if the device cannot be queried.
+int grid_workgroups() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cu < 8)
+      cu = 256;
+    cache[dev] = cu / 8 * 8;
+  }
+  return cache[dev];
+}
+
+int host_chunks(int64_t L, int64_t K) { return L == 0 ? 1 : static_cast<int>((L + K - 1) / K); }
+
+// The unit size the device picks when every sequence is live with max_ctx
+// committed keys (bf16 row groups): the smallest multiple of 64, at least
+// kMinUnit, that gives at most one unit per workgroup.
 int auto_chunk(int B, int T, int Hq, int Hkv, int max_ctx) {
   const int64_t R = static_cast<int64_t>(Hq / Hkv) * T;
-  const int64_t rg = (R + kRowsWG - 1) / kRowsWG;
-  const int64_t units = static_cast<int64_t>(B) * Hkv * rg;
-  const int64_t keys = units * (max_ctx > 0 ? max_ctx : 1);
-  const int64_t target = 512;  // about two workgroups per compute unit
-  int64_t ch = (keys + target - 1) / target;
-  ch = (ch + 63) / 64 * 64;
-  if (ch < 256) ch = 256;
-  if (ch > 8192) ch = 8192;
-  return static_cast<int>(ch);
+  const int64_t pairs = static_cast<int64_t>(B) * Hkv * ((R + kRowsWG - 1) / kRowsWG);
+  const int64_t nw = grid_workgroups();
+  auto units = [&](int K) { return pairs * host_chunks(max_ctx, K); };
+  int lo = kMinUnit;
+  int hi = std::max(kMinUnit, (max_ctx + 63) / 64 * 64);
+  if (units(lo) <= nw) return lo;
+  if (units(hi) > nw) return hi;
+  while (hi - lo > 64) {
+    const int mid = (lo / 64 + hi / 64) / 2 * 64;
+    if (units(mid) <= nw)
+      hi = mid;
+    else
+      lo = mid;
+  }
+  return hi;
 }
 
 bool valid_sizes(int B, int T, int Hq, int Hkv, int D, int max_ctx, int chunk_keys) {
@@ -780,19 +964,41 @@ bool valid_sizes(int B, int T, int Hq, int Hkv, int D, int max_ctx, int chunk_ke
   return true;
 }
 
-size_t workspace_bytes(int B, int T, int Hq, int Hkv, int D, int max_ctx, int chunk) {
-  const int64_t nchunk = max_ctx == 0 ? 1 : (max_ctx + chunk - 1) / chunk;
-  if (nchunk <= 1) return 0;
+// Workspace layout: the schedule table ((1 + B) int32), then partial O
+// [unit][rows_wg][D] fp32, then (m, l) [unit][rows_wg]. Sized for the larger
+// of the bf16 (256 rows per unit) and fp32 (64 rows per unit) kernels. No
+// workspace when every pair is a single unit (written directly).
+struct WsLayout {
+  size_t sched = 0, part_o = 0, part_ml = 0, total = 0;
+};
+
+WsLayout workspace_layout(int B, int T, int Hq, int Hkv, int D, int max_ctx, int chunk_keys) {
+  WsLayout w;
   const int64_t R = static_cast<int64_t>(Hq / Hkv) * T;
-  const int64_t rows = static_cast<int64_t>(B) * Hkv * nchunk * R;
-  const size_t o_bytes = tvh::align_up(static_cast<size_t>(rows) * D * sizeof(float), 256);
-  const size_t ml_bytes = tvh::align_up(static_cast<size_t>(rows) * sizeof(float2), 256);
-  return o_bytes + ml_bytes;
+  const int64_t nw = grid_workgroups();
+  int64_t rows_max = 0;
+  for (const int rows_wg : {kRowsWG, kRowsWGf32}) {
+    const int64_t pairs = static_cast<int64_t>(B) * Hkv * ((R + rows_wg - 1) / rows_wg);
+    int64_t units = 0;
+    if (chunk_keys > 0) {
+      const int64_t nch = host_chunks(max_ctx, chunk_keys);
+      units = nch > 1 ? pairs * nch : 0;
+    } else {
+      units = max_ctx > kMinUnit ? std::max(nw, pairs) : 0;
+    }
+    rows_max = std::max(rows_max, units * rows_wg);
+  }
+  if (rows_max == 0) return w;
+  w.sched = 0;
+  w.part_o = tvh::align_up(static_cast<size_t>(1 + B) * sizeof(int32_t), 256);
+  w.part_ml = w.part_o + tvh::align_up(static_cast<size_t>(rows_max) * D * sizeof(float), 256);
+  w.total = w.part_ml + tvh::align_up(static_cast<size_t>(rows_max) * sizeof(float2), 256);
+  return w;
 }
 
 template <int D>
-void launch_all(const AttnParams& p, int in_dtype, int rowgroups, hipStream_t stream) {
-  const dim3 grid(p.nchunk, rowgroups, p.B * p.Hkv);
+void launch_all(const AttnParams& p, int in_dtype, bool combine, hipStream_t stream) {
+  const dim3 grid(p.nw);
   if (in_dtype == TV_BF16) {
     if (p.parts == 1)
       hipLaunchKernelGGL((attn_split_bf16_kernel<D, 1>), grid, dim3(kThreads), 0, stream, p);
@@ -802,7 +1008,7 @@ void launch_all(const AttnParams& p, int in_dtype, int rowgroups, hipStream_t st
       hipLaunchKernelGGL((attn_split_bf16_kernel<D, 3>), grid, dim3(kThreads), 0, stream, p);
   } else
     hipLaunchKernelGGL(attn_split_f32_kernel<D>, grid, dim3(kThreadsF32), 0, stream, p);
-  if (p.nchunk > 1) {
+  if (combine) {
     const dim3 cgrid((p.R + 3) / 4, p.B * p.Hkv);
     hipLaunchKernelGGL(attn_combine_kernel<D>, cgrid, dim3(kThreadsCombine), 0, stream, p);
   }
@@ -818,8 +1024,7 @@ extern "C" int tv_tree_attention_auto_chunk(int B, int T, int Hq, int Hkv, int m
 extern "C" size_t tv_tree_attention_workspace_size(int B, int T, int Hq, int Hkv, int D,
                                                    int max_ctx, int chunk_keys) {
   if (!valid_sizes(B, T, Hq, Hkv, D, max_ctx, chunk_keys)) return static_cast<size_t>(-1);
-  const int chunk = chunk_keys ? chunk_keys : auto_chunk(B, T, Hq, Hkv, max_ctx);
-  return workspace_bytes(B, T, Hq, Hkv, D, max_ctx, chunk);
+  return workspace_layout(B, T, Hq, Hkv, D, max_ctx, chunk_keys).total;
 }
 
 extern "C" int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
@@ -847,9 +1052,9 @@ extern "C" int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int6
     return TV_ERR_ALIGN;
   if (kv_ss < 0 || static_cast<int64_t>(kv_capacity) * kv_ss + D > INT32_MAX) return TV_ERR_SHAPE;
   if (B == 0) return TV_OK;
-  const int chunk = chunk_keys ? chunk_keys : auto_chunk(B, T, Hq, Hkv, max_ctx);
-  const size_t need = workspace_bytes(B, T, Hq, Hkv, D, max_ctx, chunk);
-  if (need > 0 && (!workspace || ws_bytes < need || !tvh::aligned256(workspace)))
+  if (static_cast<int64_t>(B) * Hkv > 65535) return TV_ERR_SHAPE;
+  const WsLayout ws = workspace_layout(B, T, Hq, Hkv, D, max_ctx, chunk_keys);
+  if (ws.total > 0 && (!workspace || ws_bytes < ws.total || !tvh::aligned256(workspace)))
     return TV_ERR_WORKSPACE;
 
   AttnParams p;
@@ -874,27 +1079,27 @@ extern "C" int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int6
   p.W = (T + 31) / 32;
   p.max_ctx = max_ctx;
   p.kv_capacity = kv_capacity;
-  p.chunk = chunk;
-  p.nchunk = max_ctx == 0 ? 1 : (max_ctx + chunk - 1) / chunk;
   p.parts = probability_parts;
+  p.kunit = chunk_keys;
+  p.rows_wg = in_dtype == TV_BF16 ? kRowsWG : kRowsWGf32;
+  p.RG = (p.R + p.rows_wg - 1) / p.rows_wg;
+  p.nw = grid_workgroups();
   p.scale_log2 = scale * kLog2e;
   p.out = out;
   p.lse = lse;
+  p.sched = nullptr;
   p.part_o = nullptr;
   p.part_ml = nullptr;
-  if (need > 0) {
-    const int64_t rows = static_cast<int64_t>(B) * Hkv * p.nchunk * p.R;
-    p.part_o = static_cast<float*>(workspace);
-    p.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
-                                          tvh::align_up(rows * D * sizeof(float), 256));
+  if (ws.total > 0) {
+    char* base = static_cast<char*>(workspace);
+    p.sched = reinterpret_cast<int32_t*>(base + ws.sched);
+    p.part_o = reinterpret_cast<float*>(base + ws.part_o);
+    p.part_ml = reinterpret_cast<float2*>(base + ws.part_ml);
   }
   p.row_status = row_status;
-  const int rows_wg = in_dtype == TV_BF16 ? kRowsWG : kRowsWGf32;
-  const int rowgroups = (p.R + rows_wg - 1) / rows_wg;
-  if (rowgroups > 65535 || static_cast<int64_t>(B) * Hkv > 65535) return TV_ERR_SHAPE;
   if (D == 128)
-    launch_all<128>(p, in_dtype, rowgroups, stream);
+    launch_all<128>(p, in_dtype, ws.total > 0, stream);
   else
-    launch_all<64>(p, in_dtype, rowgroups, stream);
+    launch_all<64>(p, in_dtype, ws.total > 0, stream);
   return tvh::launch_status();
 }
