@@ -153,9 +153,26 @@ __device__ __forceinline__ int wave_sum_i(int x) {
 // Every wave loads the committed lengths of the first 64 sequences once
 // (lane b holds sequence b, -1 if not live); longer batches re-read the rest
 // from memory (L2) in each pass.
-__device__ __forceinline__ int lane_len(const AttnParams& p) {
+__device__ __forceinline__ int lane_len(const AttnParams& p, int& n0) {
   const int lane = threadIdx.x & 63;
-  return lane < p.B ? live_len(p, lane) : -1;
+  int L = -1;
+  n0 = 0;
+  if (lane < p.B) {
+    int n;
+    if (seq_check(p, lane, n, L) != TV_ROW_OK) L = -1;
+    n0 = n;
+  }
+  return L;
+}
+// (n, L) of live sequence b: from the lane cache for b < 64.
+__device__ __forceinline__ void unit_seq(const AttnParams& p, int b, int len0, int n0, int& n,
+                                         int& L) {
+  if (b < 64) {
+    n = __shfl(n0, b);
+    L = __shfl(len0, b);
+  } else {
+    seq_check(p, b, n, L);
+  }
 }
 __device__ __forceinline__ int block_len(const AttnParams& p, int b0, int len0) {
   const int b = b0 + (threadIdx.x & 63);
@@ -372,7 +389,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int len0 = lane_len(p);
+  int n0;
+  const int len0 = lane_len(p, n0);
   const int K = choose_unit(p, len0);
   if (p.sched && blockIdx.x == 0 && wave == 0) write_sched(p, len0, K);
 
@@ -380,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   auto run_unit = [&](int u, int b, int kvh, int rg, int c, int nch)
                       __attribute__((always_inline)) {
   int n, L;
-  seq_check(p, b, n, L);
+  unit_seq(p, b, len0, n0, n, L);
   const bool last = (c == nch - 1);
   const int kbeg = c * K;
   const int kend = last ? L + n : min(kbeg + K, L);
@@ -732,14 +750,15 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
   __shared__ uint32_t sMask[TV_MAX_TREE * (TV_MAX_TREE / 32)];
 
   const int tid = threadIdx.x;
-  const int len0 = lane_len(p);
+  int n0;
+  const int len0 = lane_len(p, n0);
   const int K = choose_unit(p, len0);
   if (p.sched && blockIdx.x == 0 && tid < tv::kWave) write_sched(p, len0, K);
 
   auto run_unit = [&](int u, int b, int kvh, int rg, int c, int nch)
                       __attribute__((always_inline)) {
   int n, L;
-  seq_check(p, b, n, L);
+  unit_seq(p, b, len0, n0, n, L);
   const bool last = (c == nch - 1);
   const int kbeg = c * K;
   const int kend = last ? L + n : min(kbeg + K, L);
@@ -846,15 +865,15 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
 // than one chunk: m* = max m_c, l* = sum l_c 2^(m_c - m*),
 // O = sum O_c 2^(m_c - m*) / l*, lse = (m* + log2 l*) ln 2.
 // Lane c holds chunk c's (m, l) and weight; the partial rows are fetched
-// eight chunks at a time with independent loads (clamped chunk index, zero
-// weight past the end), so the merge is bandwidth- rather than
-// latency-bound.
+// sixteen chunks at a time with independent loads (clamped chunk index, zero
+// weight past the end), issued together with the (m, l) loads, so the merge
+// is bandwidth- rather than latency-bound.
 
 template <int D>
 __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParams p) {
   constexpr int PER = D / tv::kWave;  // floats per lane (2 at D = 128)
   typedef float vecf __attribute__((ext_vector_type(PER)));
-  constexpr int U = 8;
+  constexpr int U = 16;
   const int bk = blockIdx.y;
   const int b = bk / p.Hkv;
   const int kvh = bk - b * p.Hkv;
@@ -879,38 +898,68 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   const int64_t u0 = p.sched[1 + b] + static_cast<int64_t>(kvh * p.RG + rg) * nch;
   const int64_t base = u0 * p.rows_wg + (r - rg * p.rows_wg);
   const int64_t stride = p.rows_wg;
-  float mstar = -INFINITY;
-  for (int c0 = 0; c0 < nch; c0 += tv::kWave) {
-    const int cc = c0 + lane;
-    if (cc < nch) mstar = fmaxf(mstar, p.part_ml[base + cc * stride].x);
-  }
-  mstar = tv::wave_max(mstar);
-  float lpart = 0.f;
+  auto row_of = [&](int c) __attribute__((always_inline)) {
+    return *reinterpret_cast<const vecf*>(p.part_o + (base + c * stride) * D + PER * lane);
+  };
+  float mstar, lstar;
   vecf acc = vecf(0.f);
-  for (int c0 = 0; c0 < nch; c0 += tv::kWave) {
-    const int cc = c0 + lane;
-    float w = 0.f;
-    if (cc < nch) {
-      const float2 ml = p.part_ml[base + cc * stride];
-      w = exp2f(ml.x - mstar);
-      lpart = fmaf(ml.y, w, lpart);
+  if (nch <= tv::kWave) {
+    // One round trip: lane c's (m, l) and the first U partial rows are
+    // requested together; only the weights wait for the maxima.
+    float2 ml = make_float2(-INFINITY, 0.f);
+    if (lane < nch) ml = p.part_ml[base + lane * stride];
+    vecf v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = row_of(min(u, nch - 1));
+    mstar = tv::wave_max(ml.x);
+    const float w = lane < nch ? exp2f(ml.x - mstar) : 0.f;
+    lstar = tv::wave_sum(ml.y * w);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+      acc += v[u] * (u < nch ? wu : 0.f);
     }
-    const int cnt = min(tv::kWave, nch - c0);
-    for (int k = 0; k < cnt; k += U) {
-      vecf v[U];
+    for (int k = U; k < nch; k += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = row_of(min(k + u, nch - 1));
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int c = c0 + min(k + u, cnt - 1);
-        v[u] = *reinterpret_cast<const vecf*>(p.part_o + (base + c * stride) * D + PER * lane);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(k + u, 63)));
-        acc += v[u] * (k + u < cnt ? wu : 0.f);
+        const float wu =
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(k + u, 63)));
+        acc += v[u] * (k + u < nch ? wu : 0.f);
       }
     }
+  } else {
+    mstar = -INFINITY;
+    for (int c0 = 0; c0 < nch; c0 += tv::kWave) {
+      const int cc = c0 + lane;
+      if (cc < nch) mstar = fmaxf(mstar, p.part_ml[base + cc * stride].x);
+    }
+    mstar = tv::wave_max(mstar);
+    float lpart = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += tv::kWave) {
+      const int cc = c0 + lane;
+      float w = 0.f;
+      if (cc < nch) {
+        const float2 ml = p.part_ml[base + cc * stride];
+        w = exp2f(ml.x - mstar);
+        lpart = fmaf(ml.y, w, lpart);
+      }
+      const int cnt = min(tv::kWave, nch - c0);
+      for (int k = 0; k < cnt; k += U) {
+        vecf v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = row_of(c0 + min(k + u, cnt - 1));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float wu =
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(k + u, 63)));
+          acc += v[u] * (k + u < cnt ? wu : 0.f);
+        }
+      }
+    }
+    lstar = tv::wave_sum(lpart);
   }
-  const float lstar = tv::wave_sum(lpart);
   const float inv = 1.f / lstar;
   *reinterpret_cast<vecf*>(dst + PER * lane) = acc * inv;
   if (lane == 0) p.lse[orow] = (mstar + __log2f(lstar)) * kLn2;
