@@ -12,7 +12,9 @@ import pytest
 import torch
 
 import oracle
+from oracle.decode import decode
 from workloads import make_config, make_custom
+from workloads.gen import bf16_bits_from_f32
 
 from gpu_util import (bf16_p_bound, check_attention, check_greedy, check_sample,
                       oracle_attention, run_attention, run_greedy, run_mask, run_sample, upload)
@@ -129,6 +131,26 @@ def test_attention_probability_parts(parts):
                                    atol_out=bf16_p_bound(w) if parts == 1 else 2e-3)
     if parts == 3:  # probabilities fp32-faithful: only fp32 accumulation error remains
         assert err_o < 2e-5 and err_l < 2e-5, (err_o, err_l)
+
+
+@pytest.mark.parametrize("where,parts", [("committed", 1), ("committed", 3), ("tree", 1),
+                                         ("tree", 3)])
+def test_attention_runaway_scores_redone_with_exact_max(where, parts):
+    # One key is 8x a query vector, so its score lies far above those of the
+    # first keys of its unit: probabilities against that first-keys reference
+    # would run past 2^32, and the unit is redone against its exact max.
+    w = make_custom(111, 2, 14, 2, 128, 50, "bf16", [1500, 90], 32, trie_tokens=False)
+    qf = decode(w.q, w.dtype)
+    b, node, h = 0, 5, 3
+    key = 700 if where == "committed" else int(w.ctx_len[b]) + node
+    w.k[b, h // w.G, key] = bf16_bits_from_f32(8.0 * qf[b, node, h])
+    d = upload(w)
+    mask = _mask_check(w, d)
+    got = run_attention(w, d, mask, chunk_keys=512, parts=parts)
+    want = oracle_attention(w)
+    row = want[0][b, node, h]
+    assert np.abs(row - decode(w.v, w.dtype)[b, h // w.G, key]).max() < 1e-3  # one key dominates
+    check_attention(w, got, want, atol_out=bf16_p_bound(w) if parts == 1 else 2e-3)
 
 
 def test_attention_many_rows_two_row_groups():

@@ -64,7 +64,7 @@ constexpr int kRowsWGf32 = 64;     // packed rows per fp32 workgroup (4 lanes ea
 constexpr int kKBf32 = 32;         // keys per fp32 LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRefSlack = 32.0f; // P may reach 2^32 above a row's reference max
+constexpr float kRowSumLimit = 4294967296.0f;  // 2^32: a row sum above it means P ran away
 
 struct AttnParams {
   const void* q;
@@ -471,11 +471,11 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
 
   f32x4_t o[DT][kRT];
   // Per row: mref = the reference max (log2 units) that P = 2^(s cs - mref)
-  // is taken against, m_seen = the exact chunk max once a pass has run;
-  // per lane: lmax = the largest raw score seen, l_run = the partial sum.
-  float mref[kRT], neg_m[kRT], m_seen[kRT], l_run[kRT], lmax[kRT];
+  // is taken against; per lane: l_run = the partial sum; per row: l_tot =
+  // the row sum after a pass.
+  float mref[kRT], neg_m[kRT], l_run[kRT], l_tot[kRT];
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) mref[rt] = m_seen[rt] = 0.f;
+  for (int rt = 0; rt < kRT; ++rt) mref[rt] = 0.f;
   const float cs = p.scale_log2;          // > 0
   const int vis_all_end = min(L, kend);  // keys below this are visible to every row
 
@@ -545,9 +545,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
       neg_m[rt] = (mref[rt] == -INFINITY) ? 0.f : -mref[rt];
     }
   };
-  // P = 2^(s cs - mref) as bf16 parts (the MFMA B operand P^T). The lane
-  // max only feeds the end-of-pass overflow test, so no cross-lane step is
-  // needed here.
+  // P = 2^(s cs - mref) as bf16 parts (the MFMA B operand P^T). No running
+  // max is kept: a score far above the reference shows up in the row sum.
   auto softmax_block = [&](const f32x4_t (&sacc)[2][kRT], bf16x8_t (&pb)[PARTS][kRT])
                            __attribute__((always_inline)) {
 #pragma unroll
@@ -557,8 +556,6 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[4 * u + e] = fmaf(sacc[u][rt][e], cs, neg_m[rt]);
-      lmax[rt] = fmaxf(fmaxf(fmaxf(lmax[rt], y[0]), fmaxf(y[1], y[2])),
-                       fmaxf(fmaxf(y[3], y[4]), fmaxf(fmaxf(y[5], y[6]), y[7])));
 #pragma unroll
       for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(y[e]);
       l_run[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
@@ -603,15 +600,16 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   };
 
   // ---- passes over the chunk. The first takes each row's reference from
-  // the chunk's first 32 keys; a second runs only if some row's scores rose
-  // more than kRefSlack above it, with the exact chunk max as reference.
+  // the chunk's first 32 keys. If some row's sum l exceeds 2^32 (or is not
+  // finite), a score rose far above that reference (P <= l): then a
+  // max-only pass finds the exact chunk max per row and a second pass runs
+  // with it as reference, where every P <= 1.
   // Leading tiles whose keys every row sees run software-pipelined: the
   // S^T MFMAs of the next 32 keys are issued together with the softmax of
   // the current ones, so the matrix cores and the VALU work side by side.
   // The remaining tail tiles (tree block, chunk end) run masked, unpipelined.
   const int nfull = max(0, (vis_all_end - kbeg) / kKB);
-#pragma unroll 1
-  for (int attempt = 0; attempt < 2; ++attempt) {
+  auto run_pass = [&](const int attempt) __attribute__((always_inline)) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -619,7 +617,6 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
       l_run[rt] = 0.f;
-      lmax[rt] = -INFINITY;
       neg_m[rt] = (mref[rt] == -INFINITY) ? 0.f : -mref[rt];
     }
     if (tid == 0) sOvf = 0;
@@ -672,29 +669,61 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
         }
       }
     }
-    // ---- end of pass: exact chunk max per row and the overflow test ----
+    // ---- end of pass: row sums and the runaway test ----
     bool ovf = false;
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
-      const float ymax = row_max4(lmax[rt]);
-      m_seen[rt] = ymax - neg_m[rt];
-      ovf |= ymax > kRefSlack;
+      l_tot[rt] = row_sum4(l_run[rt]);
+      ovf |= !(l_tot[rt] <= kRowSumLimit);
     }
     if (wave_active && __any(ovf) && lane == 0) sOvf = 1;
     TV_WAIT_VMCNT(0);
     lds_barrier();
     const int again = sOvf;
     lds_barrier();
-    if (!again) break;
+    return again;
+  };
+  // The common case is a single pass; the retry is a separate copy of the
+  // pass (no loop around it), so the first pass's code and registers are
+  // not shaped by a loop-carried second attempt.
+  // Exact max of the visible scores of every row over the whole chunk.
+  auto max_pass = [&]() {
+    float lm[kRT];
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) mref[rt] = m_seen[rt];
+    for (int rt = 0; rt < kRT; ++rt) lm[rt] = -INFINITY;
+    issue_tile(0);
+    if (ntile > 1) issue_tile(1);
+#pragma unroll 1
+    for (int t = 0; t < ntile; ++t) {
+      enter_tile(t);
+#pragma unroll
+      for (int sbk = 0; sbk < 2; ++sbk) {
+        const int skey0 = kbeg + t * kKB + 32 * sbk;
+        if (skey0 < kend) {
+          f32x4_t sacc[2][kRT];
+          s_block(t, sbk, sacc);
+          if (skey0 + 32 > vis_all_end) mask_block(skey0, sacc);
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) lm[rt] = fmaxf(lm[rt], sacc[u][rt][e]);
+        }
+      }
+    }
+    TV_WAIT_VMCNT(0);
+    lds_barrier();
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) mref[rt] = row_max4(lm[rt]) * cs;
+  };
+  if (run_pass(0)) {
+    max_pass();
+    run_pass(1);
   }
 
   // ---- epilogue ----
   if (!wave_active) return;
-  float l_tot[kRT];
-#pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) l_tot[rt] = row_sum4(l_run[rt]);
   const bool direct = (nch == 1);
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
