@@ -168,8 +168,8 @@ __device__ __forceinline__ int lane_len(const AttnParams& p, int& n0) {
 __device__ __forceinline__ void unit_seq(const AttnParams& p, int b, int len0, int n0, int& n,
                                          int& L) {
   if (b < 64) {
-    n = __shfl(n0, b);
-    L = __shfl(len0, b);
+    n = __builtin_amdgcn_readlane(n0, b);
+    L = __builtin_amdgcn_readlane(len0, b);
   } else {
     seq_check(p, b, n, L);
   }
@@ -178,8 +178,27 @@ __device__ __forceinline__ int block_len(const AttnParams& p, int b0, int len0) 
   const int b = b0 + (threadIdx.x & 63);
   return b0 == 0 ? len0 : (b < p.B ? live_len(p, b) : -1);
 }
+// Balanced units: the tree block (masked, unpipelined) costs about as much as
+// this many committed keys, so the last unit of a pair, which holds it, gets
+// that many fewer committed keys.
+constexpr int kTreeExtra = 128;
+
+// Units of a pair with L committed keys and K keys per unit.
+__device__ __forceinline__ int pair_units(const AttnParams& p, int L, int K) {
+  const int x = p.kunit > 0 ? 0 : kTreeExtra;
+  return L == 0 ? 1 : (L + x + K - 1) / K;
+}
+// First committed key of unit c of a pair: c K for fixed chunks; in balanced
+// mode the units split L + kTreeExtra evenly, boundaries rounded down to
+// whole 64-key tiles. Since K >= 2 kTreeExtra, the last unit keeps at least
+// one committed key and every unit at most K + 63 keys.
+__device__ __forceinline__ int unit_start(const AttnParams& p, int L, int K, int nch, int c) {
+  if (p.kunit > 0) return min(c * K, L);
+  return static_cast<int>(static_cast<int64_t>(c) * (L + kTreeExtra) / nch) & ~63;
+}
+
 __device__ __forceinline__ int units_of(const AttnParams& p, int L, int K) {
-  return L < 0 ? 0 : num_chunks(L, K) * p.Hkv * p.RG;
+  return L < 0 ? 0 : pair_units(p, L, K) * p.Hkv * p.RG;
 }
 
 // Units of the whole launch (wave-uniform; every lane must call).
@@ -203,7 +222,10 @@ __device__ int choose_unit(const AttnParams& p, int len0) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) maxl = max(maxl, __shfl_xor(maxl, o));
   keys = wave_sum_i(keys);
-  const int hi = max(kMinUnit, (maxl + 63) / 64 * 64);  // one unit per pair
+  // One unit per pair (L + kTreeExtra <= hi). Also the only choice when the
+  // caller passed no workspace for partials.
+  const int hi = max(kMinUnit, (maxl + kTreeExtra + 63) / 64 * 64);
+  if (p.part_o == nullptr) return hi;
   // Lower bound: the committed keys of all pairs spread evenly over nw
   // units; rounding each pair up adds at most one unit per pair, so a few
   // steps of 64 usually reach the answer.
@@ -400,8 +422,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   int n, L;
   unit_seq(p, b, len0, n0, n, L);
   const bool last = (c == nch - 1);
-  const int kbeg = c * K;
-  const int kend = last ? L + n : min(kbeg + K, L);
+  const int kbeg = unit_start(p, L, K, nch, c);
+  const int kend = last ? L + n : unit_start(p, L, K, nch, c + 1);
   const int ntile = (kend - kbeg + kKB - 1) / kKB;
   const int kv_ss = static_cast<int>(p.kv_ss);  // host checks capacity * stride < 2^31
 
@@ -789,8 +811,8 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
   int n, L;
   unit_seq(p, b, len0, n0, n, L);
   const bool last = (c == nch - 1);
-  const int kbeg = c * K;
-  const int kend = last ? L + n : min(kbeg + K, L);
+  const int kbeg = unit_start(p, L, K, nch, c);
+  const int kend = last ? L + n : unit_start(p, L, K, nch, c + 1);
   if (last) {
     const uint32_t* mrow = p.mask + static_cast<int64_t>(b) * p.T * p.W;
     for (int idx = tid; idx < n * p.W; idx += kThreadsF32) sMask[idx] = mrow[idx];
@@ -911,7 +933,7 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   if (r >= p.R) return;
   int n, L;
   if (seq_check(p, b, n, L) != TV_ROW_OK) return;  // padded / invalid: done by the split
-  const int nch = num_chunks(L, p.sched[0]);
+  const int nch = pair_units(p, L, p.sched[0]);
   if (nch == 1) return;                             // written directly by the split
   const int i = r / p.G;
   const int h = kvh * p.G + (r - i * p.G);
@@ -1062,7 +1084,8 @@ WsLayout workspace_layout(int B, int T, int Hq, int Hkv, int D, int max_ctx, int
       const int64_t nch = host_chunks(max_ctx, chunk_keys);
       units = nch > 1 ? pairs * nch : 0;
     } else {
-      units = max_ctx > kMinUnit ? std::max(nw, pairs) : 0;
+      // Every pair is one unit when max_ctx + kTreeExtra <= kMinUnit.
+      units = max_ctx + kTreeExtra > kMinUnit ? std::max(nw, pairs) : 0;
     }
     rows_max = std::max(rows_max, units * rows_wg);
   }
