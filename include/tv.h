@@ -97,14 +97,19 @@ int tv_build_tree_mask(const int32_t* parent, const int32_t* n_nodes, int B, int
 
 /*
  * Workspace (bytes) tv_tree_attention needs for these sizes and chunk choice
- * (chunk_keys == 0: the automatic choice tv_tree_attention makes). Returns 0
- * when no workspace is needed (a single key chunk per sequence) and
- * (size_t)-1 for invalid sizes.
+ * on the current device (chunk_keys == 0: units balanced on the device).
+ * Returns 0 when no workspace is needed (every (sequence, KV head) pair is a
+ * single unit: max_ctx <= chunk_keys, or max_ctx <= 128 when balanced) and
+ * (size_t)-1 for invalid sizes. The size depends on the device's compute
+ * unit count, so query it on the device the call will run on.
  */
 size_t tv_tree_attention_workspace_size(int B, int T, int Hq, int Hkv, int D, int max_ctx,
                                         int chunk_keys);
 
-/* The key-chunk size tv_tree_attention uses for chunk_keys == 0. */
+/*
+ * The unit size (keys) that chunk_keys == 0 picks when every sequence is live
+ * with max_ctx committed keys (the device picks from the actual lengths).
+ */
 int tv_tree_attention_auto_chunk(int B, int T, int Hq, int Hkv, int max_ctx);
 
 /*
@@ -129,15 +134,18 @@ int tv_tree_attention_auto_chunk(int B, int T, int Hq, int Hkv, int max_ctx);
  *   k, v     [B][Hkv][kv_capacity][D] caches; element (b,g,s,d) at
  *            base + b*kv_sb + g*kv_sh + s*kv_ss + d
  *   ctx_len  int32 [B]; n_nodes int32 [B]; mask from tv_build_tree_mask
- *   max_ctx  host bound on every ctx_len (sizes the grid); kv_capacity slots
+ *   max_ctx  host bound on every ctx_len (sizes the workspace); a sequence
+ *            with ctx_len > max_ctx gets TV_ROW_CTX_BOUND; kv_capacity slots
  *   scale    softmax scale, finite and > 0 (1/sqrt(D) is the usual choice)
  *   in_dtype TV_F32 (fp32-faithful arithmetic) or TV_BF16 (bf16 matrix cores,
  *            fp32 accumulation)
  *   probability_parts  1..3 (bf16 only): the probabilities enter the P.V
  *            product as a sum of that many bf16 terms (3 = fp32-faithful P)
- *   chunk_keys  keys per split-KV partition (multiple of 64, 64..65536) or 0
- *            for the automatic choice; results are bitwise independent of the
- *            other sequences of the batch for a fixed chunk_keys
+ *   chunk_keys  keys per split-KV unit (multiple of 64, 64..65536), or 0 to
+ *            let the device balance the units of the whole launch over its
+ *            compute units from the actual lengths; results are bitwise
+ *            independent of the other sequences of the batch for a fixed
+ *            chunk_keys (with 0 they agree to rounding)
  *   out      float32 [B][T][Hq][D] contiguous; lse float32 [B][T][Hq]
  *   workspace/ws_bytes  device scratch of at least
  *            tv_tree_attention_workspace_size(...) bytes, 256-byte aligned
