@@ -333,6 +333,39 @@ def test_sample_small_vocab_many_rows(seed):
     assert check_sample(w, got, want) <= 1
 
 
+@pytest.mark.parametrize("V", [1, 1000, 3000, 32768, 32769, 40000])
+def test_sample_vocab_sizes(V):
+    """Vocabularies on both sides of the one-round-trip walk's limit (32768
+    entries), with ragged tails: star trees force several rejections at the
+    root (residual chains), random trees mix acceptances in."""
+    for seed, tree in ((300, "star"), (301, "random")):
+        w = make_custom(seed + V, 3, 2, 1, 64, V, "bf16", [8] * 3, 12, mode="sample",
+                        tree=tree, temperature=0.8)
+        d = upload(w)
+        got = run_sample(w, d)
+        want = oracle.accept_sample(w.logits, w.temperature, w.qdraft, w.u, w.tokens, w.parent,
+                                    w.n_nodes)
+        assert check_sample(w, got, want) <= 1
+
+
+def test_sample_unnormalised_draft_keeps_residual():
+    """A draft row that dominates the residual everywhere (q = 2 r) leaves a
+    zero residual sum, so r is kept; later siblings are tested against it."""
+    V = 500
+    w = make_custom(77, 2, 2, 1, 64, V, "bf16", [8] * 2, 4, mode="sample", tree="star",
+                    temperature=1.0)
+    p0 = [oracle.sample_probs(w.logits[b, 0], w.temperature) for b in range(2)]
+    for b in range(2):
+        w.qdraft[b, 1] = (2.0 * p0[b]).astype(np.float32)
+        w.u[b, 1] = 0.75  # ratio = 1/2 -> rejected
+    d = upload(w)
+    got = run_sample(w, d)
+    want = oracle.accept_sample(w.logits, w.temperature, w.qdraft, w.u, w.tokens, w.parent,
+                                w.n_nodes)
+    assert np.all(want[4][:, 1] == 0)
+    assert check_sample(w, got, want) == 0
+
+
 def test_sample_draws_follow_target():
     """Statistical check of the GPU sampler itself: the first emitted token
     over many independent rows follows p_root (chi-square)."""

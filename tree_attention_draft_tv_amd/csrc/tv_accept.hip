@@ -27,14 +27,25 @@ constexpr int kThreads = 256;
 constexpr int kSlice = 16384;   // vocabulary entries per slice
 constexpr int kMaxSplits = 64;
 constexpr int kWalkThreads = 1024;
+constexpr int kBatch = 8;        // entries per thread loaded together in the walk's passes
 
 struct ArgBest {
   float v;
   int i;
 };
 
-int num_splits(int V) {
-  int s = (V + kSlice - 1) / kSlice;
+// Sampling slices are smaller: every entry costs a float64 exp, so the
+// statistics pass wants many short, independent workgroups.
+constexpr int kSliceSample = 2048;
+// Residual entries per thread of the register-resident sampling walk: it
+// covers V <= kRegSlots * kWalkThreads.
+constexpr int kRegSlots = 32;
+static_assert(kSliceSample % kWalkThreads == 0, "a walk block lies in one slice");
+static_assert(kRegSlots * kWalkThreads <= kMaxSplits * kSliceSample,
+              "register walk vocabularies use kSliceSample-wide slices");
+
+int num_splits(int V, int slice = kSlice) {
+  int s = (V + slice - 1) / slice;
   if (s < 1) s = 1;
   if (s > kMaxSplits) s = kMaxSplits;
   return s;
@@ -268,13 +279,31 @@ struct StatPart {
   double z;  // sum over the slice of exp((l - m) / tau)
 };
 
+// Sampling slices: kSliceSample entries, widened (in steps of kWalkThreads)
+// when the vocabulary needs more than kMaxSplits of them. A slice is always a
+// whole number of kWalkThreads-wide blocks, so each block of a row lies in
+// one slice.
+__host__ __device__ inline int sample_span(int V) {
+  int span = (V + kMaxSplits - 1) / kMaxSplits;
+  if (span < kSliceSample) span = kSliceSample;
+  return (span + kWalkThreads - 1) / kWalkThreads * kWalkThreads;
+}
+
+__host__ __device__ inline int sample_splits(int V) {
+  const int span = sample_span(V);
+  return (V + span - 1) / span;
+}
+
+// Per (sequence, row, slice): the slice max m_s of the logits, the float64
+// sum of e(x) = exp((l(x) - m_s) / tau) over the slice, and every e(x) itself
+// (stored, so the walk reads a row instead of re-evaluating V exps).
 __global__ __launch_bounds__(kThreads) void softmax_slices_kernel(
     const float* __restrict__ logits, int64_t stride, const int32_t* __restrict__ n_nodes, int T,
-    int V, int S, double tau, StatPart* __restrict__ part) {
+    int V, int S, double tau, StatPart* __restrict__ part, double* __restrict__ ebuf) {
   const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   if (!live_row(n_nodes, T, b, j)) return;
-  int lo, hi;
-  slice_bounds(V, S, s, lo, hi);
+  const int span = sample_span(V);
+  const int lo = s * span, hi = min(V, lo + span);
   const float* row = logits + (static_cast<int64_t>(b) * T + j) * stride;
   const int tid = threadIdx.x;
   __shared__ float smax[kThreads / 64];
@@ -288,7 +317,12 @@ __global__ __launch_bounds__(kThreads) void softmax_slices_kernel(
   for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, smax[w]);
   const double md = static_cast<double>(m);
   double z = 0.0;
-  for (int v = lo + tid; v < hi; v += kThreads) z += exp((static_cast<double>(row[v]) - md) / tau);
+  double* erow = ebuf + (static_cast<int64_t>(b) * T + j) * V;
+  for (int v = lo + tid; v < hi; v += kThreads) {
+    const double e = exp((static_cast<double>(row[v]) - md) / tau);
+    erow[v] = e;
+    z += e;
+  }
   z = tv::wave_sum_f64(z);
   if ((tid & 63) == 0) ssum[tid >> 6] = z;
   __syncthreads();
@@ -311,23 +345,28 @@ __device__ double block_sum_f64(double x, double* s_red) {
   return t;
 }
 
-__global__ __launch_bounds__(kWalkThreads) void sample_walk_kernel(
-    const StatPart* __restrict__ part, int S, const float* __restrict__ logits,
-    int64_t lstride, const float* __restrict__ q, int64_t qstride,
-    const float* __restrict__ u, double tau, const int32_t* __restrict__ tokens,
-    const int32_t* __restrict__ parent, const int32_t* __restrict__ n_nodes, int T, int V,
-    double* __restrict__ resid, int32_t* accept_len, int32_t* path, int32_t* bonus,
-    uint8_t* accept_mask, int8_t* decision, int32_t* row_status) {
-  __shared__ int s_flags;
-  __shared__ double s_m[TV_MAX_TREE], s_z[TV_MAX_TREE];
-  __shared__ int s_par[TV_MAX_TREE], s_tok[TV_MAX_TREE], s_path[TV_MAX_TREE];
-  __shared__ double s_red[kWalkThreads / 64];
-  __shared__ int s_accept;
-  __shared__ int s_cand;
-  const int b = blockIdx.x;
+// Shared state of the two walk kernels (one workgroup per sequence).
+struct WalkShared {
+  int flags;
+  int accept;
+  int cand;
+  int hit;
+  double base, thr;
+  double m[TV_MAX_TREE], z[TV_MAX_TREE];  // row max and sum of exp over the row
+  double scale[kMaxSplits];  // exp((m_s - M) / tau) / Z of the current row, per slice
+  int par[TV_MAX_TREE], tok[TV_MAX_TREE], path[TV_MAX_TREE];
+  double red[kWalkThreads / 64];
+};
+
+// Validates the sequence and merges the slice statistics of its rows into
+// (M, Z). Returns the row status; on a dead sequence the outputs are written.
+__device__ int walk_prologue(WalkShared& sh, const StatPart* part, int S,
+                             const int32_t* tokens, const int32_t* parent, int n, int T,
+                             int V, double tau, int b, int32_t* accept_len, int32_t* path,
+                             int32_t* bonus, uint8_t* accept_mask, int8_t* decision,
+                             int32_t* row_status, bool merge = true) {
   const int tid = threadIdx.x;
-  const int n = n_nodes[b];
-  const int st = validate_seq(parent, tokens, n, T, V, b, &s_flags);
+  const int st = validate_seq(parent, tokens, n, T, V, b, &sh.flags);
   const int64_t rbase = static_cast<int64_t>(b) * T;
   if (st != TV_ROW_OK || n == 0) {
     if (tid < T) {
@@ -340,82 +379,437 @@ __global__ __launch_bounds__(kWalkThreads) void sample_walk_kernel(
       bonus[b] = -1;
       row_status[b] = st;
     }
-    return;
+    return st == TV_ROW_OK ? -1 : st;
   }
   if (tid < n) {
-    const StatPart* pp = part + (rbase + tid) * S;
-    double M = pp[0].m;
-    for (int s = 1; s < S; ++s) M = fmax(M, pp[s].m);
-    double Z = 0.0;
-    for (int s = 0; s < S; ++s) Z += pp[s].z * exp((pp[s].m - M) / tau);
-    s_m[tid] = M;
-    s_z[tid] = Z;
-    s_par[tid] = tid == 0 ? -1 : parent[rbase + tid];
-    s_tok[tid] = tokens[rbase + tid];
+    if (merge) {
+      const StatPart* pp = part + (rbase + tid) * S;
+      double M = pp[0].m;
+      for (int s = 1; s < S; ++s) M = fmax(M, pp[s].m);
+      double Z = 0.0;
+      for (int s = 0; s < S; ++s) Z += pp[s].z * exp((pp[s].m - M) / tau);
+      sh.m[tid] = M;
+      sh.z[tid] = Z;
+    }
+    sh.par[tid] = tid == 0 ? -1 : parent[rbase + tid];
+    sh.tok[tid] = tokens[rbase + tid];
   }
   if (tid < T) {
-    s_path[tid] = -1;
+    sh.path[tid] = -1;
     decision[rbase + tid] = -1;
   }
-  __syncthreads();
+  if (tid == 0) sh.path[0] = 0;
+  return TV_ROW_OK;
+}
 
-  // The residual r is either p_cur (implicit: recomputed from the logits
-  // row) or held, normalised, in one of two float64 buffers of V entries.
+// Per-slice factors turning the stored exp terms of `row` into p_row.
+__device__ void walk_set_row(WalkShared& sh, const StatPart* part, int S, int64_t rbase,
+                             int row, double tau) {
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (tid < S) {
+    const StatPart ps = part[(rbase + row) * S + tid];
+    sh.scale[tid] = exp((ps.m - sh.m[row]) / tau) / sh.z[row];
+  } else if (tid < kMaxSplits) {
+    sh.scale[tid] = 0.0;  // slots past the vocabulary read zeros times this
+  }
+  __syncthreads();
+}
+
+// ratio = r(x) / q(x) with the conventions 0 / q = 0 and r / 0 = +inf.
+__device__ __forceinline__ int accept_test(double rx, float qx, float ux) {
+  double ratio;
+  if (rx == 0.0)
+    ratio = 0.0;
+  else if (qx == 0.f)
+    ratio = INFINITY;
+  else
+    ratio = rx / static_cast<double>(qx);
+  return static_cast<double>(ux) < ratio ? 1 : 0;
+}
+
+__device__ void walk_finish(const WalkShared& sh, int plen, int bon, int T, int b,
+                            int32_t* accept_len, int32_t* path, int32_t* bonus,
+                            uint8_t* accept_mask, int32_t* row_status) {
+  const int tid = threadIdx.x;
+  const int64_t rbase = static_cast<int64_t>(b) * T;
+  if (tid < T) {
+    path[rbase + tid] = sh.path[tid];
+    bool on = false;
+    for (int k = 0; k <= plen; ++k) on |= (sh.path[k] == tid);
+    accept_mask[rbase + tid] = on ? 1 : 0;
+  }
+  if (tid == 0) {
+    accept_len[b] = plen;
+    bonus[b] = bon;
+    row_status[b] = TV_ROW_OK;
+  }
+}
+
+// One halving step of the per-wave slot reduction: lanes with bit O set keep
+// the upper M partial sums and hand the lower M to the partner lane^O.
+template <int M, int O, int N>
+__device__ __forceinline__ void slot_fold(double (&a)[N], int lane) {
+  const bool up = (lane & O) != 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const double send = up ? a[i] : a[i + M];
+    const double keep = up ? a[i + M] : a[i];
+    a[i] = keep + __shfl_xor(send, O);
+  }
+}
+
+// dst[k] = row[k * kWalkThreads + threadIdx.x] for a row of V entries, with
+// entries at or past V read as zero by the buffer's range check (no memory
+// access), so the loads of a row need no per-lane predicate and are all in
+// flight together. The thread offset passes through an empty asm so that the
+// kRegSlots offsets are formed per call, next to their loads, instead of
+// being kept live across the whole walk.
+template <typename E>
+__device__ __forceinline__ void load_blocks(const E* row, int V, E (&dst)[kRegSlots]) {
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(row), 0,
+                                                    V * static_cast<int>(sizeof(E)), 0x00020000);
+  int off = threadIdx.x * static_cast<int>(sizeof(E));
+  asm volatile("" : "+v"(off));
+#pragma unroll
+  for (int k = 0; k < kRegSlots; ++k) {
+    const int o = off + k * kWalkThreads * static_cast<int>(sizeof(E));
+    if constexpr (sizeof(E) == 8)
+      dst[k] = __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0));
+    else
+      dst[k] = __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0));
+  }
+}
+
+typedef unsigned int v2u32_t __attribute__((ext_vector_type(2)));
+
+// row[k * kWalkThreads + threadIdx.x] = src[k], stores at or past V dropped
+// by the buffer's range check.
+__device__ __forceinline__ void store_blocks(double* row, int V, const double (&src)[kRegSlots]) {
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(row, 0, V * 8, 0x00020000);
+  int off = threadIdx.x * 8;
+  asm volatile("" : "+v"(off));
+#pragma unroll
+  for (int k = 0; k < kRegSlots; ++k)
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32_t, src[k]), rs,
+                                          off + k * kWalkThreads * 8, 0, 0);
+}
+
+// Walk for V <= kRegSlots * kWalkThreads. Thread t owns the entries
+// x = k * kWalkThreads + t (slot k). The residual r is either p_cur
+// (implicit: the stored exp terms of the row times its per-slice factor) or
+// held unnormalised in one of two float64 buffers of V entries, the
+// distribution being r * inv. Every pass loads all of a thread's slots at
+// once, so a row is one round trip: a test costs one load of q_c's row, a
+// rejection one store of the new residual and one block reduction, an
+// acceptance nothing but the switch to the new row.
+__global__ __launch_bounds__(kWalkThreads) void sample_walk_one_kernel(
+    const StatPart* __restrict__ part, int S, const float* __restrict__ q, int64_t qstride,
+    const float* __restrict__ u, double tau, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ parent, const int32_t* __restrict__ n_nodes, int T, int V,
+    const double* __restrict__ ebuf, double* __restrict__ resid, int32_t* accept_len,
+    int32_t* path, int32_t* bonus, uint8_t* accept_mask, int8_t* decision,
+    int32_t* row_status) {
+  __shared__ WalkShared sh;
+  __shared__ double s_tab[kRegSlots * (kWalkThreads / 64)];
+  constexpr int kSlices = kRegSlots * kWalkThreads / kSliceSample;  // slices of a row, at most
+  __shared__ double s_pscale[TV_MAX_TREE * kSlices];  // per (row, slice) factor of p_row
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = n_nodes[b];
+  if (walk_prologue(sh, part, S, tokens, parent, n, T, V, tau, b, accept_len, path, bonus,
+                    accept_mask, decision, row_status, false) != TV_ROW_OK)
+    return;
+  const int64_t rbase = static_cast<int64_t>(b) * T;
+  // Every row's per-slice factors exp((m_s - M) / tau) / Z up front (slices
+  // past S get 0), so no exp is evaluated inside the walk: a group of kSlices
+  // lanes per row merges the row's slice statistics (max, then the sum of
+  // z_s exp((m_s - M) / tau)) with shuffles.
+  static_assert(kSlices <= 64 && (kSlices & (kSlices - 1)) == 0, "row groups within a wave");
+  for (int r0 = 0; r0 < n; r0 += kWalkThreads / kSlices) {
+    const int row = r0 + tid / kSlices, sl = tid % kSlices;
+    const bool live = row < n && sl < S;
+    StatPart ps{-INFINITY, 0.0};
+    if (live) ps = part[(rbase + row) * S + sl];
+    double M = ps.m;
+#pragma unroll
+    for (int o = 1; o < kSlices; o <<= 1) M = fmax(M, __shfl_xor(M, o));
+    const double f = live ? exp((ps.m - M) / tau) : 0.0;
+    double Z = ps.z * f;
+#pragma unroll
+    for (int o = 1; o < kSlices; o <<= 1) Z += __shfl_xor(Z, o);
+    if (row < n) s_pscale[row * kSlices + sl] = f / Z;
+  }
+  __syncthreads();
+  // Parents of rows lane and lane + 64, for the ballots of next_child.
+  static_assert(TV_MAX_TREE <= 128, "two parent words per lane");
+  const int par_lo = lane < n ? sh.par[lane] : -2;
+  const int par_hi = lane + 64 < n ? sh.par[lane + 64] : -2;
+  double* buf[2] = {resid + static_cast<int64_t>(b) * 2 * V,
+                    resid + static_cast<int64_t>(b) * 2 * V + V};
+  int cur = 0, len = 0, held = -1;  // held: buffer holding r, -1 = implicit p_cur
+  double inv = 1.0;
+  // All of this thread's entries of r (times inv when held >= 0).
+  auto load_r = [&](double (&rv)[kRegSlots]) __attribute__((always_inline)) {
+    if (held < 0) {
+      const int ru = __builtin_amdgcn_readfirstlane(cur);
+      load_blocks(ebuf + (rbase + ru) * V, V, rv);
+      const double* f = s_pscale + ru * kSlices;
+#pragma unroll
+      for (int k = 0; k < kRegSlots; ++k) rv[k] *= f[k / (kSliceSample / kWalkThreads)];
+    } else {
+      load_blocks(buf[held], V, rv);
+    }
+  };
+  // First child of `par` at index >= from (n when there is none): two
+  // wave ballots over the parent words.
+  auto next_child = [&](int from, int par) {
+    const unsigned long long lo = __ballot(par_lo == par && lane >= from);
+    if (lo) return __ffsll(lo) - 1;
+    const unsigned long long hi = __ballot(par_hi == par && lane + 64 >= from);
+    return hi ? 64 + __ffsll(hi) - 1 : n;
+  };
+  int c = next_child(1, 0);
+  while (c < n) {
+    const int x = sh.tok[c];
+    // The whole pass's loads go out before the test, which the owner of x
+    // runs on its own copies.
+    double rv[kRegSlots];
+    float qv[kRegSlots];
+    load_r(rv);
+    load_blocks(q + (rbase + __builtin_amdgcn_readfirstlane(c)) * qstride, V, qv);
+    if (tid == (x & (kWalkThreads - 1))) {
+      const int ks = x / kWalkThreads;
+      double rx = 0.0;
+      float qx = 0.f;
+#pragma unroll
+      for (int k = 0; k < kRegSlots; ++k) {
+        rx = k == ks ? rv[k] : rx;
+        qx = k == ks ? qv[k] : qx;
+      }
+      const int acc = accept_test(rx * inv, qx, u[rbase + c]);
+      decision[rbase + c] = static_cast<int8_t>(acc);
+      sh.accept = acc;
+    }
+    __syncthreads();
+    // Both branches pass a barrier before the next test writes sh.accept.
+    if (sh.accept) {
+      ++len;  // uniform: every thread follows the same walk
+      if (tid == 0) sh.path[len] = c;
+      cur = c;
+      held = -1;
+      inv = 1.0;
+      c = next_child(c + 1, cur);
+      __syncthreads();
+      continue;
+    }
+    // Rejected: r <- max(r inv - q_c, 0) into the free buffer, inv <- 1 /
+    // its sum; a zero sum keeps the old r.
+    const int dst = held == 0 ? 1 : 0;
+    double part_sum = 0.0;
+#pragma unroll
+    for (int k = 0; k < kRegSlots; ++k) {
+      const double d = fmax(fma(rv[k], inv, -static_cast<double>(qv[k])), 0.0);
+      part_sum += d;
+      rv[k] = d;
+    }
+    store_blocks(buf[dst], V, rv);
+    const double tot = block_sum_f64(part_sum, sh.red);
+    if (tot > 0.0) {
+      held = dst;
+      inv = 1.0 / tot;
+    }
+    c = next_child(c + 1, cur);
+  }
+
+  // Bonus: smallest x with sum_{y<=x} r(y) > u0 * sum_y r(y). Index order is
+  // slot-major, then wave, then lane. (1) Each wave folds its 32 slots to
+  // per-(slot, wave) sums; (2) wave 0 scans the 512 sums in index order and
+  // finds the first block whose running sum passes the threshold; (3) that
+  // block's wave scans its 64 entries from the block's starting sum.
+  double rv[kRegSlots];
+  load_r(rv);
+  {
+    constexpr int H = kRegSlots / 2;
+    double a[H];
+    const bool up = (lane & 32) != 0;
+#pragma unroll
+    for (int i = 0; i < H; ++i)
+      a[i] = (up ? rv[i + H] : rv[i]) + __shfl_xor(up ? rv[i] : rv[i + H], 32);
+    slot_fold<8, 16>(a, lane);
+    slot_fold<4, 8>(a, lane);
+    slot_fold<2, 4>(a, lane);
+    slot_fold<1, 2>(a, lane);
+    const double tot = a[0] + __shfl_xor(a[0], 1);  // slot lane >> 1 of this wave
+    if ((lane & 1) == 0) s_tab[(lane >> 1) * (kWalkThreads / 64) + wave] = tot;
+  }
+  __syncthreads();
+  const double u0 = static_cast<double>(u[rbase]);
+  constexpr int kPer = kRegSlots * (kWalkThreads / 64) / 64;  // table entries per lane
+  if (wave == 0) {
+    double loc[kPer];
+    double lt = 0.0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      loc[j] = s_tab[lane * kPer + j];
+      lt += loc[j];
+    }
+    double inc = lt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    const double total = __shfl(inc, 63);
+    const double thr = u0 * total;
+    double p = __shfl_up(inc, 1);
+    if (lane == 0) p = 0.0;
+    int hit = -1;
+    double base = 0.0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const double nx = p + loc[j];
+      if (hit < 0 && nx > thr) {
+        hit = lane * kPer + j;
+        base = p;
+      }
+      p = nx;
+    }
+    const unsigned long long m = __ballot(hit >= 0);
+    const int first = m ? __ffsll(m) - 1 : -1;
+    if (lane == 0) sh.hit = -1;
+    if (lane == first) {
+      sh.hit = hit;
+      sh.base = base;
+      sh.thr = thr;
+    }
+    if (tid == 0) sh.cand = -1;
+  }
+  __syncthreads();
+  const int e = sh.hit;
+  if (e >= 0) {
+    if (wave == e % (kWalkThreads / 64)) {
+      const int ks = e / (kWalkThreads / 64);
+      double val = 0.0;
+#pragma unroll
+      for (int k = 0; k < kRegSlots; ++k) val = k == ks ? rv[k] : val;
+      double inc = val;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+      }
+      const double run = sh.base + inc;
+      const unsigned long long m = __ballot(run > sh.thr);
+      int pick;
+      if (m) {
+        pick = __ffsll(m) - 1;
+      } else {
+        // Rounding kept the lane scan under the threshold that the block sum
+        // passed: the draw sits at the block's end; take its last positive.
+        const unsigned long long pos = __ballot(val > 0.0);
+        pick = 63 - __clzll(pos);
+      }
+      if (lane == 0) sh.cand = ks * kWalkThreads + wave * 64 + pick;
+    }
+  } else {
+    // Rounding left the threshold above every running sum (u0 within an ulp
+    // of 1): take the last token with positive mass.
+    int last = -1;
+#pragma unroll
+    for (int k = 0; k < kRegSlots; ++k)
+      if (rv[k] > 0.0) last = k * kWalkThreads + tid;
+    if (last >= 0) atomicMax(&sh.cand, last);
+  }
+  __syncthreads();
+  walk_finish(sh, len, sh.cand, T, b, accept_len, path, bonus, accept_mask, row_status);
+}
+
+// Walk for larger vocabularies: the residual r lives in one of two float64
+// buffers of V entries per sequence, or stays implicit as p_cur (the stored
+// exp terms times the per-slice factors) until the first rejection.
+__global__ __launch_bounds__(kWalkThreads) void sample_walk_kernel(
+    const StatPart* __restrict__ part, int S, const float* __restrict__ q, int64_t qstride,
+    const float* __restrict__ u, double tau, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ parent, const int32_t* __restrict__ n_nodes, int T, int V,
+    const double* __restrict__ ebuf, double* __restrict__ resid, int32_t* accept_len,
+    int32_t* path, int32_t* bonus, uint8_t* accept_mask, int8_t* decision,
+    int32_t* row_status) {
+  __shared__ WalkShared sh;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = n_nodes[b];
+  if (walk_prologue(sh, part, S, tokens, parent, n, T, V, tau, b, accept_len, path, bonus,
+                    accept_mask, decision, row_status) != TV_ROW_OK)
+    return;
+  const int64_t rbase = static_cast<int64_t>(b) * T;
   double* buf[2] = {resid + static_cast<int64_t>(b) * 2 * V,
                     resid + static_cast<int64_t>(b) * 2 * V + V};
   int cur = 0, len = 0, held = -1;  // held: index of the buffer holding r, -1 = implicit
-  if (tid == 0) s_path[0] = 0;
-
+  const int span = sample_span(V);
+  walk_set_row(sh, part, S, rbase, 0, tau);
+  const double* erow = ebuf + rbase * V;  // + cur * V
   auto r_at = [&](int x) -> double {
-    if (held < 0) {
-      const double l = static_cast<double>(logits[(rbase + cur) * lstride + x]);
-      return exp((l - s_m[cur]) / tau) / s_z[cur];
-    }
+    if (held < 0) return erow[static_cast<int64_t>(cur) * V + x] * sh.scale[x / span];
     return buf[held][x];
   };
 
   for (;;) {
     bool accepted = false;
     for (int c = cur + 1; c < n; ++c) {
-      if (s_par[c] != cur) continue;
-      const int x = s_tok[c];
+      if (sh.par[c] != cur) continue;
+      const int x = sh.tok[c];
       if (tid == 0) {
-        const double rx = r_at(x);
-        const double qx = static_cast<double>(q[(rbase + c) * qstride + x]);
-        double ratio;
-        if (rx == 0.0)
-          ratio = 0.0;
-        else if (qx == 0.0)
-          ratio = INFINITY;
-        else
-          ratio = rx / qx;
-        const int acc = static_cast<double>(u[rbase + c]) < ratio ? 1 : 0;
+        const int acc = accept_test(r_at(x), q[(rbase + c) * qstride + x], u[rbase + c]);
         decision[rbase + c] = static_cast<int8_t>(acc);
-        s_accept = acc;
+        sh.accept = acc;
       }
       __syncthreads();
-      const int acc = s_accept;
-      __syncthreads();
-      if (acc) {
-        ++len;  // uniform: every thread follows the same walk
-        if (tid == 0) s_path[len] = c;
+      if (sh.accept) {
+        ++len;
+        if (tid == 0) sh.path[len] = c;
         cur = c;
         held = -1;
+        walk_set_row(sh, part, S, rbase, c, tau);
         accepted = true;
         break;
       }
-      // Rejected: r <- max(r - q_c, 0) / sum, into the free buffer.
+      // Rejected: r <- max(r - q_c, 0) / sum, into the free buffer. Each
+      // thread loads kBatch entries before storing any, so the loads are in
+      // flight together.
       const int dst = held == 0 ? 1 : 0;
       const float* qrow = q + (rbase + c) * qstride;
       double part_sum = 0.0;
-      for (int v = tid; v < V; v += kWalkThreads) {
-        const double res = fmax(r_at(v) - static_cast<double>(qrow[v]), 0.0);
-        buf[dst][v] = res;
-        part_sum += res;
+      for (int v0 = tid; v0 < V; v0 += kWalkThreads * kBatch) {
+        double rv[kBatch], qv[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int v = min(v0 + k * kWalkThreads, V - 1);
+          rv[k] = r_at(v);
+          qv[k] = static_cast<double>(qrow[v]);
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int v = v0 + k * kWalkThreads;
+          if (v < V) {
+            const double res = fmax(rv[k] - qv[k], 0.0);
+            buf[dst][v] = res;
+            part_sum += res;
+          }
+        }
       }
-      const double tot = block_sum_f64(part_sum, s_red);
+      const double tot = block_sum_f64(part_sum, sh.red);
       if (tot > 0.0) {
-        for (int v = tid; v < V; v += kWalkThreads) buf[dst][v] = buf[dst][v] / tot;
+        for (int v0 = tid; v0 < V; v0 += kWalkThreads * kBatch) {
+          double rv[kBatch];
+#pragma unroll
+          for (int k = 0; k < kBatch; ++k) rv[k] = buf[dst][min(v0 + k * kWalkThreads, V - 1)];
+#pragma unroll
+          for (int k = 0; k < kBatch; ++k) {
+            const int v = v0 + k * kWalkThreads;
+            if (v < V) buf[dst][v] = rv[k] / tot;
+          }
+        }
         __syncthreads();
         held = dst;
       }
@@ -423,13 +817,25 @@ __global__ __launch_bounds__(kWalkThreads) void sample_walk_kernel(
     if (!accepted) break;
   }
   __syncthreads();
-  const int plen = len;
 
   // Bonus: smallest x with sum_{y<=x} r(y) > u0 * sum_y r(y). Each thread
   // owns a contiguous range of the vocabulary.
   const int per = (V + kWalkThreads - 1) / kWalkThreads;
   const int lo = min(V, tid * per);
   const int hi = min(V, lo + per);
+  if (held < 0) {
+    // Materialise p_cur once (each thread writes and later reads only its
+    // own range).
+    for (int v0 = lo; v0 < hi; v0 += kBatch) {
+      double rv[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) rv[k] = r_at(min(v0 + k, V - 1));
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (v0 + k < hi) buf[0][v0 + k] = rv[k];
+    }
+    held = 0;
+  }
   double mine = 0.0;
   for (int v = lo; v < hi; ++v) mine += r_at(v);
   // Exclusive prefix over threads: wave scan then across waves.
@@ -443,53 +849,47 @@ __global__ __launch_bounds__(kWalkThreads) void sample_walk_kernel(
   double excl = __shfl_up(incl, 1);
   if (lane == 0) excl = 0.0;
   __syncthreads();
-  if (lane == 63) s_red[tid >> 6] = incl;
+  if (lane == 63) sh.red[tid >> 6] = incl;
   __syncthreads();
   double wave_off = 0.0, total = 0.0;
   for (int w = 0; w < kWalkThreads / 64; ++w) {
-    if (w < (tid >> 6)) wave_off += s_red[w];
-    total += s_red[w];
+    if (w < (tid >> 6)) wave_off += sh.red[w];
+    total += sh.red[w];
   }
-  const double u0 = static_cast<double>(u[rbase]);
-  const double thr = u0 * total;
+  const double thr = static_cast<double>(u[rbase]) * total;
   double run = wave_off + excl;
   int cand = INT_MAX;
-  for (int v = lo; v < hi; ++v) {
-    run += r_at(v);
-    if (run > thr) {
-      cand = v;
-      break;
+  for (int v0 = lo; v0 < hi && cand == INT_MAX; v0 += kBatch) {
+    double rv[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) rv[k] = r_at(min(v0 + k, V - 1));
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (cand == INT_MAX && v0 + k < hi) {
+        run += rv[k];
+        if (run > thr) cand = v0 + k;
+      }
     }
   }
-  if (tid == 0) s_cand = INT_MAX;
+  if (tid == 0) sh.cand = INT_MAX;
   __syncthreads();
-  if (cand != INT_MAX) atomicMin(&s_cand, cand);
+  if (cand != INT_MAX) atomicMin(&sh.cand, cand);
   __syncthreads();
-  int bon = s_cand;
+  int bon = sh.cand;
   if (bon == INT_MAX) {
     // Rounding left the threshold above every running sum (u0 within an ulp
     // of 1): take the last token with positive mass.
     int lastpos = -1;
     for (int v = lo; v < hi; ++v)
       if (r_at(v) > 0.0) lastpos = v;
-    if (tid == 0) s_cand = -1;
     __syncthreads();
-    if (lastpos >= 0) atomicMax(&s_cand, lastpos);
+    if (tid == 0) sh.cand = -1;
     __syncthreads();
-    bon = s_cand;
+    if (lastpos >= 0) atomicMax(&sh.cand, lastpos);
+    __syncthreads();
+    bon = sh.cand;
   }
-
-  if (tid < T) {
-    path[rbase + tid] = s_path[tid];
-    bool on = false;
-    for (int k = 0; k <= plen; ++k) on |= (s_path[k] == tid);
-    accept_mask[rbase + tid] = on ? 1 : 0;
-  }
-  if (tid == 0) {
-    accept_len[b] = plen;
-    bonus[b] = bon;
-    row_status[b] = TV_ROW_OK;
-  }
+  walk_finish(sh, len, bon, T, b, accept_len, path, bonus, accept_mask, row_status);
 }
 
 bool accept_sizes_ok(int B, int T, int V) {
@@ -500,8 +900,14 @@ size_t greedy_ws(int B, int T, int V) {
   return tvh::align_up(static_cast<size_t>(B) * T * num_splits(V) * sizeof(ArgBest), 256);
 }
 
+// Vocabularies the one-round-trip walk covers.
+bool sample_one_pass(int V) { return V <= kRegSlots * kWalkThreads; }
+
+// Sampling workspace: slice statistics, the stored exp terms of every row
+// (float64, B T V) and two float64 residual buffers per sequence.
 size_t sample_ws(int B, int T, int V) {
-  return tvh::align_up(static_cast<size_t>(B) * T * num_splits(V) * sizeof(StatPart), 256) +
+  return tvh::align_up(static_cast<size_t>(B) * T * sample_splits(V) * sizeof(StatPart), 256) +
+         tvh::align_up(static_cast<size_t>(B) * T * V * sizeof(double), 256) +
          tvh::align_up(static_cast<size_t>(B) * 2 * V * sizeof(double), 256);
 }
 
@@ -553,16 +959,24 @@ extern "C" int tv_accept_sample(const float* logits, int64_t logits_row_stride,
   if (B == 0) return TV_OK;
   if (!workspace || ws_bytes < sample_ws(B, T, V) || !tvh::aligned256(workspace))
     return TV_ERR_WORKSPACE;
-  const int S = num_splits(V);
+  const int S = sample_splits(V);
   StatPart* part = static_cast<StatPart*>(workspace);
-  double* resid = reinterpret_cast<double*>(
-      static_cast<char*>(workspace) +
-      tvh::align_up(static_cast<size_t>(B) * T * S * sizeof(StatPart), 256));
+  char* base = static_cast<char*>(workspace) +
+               tvh::align_up(static_cast<size_t>(B) * T * S * sizeof(StatPart), 256);
+  double* ebuf = reinterpret_cast<double*>(base);
   const double tau = static_cast<double>(temperature);
   hipLaunchKernelGGL(softmax_slices_kernel, dim3(S, T, B), dim3(kThreads), 0, stream, logits,
-                     logits_row_stride, n_nodes, T, V, S, tau, part);
-  hipLaunchKernelGGL(sample_walk_kernel, dim3(B), dim3(kWalkThreads), 0, stream, part, S, logits,
-                     logits_row_stride, q, q_row_stride, u, tau, tokens, parent, n_nodes, T, V,
-                     resid, accept_len, path, bonus, accept_mask, decision, row_status);
+                     logits_row_stride, n_nodes, T, V, S, tau, part, ebuf);
+  double* resid = reinterpret_cast<double*>(
+      base + tvh::align_up(static_cast<size_t>(B) * T * V * sizeof(double), 256));
+  if (sample_one_pass(V)) {
+    hipLaunchKernelGGL(sample_walk_one_kernel, dim3(B), dim3(kWalkThreads), 0, stream, part, S,
+                       q, q_row_stride, u, tau, tokens, parent, n_nodes, T, V, ebuf, resid,
+                       accept_len, path, bonus, accept_mask, decision, row_status);
+  } else {
+    hipLaunchKernelGGL(sample_walk_kernel, dim3(B), dim3(kWalkThreads), 0, stream, part, S, q,
+                       q_row_stride, u, tau, tokens, parent, n_nodes, T, V, ebuf, resid,
+                       accept_len, path, bonus, accept_mask, decision, row_status);
+  }
   return tvh::launch_status();
 }
