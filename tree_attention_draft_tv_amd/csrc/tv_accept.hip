@@ -296,20 +296,37 @@ __host__ __device__ inline int sample_splits(int V) {
 
 // Per (sequence, row, slice): the slice max m_s of the logits, the float64
 // sum of e(x) = exp((l(x) - m_s) / tau) over the slice, and every e(x) itself
-// (stored, so the walk reads a row instead of re-evaluating V exps).
+// (stored, so the walk reads a row instead of re-evaluating V exps). A slice
+// of at most kSliceSample entries is read once into registers (entry
+// lo + j * kThreads + t for thread t); wider slices (vocabularies past
+// kMaxSplits * kSliceSample) take a two-pass loop. The exponent is formed as
+// (l - m_s) * (1 / tau).
 __global__ __launch_bounds__(kThreads) void softmax_slices_kernel(
     const float* __restrict__ logits, int64_t stride, const int32_t* __restrict__ n_nodes, int T,
-    int V, int S, double tau, StatPart* __restrict__ part, double* __restrict__ ebuf) {
+    int V, int S, double inv_tau, StatPart* __restrict__ part, double* __restrict__ ebuf) {
   const int s = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   if (!live_row(n_nodes, T, b, j)) return;
   const int span = sample_span(V);
   const int lo = s * span, hi = min(V, lo + span);
   const float* row = logits + (static_cast<int64_t>(b) * T + j) * stride;
+  double* erow = ebuf + (static_cast<int64_t>(b) * T + j) * V;
   const int tid = threadIdx.x;
   __shared__ float smax[kThreads / 64];
   __shared__ double ssum[kThreads / 64];
+  constexpr int kPer = kSliceSample / kThreads;
+  const bool in_regs = hi - lo <= kSliceSample;  // uniform
+  float lv[kPer];
   float m = -INFINITY;
-  for (int v = lo + tid; v < hi; v += kThreads) m = fmaxf(m, row[v]);
+  if (in_regs) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int v = lo + k * kThreads + tid;
+      lv[k] = v < hi ? row[v] : -INFINITY;
+      m = fmaxf(m, lv[k]);
+    }
+  } else {
+    for (int v = lo + tid; v < hi; v += kThreads) m = fmaxf(m, row[v]);
+  }
   m = tv::wave_max(m);
   if ((tid & 63) == 0) smax[tid >> 6] = m;
   __syncthreads();
@@ -317,11 +334,22 @@ __global__ __launch_bounds__(kThreads) void softmax_slices_kernel(
   for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, smax[w]);
   const double md = static_cast<double>(m);
   double z = 0.0;
-  double* erow = ebuf + (static_cast<int64_t>(b) * T + j) * V;
-  for (int v = lo + tid; v < hi; v += kThreads) {
-    const double e = exp((static_cast<double>(row[v]) - md) / tau);
-    erow[v] = e;
-    z += e;
+  if (in_regs) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int v = lo + k * kThreads + tid;
+      if (v < hi) {
+        const double e = exp((static_cast<double>(lv[k]) - md) * inv_tau);
+        erow[v] = e;
+        z += e;
+      }
+    }
+  } else {
+    for (int v = lo + tid; v < hi; v += kThreads) {
+      const double e = exp((static_cast<double>(row[v]) - md) * inv_tau);
+      erow[v] = e;
+      z += e;
+    }
   }
   z = tv::wave_sum_f64(z);
   if ((tid & 63) == 0) ssum[tid >> 6] = z;
@@ -966,7 +994,7 @@ extern "C" int tv_accept_sample(const float* logits, int64_t logits_row_stride,
   double* ebuf = reinterpret_cast<double*>(base);
   const double tau = static_cast<double>(temperature);
   hipLaunchKernelGGL(softmax_slices_kernel, dim3(S, T, B), dim3(kThreads), 0, stream, logits,
-                     logits_row_stride, n_nodes, T, V, S, tau, part, ebuf);
+                     logits_row_stride, n_nodes, T, V, S, 1.0 / tau, part, ebuf);
   double* resid = reinterpret_cast<double*>(
       base + tvh::align_up(static_cast<size_t>(B) * T * V * sizeof(double), 256));
   if (sample_one_pass(V)) {
