@@ -25,9 +25,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kSlice = 16384;   // vocabulary entries per slice
+constexpr int kVec = kSlice / (4 * 256);  // 16-byte loads per argmax thread per round
 constexpr int kMaxSplits = 64;
 constexpr int kWalkThreads = 1024;
 constexpr int kBatch = 8;        // entries per thread loaded together in the walk's passes
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct ArgBest {
   float v;
@@ -92,27 +95,27 @@ __global__ __launch_bounds__(kThreads) void argmax_slices_kernel(
     bv = row[lo + tid];
     bi = lo + tid;
   }
-  int v0 = lo_al + 4 * tid;
+  // The body: kVec 16-byte loads per thread issued together (one round trip
+  // covers a 16384-entry slice); addresses past the body are clamped to its
+  // last vector and their values ignored, so no load sits behind a branch.
+  // The logits are read once: non-temporal loads.
   const int hi4 = lo_al + ((hi - lo_al) & ~3);
-  for (; v0 + 4 * kThreads * 3 < hi4; v0 += 4 * kThreads * 4) {
-    float4 x[4];
+  for (int v0 = lo_al + 4 * tid; v0 < hi4; v0 += 4 * kThreads * kVec) {
+    f32x4_t x[kVec];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const float4*>(row + v0 + 4 * kThreads * u);
+    for (int u = 0; u < kVec; ++u)
+      x[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4_t*>(row + min(v0 + 4 * kThreads * u, hi4 - 4)));
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kVec; ++u) {
       const int base = v0 + 4 * kThreads * u;
-      if (x[u].x > bv || bi == INT_MAX) { bv = x[u].x; bi = base; }
-      if (x[u].y > bv) { bv = x[u].y; bi = base + 1; }
-      if (x[u].z > bv) { bv = x[u].z; bi = base + 2; }
-      if (x[u].w > bv) { bv = x[u].w; bi = base + 3; }
+      if (base < hi4) {
+        if (x[u].x > bv || bi == INT_MAX) { bv = x[u].x; bi = base; }
+        if (x[u].y > bv) { bv = x[u].y; bi = base + 1; }
+        if (x[u].z > bv) { bv = x[u].z; bi = base + 2; }
+        if (x[u].w > bv) { bv = x[u].w; bi = base + 3; }
+      }
     }
-  }
-  for (; v0 < hi4; v0 += 4 * kThreads) {
-    const float4 x = *reinterpret_cast<const float4*>(row + v0);
-    if (x.x > bv || bi == INT_MAX) { bv = x.x; bi = v0; }
-    if (x.y > bv) { bv = x.y; bi = v0 + 1; }
-    if (x.z > bv) { bv = x.z; bi = v0 + 2; }
-    if (x.w > bv) { bv = x.w; bi = v0 + 3; }
   }
   const int tv = hi4 + tid;
   if (tv < hi) {
