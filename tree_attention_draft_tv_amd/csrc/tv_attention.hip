@@ -84,15 +84,15 @@ struct AttnParams {
   float* out;
   float* lse;
   int32_t* sched;   // [0] keys per unit, [1 + b] first unit of sequence b
-  float* part_o;    // [unit][rows_wg][D], un-normalised
-  float2* part_ml;  // [unit][rows_wg]: (reference max in log2 units, sum)
+  float* part_o;    // [unit][rows_wg][D], un-normalised: fp32, or int16 fixed point (q16)
+  float4* part_ml;  // per pair [rows_wg][unit of the pair]: (reference max in log2 units, sum,
+                    // int16 scale, 0)
   int32_t* row_status;
 };
 
-// Status of sequence b: TV_ROW_OK (live), -1 (padded: n == 0) or an error.
-__device__ __forceinline__ int seq_check(const AttnParams& p, int b, int& n, int& L) {
-  n = p.n_nodes[b];
-  L = p.ctx_len[b];
+// Status of a sequence with n live rows and L committed keys: TV_ROW_OK
+// (live), -1 (padded: n == 0) or an error.
+__device__ __forceinline__ int seq_status(const AttnParams& p, int n, int L) {
   if (n < 0 || n > p.T) return TV_ROW_NNODES;
   if (n == 0) return -1;
   if (L < 0 || L > p.max_ctx || static_cast<int64_t>(L) + n > p.kv_capacity)
@@ -100,29 +100,47 @@ __device__ __forceinline__ int seq_check(const AttnParams& p, int b, int& n, int
   return TV_ROW_OK;
 }
 
+// Status of sequence b (see seq_status); also returns its n and L.
+__device__ __forceinline__ int seq_check(const AttnParams& p, int b, int& n, int& L) {
+  n = p.n_nodes[b];
+  L = p.ctx_len[b];
+  return seq_status(p, n, L);
+}
+
+
 __device__ __forceinline__ int num_chunks(int L, int chunk) {
   return L == 0 ? 1 : (L + chunk - 1) / chunk;
 }
 
 // Padded (n == 0) and invalid sequences: every output row gets the padding
 // values (O = 0, lse = -inf) and every sequence its status, spread over the
-// whole grid after the units are done.
+// whole grid. st0 holds the statuses of the first 64 sequences (lane b:
+// sequence b); later blocks of 64 are read in one round before their stores
+// (a load placed after the stores would wait for them: the compiler cannot
+// rule out that they alias the length arrays).
 template <int D>
-__device__ void finish_non_live(const AttnParams& p) {
+__device__ void finish_non_live(const AttnParams& p, int st0) {
   constexpr int D4 = D / 4;
   const int nthreads = gridDim.x * blockDim.x;
   const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int per_seq = p.T * p.Hq * D4;
-  for (int b = 0; b < p.B; ++b) {
-    int n, L;
-    const int st = seq_check(p, b, n, L);
-    if (gtid == b % nthreads) p.row_status[b] = (st == -1) ? TV_ROW_OK : st;
-    if (st == TV_ROW_OK) continue;
-    float4* o = reinterpret_cast<float4*>(p.out + static_cast<int64_t>(b) * p.T * p.Hq * D);
-    float* l = p.lse + static_cast<int64_t>(b) * p.T * p.Hq;
-    for (int idx = gtid; idx < per_seq; idx += nthreads) {
-      o[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (idx % D4 == 0) l[idx / D4] = -INFINITY;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const bool has = b0 + lane < p.B;
+    int st = st0;
+    if (b0 > 0 && has) {
+      int n, L;
+      st = seq_check(p, b0 + lane, n, L);
+    }
+    if (gtid < 64 && has) p.row_status[b0 + lane] = (st == -1) ? TV_ROW_OK : st;
+    for (uint64_t m = __ballot(has && st != TV_ROW_OK); m; m &= m - 1) {
+      const int b = b0 + __builtin_ctzll(m);
+      float4* o = reinterpret_cast<float4*>(p.out + static_cast<int64_t>(b) * p.T * p.Hq * D);
+      float* l = p.lse + static_cast<int64_t>(b) * p.T * p.Hq;
+      for (int idx = gtid; idx < per_seq; idx += nthreads) {
+        o[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (idx % D4 == 0) l[idx / D4] = -INFINITY;
+      }
     }
   }
 }
@@ -151,15 +169,17 @@ __device__ __forceinline__ int wave_sum_i(int x) {
 }
 
 // Every wave loads the committed lengths of the first 64 sequences once
-// (lane b holds sequence b, -1 if not live); longer batches re-read the rest
-// from memory (L2) in each pass.
-__device__ __forceinline__ int lane_len(const AttnParams& p, int& n0) {
+// (lane b holds sequence b, -1 if not live, and its status in st0); longer
+// batches re-read the rest from memory (L2) in each pass.
+__device__ __forceinline__ int lane_len(const AttnParams& p, int& n0, int& st0) {
   const int lane = threadIdx.x & 63;
   int L = -1;
   n0 = 0;
+  st0 = TV_ROW_OK;
   if (lane < p.B) {
     int n;
-    if (seq_check(p, lane, n, L) != TV_ROW_OK) L = -1;
+    st0 = seq_check(p, lane, n, L);
+    if (st0 != TV_ROW_OK) L = -1;
     n0 = n;
   }
   return L;
@@ -214,14 +234,23 @@ __device__ int total_units(const AttnParams& p, int len0, int K) {
 __device__ int choose_unit(const AttnParams& p, int len0) {
   if (p.kunit > 0) return p.kunit;
   int maxl = 0, keys = 0;
-  for (int b0 = 0; b0 < p.B; b0 += 64) {
-    const int L = block_len(p, b0, len0);
-    maxl = max(maxl, L);
-    keys += max(L, 0);
-  }
+  if (p.B <= 64) {
+    // Every length is in a lane of len0: read them as scalars.
+    for (int b = 0; b < p.B; ++b) {
+      const int L = __builtin_amdgcn_readlane(len0, b);
+      maxl = max(maxl, L);
+      keys += max(L, 0);
+    }
+  } else {
+    for (int b0 = 0; b0 < p.B; b0 += 64) {
+      const int L = block_len(p, b0, len0);
+      maxl = max(maxl, L);
+      keys += max(L, 0);
+    }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) maxl = max(maxl, __shfl_xor(maxl, o));
-  keys = wave_sum_i(keys);
+    for (int o = 32; o > 0; o >>= 1) maxl = max(maxl, __shfl_xor(maxl, o));
+    keys = wave_sum_i(keys);
+  }
   // One unit per pair (L + kTreeExtra <= hi). Also the only choice when the
   // caller passed no workspace for partials.
   const int hi = max(kMinUnit, (maxl + kTreeExtra + 63) / 64 * 64);
@@ -233,6 +262,24 @@ __device__ int choose_unit(const AttnParams& p, int len0) {
   int lo = static_cast<int>((pair_keys + p.nw - 1) / p.nw);
   lo = max(kMinUnit, (lo + 63) / 64 * 64);
   if (lo >= hi) return hi;
+  if (p.B <= 64) {
+    // Lane j tries lo + 64 j: 64 candidate sizes per round, the smallest
+    // whose unit count fits is taken (the count only falls as K grows).
+    const int lane = threadIdx.x & 63;
+    const int64_t per = static_cast<int64_t>(p.Hkv) * p.RG;
+    for (int round = 0; round < 2; ++round) {
+      const int kc = lo + 64 * lane;
+      int64_t cnt = 0;
+      for (int b = 0; b < p.B; ++b) {
+        const int L = __builtin_amdgcn_readlane(len0, b);
+        if (L >= 0) cnt += L == 0 ? 1 : (L + kTreeExtra + kc - 1) / kc;
+      }
+      const uint64_t fits = __ballot(kc <= hi && cnt * per <= p.nw);
+      if (fits) return lo + 64 * static_cast<int>(__builtin_ctzll(fits));
+      if (hi - lo <= 64 * 63) return hi;
+      lo += 64 * 64;
+    }
+  }
   for (int step = 0; step < 4 && lo < hi; ++step, lo += 64)
     if (total_units(p, len0, lo) <= p.nw) return lo;
   if (total_units(p, len0, hi) > p.nw) return hi;
@@ -253,6 +300,27 @@ __device__ int choose_unit(const AttnParams& p, int len0) {
 __device__ bool decode_unit(const AttnParams& p, int len0, int K, int u, int& b, int& kvh, int& rg,
                             int& c, int& nch) {
   const int lane = threadIdx.x & 63;
+  if (p.B <= 64) {
+    // Lane b holds the unit count of sequence b; walk them as scalars.
+    const int cnt = units_of(p, len0, K);
+    int base = 0;
+    for (int bb = 0; bb < p.B; ++bb) {
+      const int cb = __builtin_amdgcn_readlane(cnt, bb);
+      if (u < base + cb) {
+        b = bb;
+        const int per_pair = cb / (p.Hkv * p.RG);
+        const int local = u - base;
+        nch = per_pair;
+        const int pair = local / per_pair;
+        c = local - pair * per_pair;
+        kvh = pair / p.RG;
+        rg = pair - kvh * p.RG;
+        return true;
+      }
+      base += cb;
+    }
+    return false;
+  }
   int base = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     const int cnt = units_of(p, block_len(p, b0, len0), K);
@@ -285,6 +353,16 @@ __device__ bool decode_unit(const AttnParams& p, int len0, int K, int u, int& b,
 __device__ void write_sched(const AttnParams& p, int len0, int K) {
   const int lane = threadIdx.x & 63;
   if (lane == 0) p.sched[0] = K;
+  if (p.B <= 64) {
+    const int cnt = units_of(p, len0, K);
+    int base = 0, first = 0;
+    for (int bb = 0; bb < p.B; ++bb) {
+      if (lane == bb) first = base;
+      base += __builtin_amdgcn_readlane(cnt, bb);
+    }
+    if (lane < p.B) p.sched[1 + lane] = first;
+    return;
+  }
   int base = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     const int cnt = units_of(p, block_len(p, b0, len0), K);
@@ -411,8 +489,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int n0;
-  const int len0 = lane_len(p, n0);
+  int n0, st0;
+  const int len0 = lane_len(p, n0, st0);
   const int K = choose_unit(p, len0);
   if (p.sched && blockIdx.x == 0 && wave == 0) write_sched(p, len0, K);
 
@@ -747,6 +825,20 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   // ---- epilogue ----
   if (!wave_active) return;
   const bool direct = (nch == 1);
+  // With one probability part the unit partials are stored as 16-bit fixed
+  // point against the row's largest |O| (error at most that / 65534 per
+  // entry, i.e. max|v| / 65534 after normalisation); more parts keep fp32.
+  constexpr bool kQ16 = (PARTS == 1);
+  float amax[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    float a = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a = fmaxf(a, fabsf(o[dt][rt][e]));
+    amax[rt] = (kQ16 && !direct) ? row_max4(a) : 0.f;
+  }
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     const int r = row0 + rt * 16 + l16;
@@ -766,17 +858,35 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
       if (g == 0) p.lse[orow] = live ? (mref[rt] + __log2f(l_tot[rt])) * kLn2 : -INFINITY;
     } else {
       const int64_t prow = static_cast<int64_t>(u) * p.rows_wg + (r - rg * kRowsWG);
-      float* dst = p.part_o + prow * D;
+      if constexpr (kQ16) {
+        int16_t* dst = reinterpret_cast<int16_t*>(p.part_o) + prow * D;
+        const float qs = amax[rt] > 0.f ? 32767.f / amax[rt] : 0.f;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const f32x4_t v = o[dt][rt];
-        *reinterpret_cast<float4*>(dst + 16 * dt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+        for (int dt = 0; dt < DT; ++dt) {
+          const f32x4_t v = o[dt][rt];
+          const uint32_t q0 = static_cast<uint16_t>(__float2int_rn(v[0] * qs));
+          const uint32_t q1 = static_cast<uint16_t>(__float2int_rn(v[1] * qs));
+          const uint32_t q2 = static_cast<uint16_t>(__float2int_rn(v[2] * qs));
+          const uint32_t q3 = static_cast<uint16_t>(__float2int_rn(v[3] * qs));
+          *reinterpret_cast<uint2*>(dst + 16 * dt + 4 * g) = make_uint2(q0 | (q1 << 16), q2 | (q3 << 16));
+        }
+      } else {
+        float* dst = p.part_o + prow * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const f32x4_t v = o[dt][rt];
+          *reinterpret_cast<float4*>(dst + 16 * dt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+        }
       }
-      if (g == 0) p.part_ml[prow] = make_float2(mref[rt], l_tot[rt]);
+      if (g == 0)
+        p.part_ml[static_cast<int64_t>(u - c) * p.rows_wg + (r - rg * kRowsWG) * nch + c] =
+            make_float4(mref[rt], l_tot[rt], amax[rt], 0.f);
     }
   }
   };
 
+  // Padding outputs first: their stores drain while the first tiles load.
+  finish_non_live<D>(p, st0);
   const int u0 = first_unit(p);
   for (int u = u0;; u += p.nw) {
     int b, kvh, rg, c, nch;
@@ -784,7 +894,6 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
     if (u != u0) __syncthreads();  // the previous unit's LDS reads are done
     run_unit(u, b, kvh, rg, c, nch);
   }
-  finish_non_live<D>(p);
 }
 
 // ---------------------------------------------------------- fp32 (VALU) ---
@@ -801,8 +910,8 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
   __shared__ uint32_t sMask[TV_MAX_TREE * (TV_MAX_TREE / 32)];
 
   const int tid = threadIdx.x;
-  int n0;
-  const int len0 = lane_len(p, n0);
+  int n0, st0;
+  const int len0 = lane_len(p, n0, st0);
   const int K = choose_unit(p, len0);
   if (p.sched && blockIdx.x == 0 && tid < tv::kWave) write_sched(p, len0, K);
 
@@ -897,10 +1006,14 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
     const int64_t prow = static_cast<int64_t>(u) * p.rows_wg + (r - rg * kRowsWGf32);
 #pragma unroll
     for (int d = 0; d < DQ; ++d) p.part_o[prow * D + quarter * DQ + d] = ov[d];
-    if (quarter == 0) p.part_ml[prow] = make_float2(m_run, l_run);
+    if (quarter == 0)
+      p.part_ml[static_cast<int64_t>(u - c) * p.rows_wg + (r - rg * kRowsWGf32) * nch + c] =
+          make_float4(m_run, l_run, 0.f, 0.f);
   }
   };
 
+  // Padding outputs first: their stores drain while the first tiles load.
+  finish_non_live<D>(p, st0);
   const int u0 = first_unit(p);
   for (int u = u0;; u += p.nw) {
     int b, kvh, rg, c, nch;
@@ -908,112 +1021,104 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
     if (u != u0) __syncthreads();  // the previous unit's LDS reads are done
     run_unit(u, b, kvh, rg, c, nch);
   }
-  finish_non_live<D>(p);
 }
 
 // ----------------------------------------------------- log-sum-exp merge ---
-// One wave per packed row merges the chunk partials of sequences with more
-// than one chunk: m* = max m_c, l* = sum l_c 2^(m_c - m*),
-// O = sum O_c 2^(m_c - m*) / l*, lse = (m* + log2 l*) ln 2.
-// Lane c holds chunk c's (m, l) and weight; the partial rows are fetched
-// sixteen chunks at a time with independent loads (clamped chunk index, zero
-// weight past the end), issued together with the (m, l) loads, so the merge
-// is bandwidth- rather than latency-bound.
+// Merges the unit partials of pairs with more than one unit:
+// m* = max m_c, l* = sum l_c 2^(m_c - m*), O = sum O_c 2^(m_c - m*) / l*,
+// lse = (m* + log2 l*) ln 2. D/4 lanes share a packed row, four entries of
+// it each. The (m, l) of a row's units are contiguous (the split kernel
+// writes them as [row][unit] per pair), so every lane of the row reads them
+// all with a broadcast load and computes the weights itself: no cross-lane
+// reduction. Up to 16 units per round are requested at once. Q16: the
+// partial rows are int16 fixed point, entry = q * scale / 32767.
 
-template <int D>
+template <int D, bool Q16>
 __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParams p) {
-  constexpr int PER = D / tv::kWave;  // floats per lane (2 at D = 128)
-  typedef float vecf __attribute__((ext_vector_type(PER)));
+  constexpr int LPR = D / 4;                                     // lanes per packed row
+  constexpr int RPB = kThreadsCombine / LPR;                     // packed rows per block
   constexpr int U = 16;
   const int bk = blockIdx.y;
   const int b = bk / p.Hkv;
   const int kvh = bk - b * p.Hkv;
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * (kThreadsCombine / tv::kWave) + (threadIdx.x >> 6);
+  const int sub = threadIdx.x & (LPR - 1);
+  const int r = blockIdx.x * RPB + threadIdx.x / LPR;
+  // Every scalar input in one round trip.
+  const int n = p.n_nodes[b];
+  const int L = p.ctx_len[b];
+  const int K = p.sched[0];
+  const int first = p.sched[1 + b];
+  // Keeps the four loads ahead of the branches below (the compiler would
+  // otherwise sink each one into the branch that first needs it and wait
+  // for them one by one).
+  asm volatile("" ::"s"(n), "s"(L), "s"(K), "s"(first));
   if (r >= p.R) return;
-  int n, L;
-  if (seq_check(p, b, n, L) != TV_ROW_OK) return;  // padded / invalid: done by the split
-  const int nch = pair_units(p, L, p.sched[0]);
-  if (nch == 1) return;                             // written directly by the split
+  if (seq_status(p, n, L) != TV_ROW_OK) return;  // padded / invalid: done by the split
+  const int nch = pair_units(p, L, K);
+  if (nch == 1) return;                           // written directly by the split
   const int i = r / p.G;
   const int h = kvh * p.G + (r - i * p.G);
   const int64_t orow = (static_cast<int64_t>(b) * p.T + i) * p.Hq + h;
-  float* dst = p.out + orow * D;
+  float4* dst = reinterpret_cast<float4*>(p.out + orow * D) + sub;
   if (i >= n) {
-    *reinterpret_cast<vecf*>(dst + PER * lane) = vecf(0.f);
-    if (lane == 0) p.lse[orow] = -INFINITY;
+    *dst = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (sub == 0) p.lse[orow] = -INFINITY;
     return;
   }
-  // Partial row of chunk cc: unit u0 + cc, row r - rg rows_wg of that unit.
   const int rg = r / p.rows_wg;
-  const int64_t u0 = p.sched[1 + b] + static_cast<int64_t>(kvh * p.RG + rg) * nch;
-  const int64_t base = u0 * p.rows_wg + (r - rg * p.rows_wg);
-  const int64_t stride = p.rows_wg;
-  auto row_of = [&](int c) __attribute__((always_inline)) {
-    return *reinterpret_cast<const vecf*>(p.part_o + (base + c * stride) * D + PER * lane);
-  };
-  float mstar, lstar;
-  vecf acc = vecf(0.f);
-  if (nch <= tv::kWave) {
-    // One round trip: lane c's (m, l) and the first U partial rows are
-    // requested together; only the weights wait for the maxima.
-    float2 ml = make_float2(-INFINITY, 0.f);
-    if (lane < nch) ml = p.part_ml[base + lane * stride];
-    vecf v[U];
+  const int rl = r - rg * p.rows_wg;
+  const int64_t u0 = first + static_cast<int64_t>(kvh * p.RG + rg) * nch;
+  const int64_t row_elem = (u0 * p.rows_wg + rl) * D + 4 * sub;  // entry offset of unit 0
+  const int64_t ustride = static_cast<int64_t>(p.rows_wg) * D;    // entries between units
+  const float4* pml = p.part_ml + u0 * p.rows_wg + static_cast<int64_t>(rl) * nch;
+  float mstar = -INFINITY, lstar = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < nch; c0 += U) {
+    // Unconditional loads (units past the last re-read it, with weight 0),
+    // so that all of them are in flight together.
+    float4 ml[U];
+    float4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = row_of(min(u, nch - 1));
-    mstar = tv::wave_max(ml.x);
-    const float w = lane < nch ? exp2f(ml.x - mstar) : 0.f;
-    lstar = tv::wave_sum(ml.y * w);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
-      acc += v[u] * (u < nch ? wu : 0.f);
-    }
-    for (int k = U; k < nch; k += U) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = row_of(min(k + u, nch - 1));
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float wu =
-            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(k + u, 63)));
-        acc += v[u] * (k + u < nch ? wu : 0.f);
+    for (int k = 0; k < U; ++k) {
+      const int kk = min(c0 + k, nch - 1);
+      ml[k] = pml[kk];
+      const int64_t off = row_elem + kk * ustride;
+      if constexpr (Q16) {
+        const uint2 raw =
+            *reinterpret_cast<const uint2*>(reinterpret_cast<const int16_t*>(p.part_o) + off);
+        v[k] = make_float4(static_cast<float>(static_cast<int16_t>(raw.x & 0xFFFFu)),
+                           static_cast<float>(static_cast<int16_t>(raw.x >> 16)),
+                           static_cast<float>(static_cast<int16_t>(raw.y & 0xFFFFu)),
+                           static_cast<float>(static_cast<int16_t>(raw.y >> 16)));
+      } else {
+        v[k] = *reinterpret_cast<const float4*>(p.part_o + off);
       }
     }
-  } else {
-    mstar = -INFINITY;
-    for (int c0 = 0; c0 < nch; c0 += tv::kWave) {
-      const int cc = c0 + lane;
-      if (cc < nch) mstar = fmaxf(mstar, p.part_ml[base + cc * stride].x);
-    }
-    mstar = tv::wave_max(mstar);
-    float lpart = 0.f;
-    for (int c0 = 0; c0 < nch; c0 += tv::kWave) {
-      const int cc = c0 + lane;
-      float w = 0.f;
-      if (cc < nch) {
-        const float2 ml = p.part_ml[base + cc * stride];
-        w = exp2f(ml.x - mstar);
-        lpart = fmaf(ml.y, w, lpart);
-      }
-      const int cnt = min(tv::kWave, nch - c0);
-      for (int k = 0; k < cnt; k += U) {
-        vecf v[U];
+    float m = mstar;
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = row_of(c0 + min(k + u, cnt - 1));
+    for (int k = 0; k < U; ++k) m = fmaxf(m, ml[k].x);
+    // Units with finite m only (a live row's reference always is).
+    const float sc = mstar == -INFINITY ? 0.f : exp2f(mstar - m);
+    lstar *= sc;
+    acc.x *= sc;
+    acc.y *= sc;
+    acc.z *= sc;
+    acc.w *= sc;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float wu =
-              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(k + u, 63)));
-          acc += v[u] * (k + u < cnt ? wu : 0.f);
-        }
-      }
+    for (int k = 0; k < U; ++k) {
+      const float wk = c0 + k < nch ? exp2f(ml[k].x - m) : 0.f;
+      lstar = fmaf(ml[k].y, wk, lstar);
+      const float wo = Q16 ? wk * (ml[k].z * (1.f / 32767.f)) : wk;
+      acc.x = fmaf(v[k].x, wo, acc.x);
+      acc.y = fmaf(v[k].y, wo, acc.y);
+      acc.z = fmaf(v[k].z, wo, acc.z);
+      acc.w = fmaf(v[k].w, wo, acc.w);
     }
-    lstar = tv::wave_sum(lpart);
+    mstar = m;
   }
   const float inv = 1.f / lstar;
-  *reinterpret_cast<vecf*>(dst + PER * lane) = acc * inv;
-  if (lane == 0) p.lse[orow] = (mstar + __log2f(lstar)) * kLn2;
+  *dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (sub == 0) p.lse[orow] = (mstar + __log2f(lstar)) * kLn2;
 }
 
 // Workgroups per launch: one per compute unit (a multiple of 8), cached per
@@ -1093,7 +1198,7 @@ WsLayout workspace_layout(int B, int T, int Hq, int Hkv, int D, int max_ctx, int
   w.sched = 0;
   w.part_o = tvh::align_up(static_cast<size_t>(1 + B) * sizeof(int32_t), 256);
   w.part_ml = w.part_o + tvh::align_up(static_cast<size_t>(rows_max) * D * sizeof(float), 256);
-  w.total = w.part_ml + tvh::align_up(static_cast<size_t>(rows_max) * sizeof(float2), 256);
+  w.total = w.part_ml + tvh::align_up(static_cast<size_t>(rows_max) * sizeof(float4), 256);
   return w;
 }
 
@@ -1110,8 +1215,12 @@ void launch_all(const AttnParams& p, int in_dtype, bool combine, hipStream_t str
   } else
     hipLaunchKernelGGL(attn_split_f32_kernel<D>, grid, dim3(kThreadsF32), 0, stream, p);
   if (combine) {
-    const dim3 cgrid((p.R + 3) / 4, p.B * p.Hkv);
-    hipLaunchKernelGGL(attn_combine_kernel<D>, cgrid, dim3(kThreadsCombine), 0, stream, p);
+    const dim3 cgrid((p.R + kThreadsCombine / (D / 4) - 1) / (kThreadsCombine / (D / 4)),
+                     p.B * p.Hkv);
+    if (in_dtype == TV_BF16 && p.parts == 1)
+      hipLaunchKernelGGL((attn_combine_kernel<D, true>), cgrid, dim3(kThreadsCombine), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_combine_kernel<D, false>), cgrid, dim3(kThreadsCombine), 0, stream, p);
   }
 }
 
@@ -1195,7 +1304,7 @@ extern "C" int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int6
     char* base = static_cast<char*>(workspace);
     p.sched = reinterpret_cast<int32_t*>(base + ws.sched);
     p.part_o = reinterpret_cast<float*>(base + ws.part_o);
-    p.part_ml = reinterpret_cast<float2*>(base + ws.part_ml);
+    p.part_ml = reinterpret_cast<float4*>(base + ws.part_ml);
   }
   p.row_status = row_status;
   if (D == 128)
