@@ -49,6 +49,9 @@ def parse():
                     help="target host time of the oracle baseline sample")
     ap.add_argument("--no-sampling", action="store_true",
                     help="skip the secondary sampling-acceptance measurement")
+    ap.add_argument("--graph", type=int, default=0,
+                    help="1: replay the steps from a captured HIP graph (the library's calls "
+                         "are graph-capturable); 0: launch them one by one")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -215,20 +218,21 @@ def main():
                torch.empty((B,), dtype=torch.int32, device=dev))
     dec = torch.empty((B, T), dtype=torch.int8, device=dev)
 
-    def step(i, ev=None):
+    def do_mask(i):
         s = sets[i % len(sets)]
         bb = bufs[i % len(bufs)]
-        if ev is not None:
-            ev[0].record()
-        mask, _, _ = tv.build_tree_mask(s["parent"], s["n"], out=bb["mask"])
-        if ev is not None:
-            ev[1].record()
-        tv.tree_attention(s["q"], s["k"], s["v"], s["ctx"], s["n"], mask, w.max_ctx,
+        return tv.build_tree_mask(s["parent"], s["n"], out=bb["mask"])[0]
+
+    def do_attention(i):
+        s = sets[i % len(sets)]
+        bb = bufs[i % len(bufs)]
+        tv.tree_attention(s["q"], s["k"], s["v"], s["ctx"], s["n"], bb["mask"][0], w.max_ctx,
                           scale=float(w.scale), probability_parts=args.parts,
                           chunk_keys=args.chunk, out=bb["out"], lse=bb["lse"],
                           row_status=bb["ast"], workspace=ws_attn)
-        if ev is not None:
-            ev[2].record()
+
+    def do_accept(i):
+        s = sets[i % len(sets)]
         if mode == 0:
             tv.accept_greedy(s["logits"], s["tokens"], s["parent"], s["n"], outputs=acc_out,
                              workspace=ws_acc)
@@ -236,33 +240,74 @@ def main():
             tv.accept_sample(s["logits"], float(w.temperature), s["qd"], s["u"], s["tokens"],
                              s["parent"], s["n"], outputs=acc_out[:4] + (dec, acc_out[4]),
                              workspace=ws_acc)
-        if ev is not None:
-            ev[3].record()
+
+    def step(i):
+        do_mask(i)
+        do_attention(i)
+        do_accept(i)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     # Timed region 1: whole steps, wall clock between two synchronisations.
+    # With --graph 1 one graph holds one step per input copy and is replayed.
+    nsets = len(sets)
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(nsets):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(nsets):
+                step(i)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+    steps = args.steps
+    if graph is not None:
+        steps = max(nsets, (args.steps + nsets - 1) // nsets * nsets)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
+    if graph is not None:
+        for _ in range(steps // nsets):
+            graph.replay()
+    else:
+        for i in range(steps):
+            step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # Timed region 2: the same steps with HIP events between the calls, on the
-    # stream the kernels are launched on.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    t_mask = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-    t_attn = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-    t_acc = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
+    # Timed region 2: each call of the step on its own, run back to back
+    # `reps` times between two HIP events recorded on the stream the kernels
+    # are launched on (torch's current stream, which the binding passes to
+    # the library); the average includes the launch gaps inside a call.
+    reps = max(20, args.steps)
 
-    ms_per_step = wall / args.steps * 1e3
+    def timed(fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t_mask = timed(do_mask)
+    t_attn = timed(do_attention)
+    t_acc = timed(do_accept)
+
+    ms_per_step = wall / steps * 1e3
     nodes = w.draft_nodes
-    value = nodes / (wall / args.steps)
+    value = nodes / (wall / steps)
     a_bytes = attention_alg_bytes(w)
     a_flops = attention_flops(w)
     acc_bytes = accept_alg_bytes(w)
@@ -273,14 +318,15 @@ def main():
         "value": round(value, 1),
         "unit": "verified draft nodes/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded; cold: %d rotating input copies)" % len(sets),
+        "data": "synthetic (seeded; cold: %d rotating input copies)%s" % (
+            len(sets), "; steps replayed from a HIP graph" if graph is not None else ""),
         "config": {
             "workload": "%s: B=%d (%d live), Hq/Hkv=%d/%d, D=%d, ctx %d..%d, N=%d draft nodes "
                         "(T=%d), V=%d, %s acceptance" % (

@@ -140,7 +140,11 @@ int tv_tree_attention_auto_chunk(int B, int T, int Hq, int Hkv, int max_ctx);
  *   in_dtype TV_F32 (fp32-faithful arithmetic) or TV_BF16 (bf16 matrix cores,
  *            fp32 accumulation)
  *   probability_parts  1..3 (bf16 only): the probabilities enter the P.V
- *            product as a sum of that many bf16 terms (3 = fp32-faithful P)
+ *            product as a sum of that many bf16 terms (3 = fp32-faithful P).
+ *            With 1, the per-unit partial outputs of split-KV are kept as
+ *            16-bit fixed point against each row's largest magnitude, which
+ *            adds at most max|v| / 65534 to each output entry; with 2 or 3
+ *            they are kept in fp32
  *   chunk_keys  keys per split-KV unit (multiple of 64, 64..65536), or 0 to
  *            let the device balance the units of the whole launch over its
  *            compute units from the actual lengths; results are bitwise

@@ -153,6 +153,43 @@ def test_attention_runaway_scores_redone_with_exact_max(where, parts):
     check_attention(w, got, want, atol_out=bf16_p_bound(w) if parts == 1 else 2e-3)
 
 
+@pytest.mark.parametrize("chunk", [256, 0])
+def test_attention_fixed_point_partials_error_bound(chunk):
+    # Every (node, head) row attends to one committed key of its own: its
+    # query is a multiple of that key, so the key's score lies ~28 above all
+    # others and its one-part probability is exactly 1 (the rest ~1e-12).
+    # Values are large (|v| up to ~300), so what is left of the error is the
+    # 16-bit fixed point of the split partials: at most max|v| / 65534 per
+    # entry. With two parts the partials stay fp32 and the error is tiny.
+    w = make_custom(131, 1, 7, 1, 128, 50, "bf16", [2000], 8, trie_tokens=False)
+    rng = np.random.default_rng(17)
+    kf = decode(w.k, w.dtype)
+    vf = decode(w.v, w.dtype)
+    qf = decode(w.q, w.dtype)
+    n, L = int(w.n_nodes[0]), int(w.ctx_len[0])
+    live = L + n
+    w.v[0, 0, :live] = bf16_bits_from_f32(64.0 * vf[0, 0, :live])
+    target = rng.integers(0, L, size=(n, w.Hq))
+    for i in range(n):
+        for h in range(w.Hq):
+            kk = kf[0, 0, target[i, h]]
+            alpha = 40.0 / (float(w.scale) * float(kk @ kk))
+            qf[0, i, h] = alpha * kk
+    w.q[0, :n] = bf16_bits_from_f32(qf[0, :n])
+    d = upload(w)
+    mask = _mask_check(w, d)
+    want = oracle_attention(w)
+    vmax = np.abs(decode(w.v, w.dtype)[0, 0, :live]).max()
+    bound = vmax / 65534.0
+    got1 = run_attention(w, d, mask, chunk_keys=chunk, parts=1)
+    err1 = np.abs(got1[0][0, :n] - want[0][0, :n]).max()
+    assert err1 <= bound * 1.001 + 1e-4, (err1, bound)
+    assert np.abs(got1[1][0, :n] - want[1][0, :n]).max() <= 1e-4
+    got2 = run_attention(w, d, mask, chunk_keys=chunk, parts=2)
+    err2 = np.abs(got2[0][0, :n] - want[0][0, :n]).max()
+    assert err2 <= 2e-4, err2
+
+
 def test_attention_many_rows_two_row_groups():
     # R = 16 heads per KV head x 65 rows = 1040 packed rows: five row groups.
     w = make_custom(51, 1, 16, 1, 128, 50, "bf16", [333], 64, max_depth=12, max_children=6,

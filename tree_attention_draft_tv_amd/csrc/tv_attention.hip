@@ -14,18 +14,20 @@
 //     queries": slots at or past ctx_len + n_nodes are never loaded.
 //
 // MI355X design (gfx950, wave64, 160 KB LDS, bf16 MFMA):
-//   * One workgroup (8 waves, two per SIMD) per (key chunk, row group,
-//     sequence, KV head). The G query heads of a KV head times the T tree
-//     rows form R = G*T packed rows (row r = node * G + head-in-group); a
-//     workgroup holds up to 256 of them, 32 per wave, so every key and value
-//     read from HBM is used by all G heads and all T nodes at once: the
-//     contraction over D and over keys is dense, so it runs on MFMA
+//   * A persistent grid of one workgroup (8 waves, two per SIMD) per compute
+//     unit. The G query heads of a KV head times the T tree rows form
+//     R = G*T packed rows (row r = node * G + head-in-group); a workgroup
+//     holds up to 256 of them, 32 per wave, so every key and value read from
+//     HBM is used by all G heads and all T nodes at once: the contraction
+//     over D and over keys is dense, so it runs on MFMA
 //     (v_mfma_f32_16x16x32_bf16).
-//   * Keys are cut into fixed chunks of C keys (split-KV). The last chunk of
-//     a sequence also covers the tree block [L, L + n), so tree masking
-//     only happens there; partial (m, l, O) go to a workspace and a second
-//     kernel merges them with a log-sum-exp combine. A sequence with one
-//     chunk is written directly.
+//   * The keys of every live (sequence, KV head, row group) pair are cut into
+//     units (split-KV); each workgroup derives the unit size and its own
+//     units from ctx_len / n_nodes on the device, balancing the launch. The
+//     last unit of a pair also covers the tree block [L, L + n), so tree
+//     masking only happens there; partial (m, l, O) go to a workspace and a
+//     second kernel merges them with a log-sum-exp combine. A pair with one
+//     unit is written directly.
 //   * K and V tiles of 64 keys are copied HBM -> LDS with
 //     global_load_lds_dwordx4 (no register staging) into a ring of four
 //     stages, two tiles ahead of the one being read. K is stored with an
@@ -34,10 +36,9 @@
 //   * S^T = K Q^T is computed so that a lane's accumulators always belong to
 //     one packed row and P^T lands directly in the MFMA B-operand layout.
 //   * Softmax in the log2 domain against a fixed per-row reference (the
-//     max of the chunk's first 32 scores): O is never rescaled, the per-key
-//     work is one FMA, one exp2, one add and a max3 per pair, and a pass
-//     whose scores rise more than 2^32 above the reference is redone with
-//     the exact chunk max.
+//     max of the unit's first 32 scores): O is never rescaled, the per-key
+//     work is one FMA, one exp2, one add and half a bf16 pack, and a pass
+//     whose row sums exceed 2^32 is redone with the exact unit max.
 //   * The loop is software-pipelined over 32-key sub-blocks: the S^T MFMAs
 //     of sub-block j+1 are issued together with the softmax of sub-block j,
 //     so matrix cores and VALU work side by side within a wave.
@@ -107,10 +108,6 @@ __device__ __forceinline__ int seq_check(const AttnParams& p, int b, int& n, int
   return seq_status(p, n, L);
 }
 
-
-__device__ __forceinline__ int num_chunks(int L, int chunk) {
-  return L == 0 ? 1 : (L + chunk - 1) / chunk;
-}
 
 // Padded (n == 0) and invalid sequences: every output row gets the padding
 // values (O = 0, lse = -inf) and every sequence its status, spread over the
@@ -1170,7 +1167,8 @@ bool valid_sizes(int B, int T, int Hq, int Hkv, int D, int max_ctx, int chunk_ke
 }
 
 // Workspace layout: the schedule table ((1 + B) int32), then partial O
-// [unit][rows_wg][D] fp32, then (m, l) [unit][rows_wg]. Sized for the larger
+// [unit][rows_wg][D] (fp32, or int16 fixed point in the same space), then
+// (m, l, scale, 0) per pair as [rows_wg][unit of the pair]. Sized for the larger
 // of the bf16 (256 rows per unit) and fp32 (64 rows per unit) kernels. No
 // workspace when every pair is a single unit (written directly).
 struct WsLayout {
