@@ -27,6 +27,11 @@ throughput" unless noted):
 * ``accept.accept_sample`` — SpecInfer-style rejection sampling against the
   draft with a residual resample (same commit; "exact SpecInfer-style
   acceptance" in the page's summary).
+* ``commit.commit_accepted_kv`` — the accepted path's keys and values become
+  contiguous committed context (commit "perf(activevln): lossless batched
+  replay throughput options", item incremental_kv_commit; the IluvatarLabs/vllm
+  page "Introduce SCV vectorized masking with graph/adaptive modes", its
+  commit kernel for accepted drafts).
 
 Every function works in float64 after decoding its inputs exactly from their
 stored float32 / bfloat16 values. Every result is pinned by tests against
@@ -35,6 +40,7 @@ closed forms, textbook special cases and brute force (tests/test_oracle_*.py).
 
 from .accept import accept_greedy, accept_sample, sample_probs  # noqa: F401
 from .attention import tree_attention  # noqa: F401
+from .commit import ROW_BAD_PATH, commit_accepted_kv  # noqa: F401
 from .decode import decode  # noqa: F401
 from .tree import ROW_BAD_PARENT, ROW_BAD_TOKEN, ROW_CTX_BOUND, ROW_NNODES, ROW_OK  # noqa: F401
 from .tree import ancestors, build_tree_mask  # noqa: F401
