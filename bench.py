@@ -49,6 +49,8 @@ def parse():
                     help="target host time of the oracle baseline sample")
     ap.add_argument("--no-sampling", action="store_true",
                     help="skip the secondary sampling-acceptance measurement")
+    ap.add_argument("--commit-layers", type=int, default=28,
+                    help="layers of the KV-commit measurement (0 skips it)")
     ap.add_argument("--graph", type=int, default=0,
                     help="1: replay the steps from a captured HIP graph (the library's calls "
                          "are graph-capturable); 0: launch them one by one")
@@ -361,10 +363,47 @@ def main():
 
     if not args.no_sampling and w.mode == "greedy":
         res["sampling"] = sampling_secondary(tv, torch, dev, args)
+    if args.commit_layers > 0 and w.mode == "greedy":
+        res["kv_commit"] = commit_secondary(tv, torch, dev, w, sets[0], acc_out, args)
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def commit_secondary(tv, torch, dev, w, s, acc_out, args):
+    """Accepted-path KV commit after the greedy acceptance of the same step,
+    into `layers` bf16 caches [layers, B, Hkv, capacity, D] (contents are
+    moved bit for bit, so they need no values); warm."""
+    layers = args.commit_layers
+    tv.accept_greedy(s["logits"], s["tokens"], s["parent"], s["n"], outputs=acc_out)
+    acc_len, path = acc_out[0], acc_out[1]
+    shape = (layers, w.B, w.Hkv, w.kv_capacity, w.D)
+    k = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    v = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    new_ctx = torch.empty((w.B,), dtype=torch.int32, device=dev)
+    st = torch.empty((w.B,), dtype=torch.int32, device=dev)
+
+    def call():
+        tv.commit_accepted_kv(k, v, s["ctx"], s["n"], acc_len, path, new_ctx_len=new_ctx,
+                              row_status=st)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    reps = max(20, args.steps)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    moved = int(acc_len.sum().item())
+    by = moved * w.Hkv * w.D * 2 * 2 * 2 * layers  # K and V rows, read + write, bf16
+    return {"workload": "C3 greedy acceptance, %d layers" % layers, "accepted_nodes": moved,
+            "commit_us": round(t * 1e6, 3), "alg_bytes": by, "GBps": round(by / t / 1e9, 1)}
 
 
 def sampling_secondary(tv, torch, dev, args):

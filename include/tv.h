@@ -63,7 +63,8 @@ typedef enum tv_row_status {
   TV_ROW_BAD_PARENT = 1, /* some live node i has parent outside [0, i) */
   TV_ROW_CTX_BOUND = 2,  /* ctx_len < 0, ctx_len > max_ctx or ctx_len + n > kv_capacity */
   TV_ROW_NNODES = 3,     /* n_nodes outside [0, T] */
-  TV_ROW_BAD_TOKEN = 4   /* some live draft token outside [0, V) */
+  TV_ROW_BAD_TOKEN = 4,  /* some live draft token outside [0, V) */
+  TV_ROW_BAD_PATH = 5    /* accepted path not 0 < path[1] < ... < path[a] < n, or a outside [0, n) */
 } tv_row_status;
 
 typedef enum tv_dtype { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
@@ -237,6 +238,41 @@ int tv_accept_sample(const float* logits, int64_t logits_row_stride, float tempe
                      int B, int T, int V, int32_t* accept_len, int32_t* path, int32_t* bonus,
                      uint8_t* accept_mask, int8_t* decision, void* workspace, size_t ws_bytes,
                      int32_t* row_status, hipStream_t stream);
+
+/*
+ * tv_commit_accepted_kv — accepted-path KV commit.
+ * (Page 1, commit "perf(activevln): lossless batched replay throughput
+ * options", item incremental_kv_commit: only the new turn is copied into the
+ * owned KV; page 3, the commit kernel for accepted drafts over NHD and HND
+ * cache layouts.)
+ *
+ * For each sequence b with n = n_nodes[b] > 0, L = ctx_len[b] and
+ * a = accept_len[b], in each of `layers` caches: slot L + k of K and of V
+ * takes what slot L + path[b][k] held before the call, for k = 1..a (slot L,
+ * the root, stays), and new_ctx_len[b] = L + a + 1. Every other slot is left
+ * as it is. A padded sequence (n = 0) or one with a bad status moves nothing
+ * and gets new_ctx_len = L. accept_len and path are the outputs of
+ * tv_accept_greedy / tv_accept_sample for the same tree.
+ *
+ *   k, v     caches of `layers` layers; element (layer, b, g, s, d) at
+ *            base + layer*layer_stride + b*kv_sb + g*kv_sh + s*kv_ss + d
+ *            (strides in elements of elem_bytes: HND and NHD both work)
+ *   elem_bytes 2 (bf16 / fp16) or 4 (fp32); elements are moved bit for bit
+ *   ctx_len, n_nodes, accept_len int32 [B]; path int32 [B][T]
+ *   new_ctx_len int32 [B] (output; must not be ctx_len itself)
+ *   row_status int32 [B]: TV_ROW_OK, TV_ROW_NNODES, TV_ROW_CTX_BOUND
+ *            (ctx_len < 0 or ctx_len + n > kv_capacity) or TV_ROW_BAD_PATH
+ *
+ * Constraints: D * elem_bytes a multiple of 16 and at most 512 (else
+ * TV_ERR_UNSUPPORTED); k, v 16-byte aligned and every stride a multiple of
+ * 16 bytes (else TV_ERR_ALIGN); 1 <= T <= TV_MAX_TREE; layers >= 1. The copy
+ * runs in place and in the stream order of the caller.
+ */
+int tv_commit_accepted_kv(void* k, void* v, int64_t layer_stride, int64_t kv_sb, int64_t kv_sh,
+                          int64_t kv_ss, const int32_t* ctx_len, const int32_t* n_nodes,
+                          const int32_t* accept_len, const int32_t* path, int B, int T, int Hkv,
+                          int D, int elem_bytes, int layers, int kv_capacity,
+                          int32_t* new_ctx_len, int32_t* row_status, hipStream_t stream);
 
 /* Static, human-readable name of a tv_status or tv_row_status value. */
 const char* tv_status_string(int code);

@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.SIGNATURES) == names
@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.tv_version() == 100
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, 1, 2, 3, 4):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, 1, 2, 3, 4, 5):
         s = lib.tv_status_string(code).decode()
         assert s and s != "unknown status", code
     assert lib.tv_status_string(99).decode() == "unknown status"
@@ -152,3 +152,30 @@ def test_python_binding_rejects_cpu_tensors():
     parent = torch.zeros((1, 4), dtype=torch.int32)
     with pytest.raises(tv.TVError):
         tv.build_tree_mask(parent, torch.ones(1, dtype=torch.int32))
+
+
+def _commit(lib, **kw):
+    a = dict(k=P, v=P2, layer_stride=0, kv_sb=4 * 8192 * 128, kv_sh=8192 * 128, kv_ss=128,
+             ctx=P, n=P, acc=P, path=P, B=8, T=33, Hkv=4, D=128, elem=2, layers=1, cap=8192,
+             new_ctx=P2, st=P2)
+    a.update(kw)
+    return lib.tv_commit_accepted_kv(a["k"], a["v"], a["layer_stride"], a["kv_sb"], a["kv_sh"],
+                                     a["kv_ss"], a["ctx"], a["n"], a["acc"], a["path"], a["B"],
+                                     a["T"], a["Hkv"], a["D"], a["elem"], a["layers"], a["cap"],
+                                     a["new_ctx"], a["st"], STREAM)
+
+
+def test_commit_validation(lib):
+    assert _commit(lib, k=NULL) == -1
+    assert _commit(lib, path=NULL) == -1
+    assert _commit(lib, elem=8) == -3
+    assert _commit(lib, T=0) == -2
+    assert _commit(lib, T=129) == -2
+    assert _commit(lib, layers=0) == -2
+    assert _commit(lib, B=-1) == -2
+    assert _commit(lib, D=4) == -6          # 8-byte rows
+    assert _commit(lib, D=512) == -6        # 1024-byte rows
+    assert _commit(lib, kv_ss=129) == -4    # stride not a multiple of 16 bytes
+    assert _commit(lib, k=ctypes.c_void_p(0x100008)) == -4
+    assert _commit(lib, new_ctx=P) == -2    # new_ctx_len may not be ctx_len
+    assert _commit(lib, B=0) == 0           # nothing to do

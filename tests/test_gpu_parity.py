@@ -434,6 +434,106 @@ def test_sample_draws_follow_target():
 
 # ----------------------------------------------------------- HIP graphs ---
 
+# ------------------------------------------------------------ KV commit ---
+
+def _bits(t):
+    """Raw element bits of a device tensor (NaN payloads compared too)."""
+    a = t.cpu()
+    if a.dtype == torch.bfloat16:
+        return a.view(torch.int16).numpy()
+    return a.view(torch.int32).numpy()
+
+
+def _commit_case(w, k_host, v_host, acc, path, layers_first=False):
+    """Commit on the GPU (caches as given) and with the oracle; compare bits."""
+    dev_ = torch.device("cuda:0")
+    conv = (lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+        torch.bfloat16).to(dev_)) if w.dtype == "bf16" else (lambda a: torch.from_numpy(
+            np.ascontiguousarray(a)).to(dev_))
+    k, v = conv(k_host), conv(v_host)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev_)
+    ctx, n = i32(w.ctx_len), i32(w.n_nodes)
+    new_ctx, st = tv.commit_accepted_kv(k, v, ctx, n, i32(acc), i32(path))
+    torch.cuda.synchronize()
+    kr, vr, ctx_r, st_r = oracle.commit_accepted_kv(k_host, v_host, w.ctx_len, w.n_nodes, acc, path)
+    assert np.array_equal(st.cpu().numpy(), st_r), (st.cpu().numpy(), st_r)
+    assert np.array_equal(new_ctx.cpu().numpy(), ctx_r)
+    dt = np.int16 if w.dtype == "bf16" else np.int32
+    assert np.array_equal(_bits(k), np.ascontiguousarray(kr).view(dt))
+    assert np.array_equal(_bits(v), np.ascontiguousarray(vr).view(dt))
+    return st_r
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3"])
+def test_commit_after_greedy_acceptance(name):
+    # The path and accept_len come from the GPU acceptance of the same tree.
+    w = make_config(name)
+    d = upload(w)
+    al, path, _, _, st = run_greedy(d)
+    assert not st.any()
+    st_c = _commit_case(w, w.k, w.v, al, path)
+    assert not st_c.any()
+
+
+def test_commit_layers_nhd_fp32_and_long_paths():
+    # Three layers of an fp32 cache laid out [layer][B][capacity][Hkv][D]
+    # (NHD) and seen through strides; a chain of 128 rows whose path skips
+    # node 1 (slot L+k takes slot L+k+1: every source but the last is the
+    # next destination) across several 16-row batches; a bushy tree.
+    w = make_custom(91, 3, 8, 2, 64, 50, "f32", [300, 0, 41], 127, tree="chain",
+                    trie_tokens=False)
+    T = w.T
+    path = np.full((w.B, T), -1, np.int32)
+    acc = np.zeros(w.B, np.int32)
+    path[0, 0] = 0
+    path[0, 1:T - 1] = np.arange(2, T)
+    acc[0] = T - 2
+    path[1, :T] = np.arange(T)
+    acc[1] = T - 1
+    path[2, :3] = [0, 1, 2]
+    acc[2] = 2
+    rng = np.random.default_rng(2)
+    layers = 3
+    kl = np.stack([w.k + np.float32(10 * l) for l in range(layers)])
+    vl = np.stack([w.v - np.float32(10 * l) for l in range(layers)])
+    dev_ = torch.device("cuda:0")
+    # NHD storage, viewed as [layer][B][Hkv][capacity][D].
+    k_nhd = torch.from_numpy(np.ascontiguousarray(kl.transpose(0, 1, 3, 2, 4))).to(dev_)
+    v_nhd = torch.from_numpy(np.ascontiguousarray(vl.transpose(0, 1, 3, 2, 4))).to(dev_)
+    k = k_nhd.permute(0, 1, 3, 2, 4)
+    v = v_nhd.permute(0, 1, 3, 2, 4)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev_)
+    new_ctx, st = tv.commit_accepted_kv(k, v, i32(w.ctx_len), i32(w.n_nodes), i32(acc), i32(path))
+    torch.cuda.synchronize()
+    kr, vr, ctx_r, st_r = oracle.commit_accepted_kv(kl, vl, w.ctx_len, w.n_nodes, acc, path)
+    assert not st_r.any()
+    assert np.array_equal(st.cpu().numpy(), st_r) and np.array_equal(new_ctx.cpu().numpy(), ctx_r)
+    assert np.array_equal(k.cpu().numpy().view(np.int32), kr.view(np.int32))
+    assert np.array_equal(v.cpu().numpy().view(np.int32), vr.view(np.int32))
+    del rng
+
+
+def test_commit_status_and_untouched_sequences():
+    w = make_custom(93, 5, 4, 2, 128, 50, "bf16", [64, 10, 20, 30, 5], 9, padded_rows=[4],
+                    trie_tokens=False)
+    T = w.T
+    path = np.full((w.B, T), -1, np.int32)
+    acc = np.zeros(w.B, np.int32)
+    # 0: valid two-step path; 1: not increasing; 2: accept_len too long;
+    # 3: path[0] != 0; 4: padded sequence.
+    p0 = oracle.ancestors(w.parent[0], int(w.n_nodes[0]) - 1)[::-1]
+    path[0, :len(p0)] = p0
+    acc[0] = len(p0) - 1
+    path[1, :3] = [0, 2, 1]
+    acc[1] = 2
+    acc[2] = int(w.n_nodes[2])
+    path[2, :T] = np.arange(T)
+    path[3, :2] = [1, 2]
+    acc[3] = 1
+    st = _commit_case(w, w.k, w.v, acc, path)
+    assert list(st) == [0, oracle.ROW_BAD_PATH, oracle.ROW_BAD_PATH, oracle.ROW_BAD_PATH, 0]
+
+
 def test_graph_capture_replays_match_eager():
     w = make_config("C2")
     d = upload(w)

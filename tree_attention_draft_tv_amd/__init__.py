@@ -2,8 +2,9 @@
 
 Verifies a speculative draft token tree in one forward pass: ancestor masks
 (:func:`build_tree_mask`), tree-masked split-KV grouped-query attention
-(:func:`tree_attention`) and exact acceptance (:func:`accept_greedy`,
-:func:`accept_sample`). The compute runs in the HIP kernels of the in-tree
+(:func:`tree_attention`), exact acceptance (:func:`accept_greedy`,
+:func:`accept_sample`) and the commit of the accepted path's keys and values
+(:func:`commit_accepted_kv`). The compute runs in the HIP kernels of the in-tree
 ``libtv.so`` (C ABI in ``include/tv.h``); this package only marshals
 arguments.
 """
@@ -21,6 +22,7 @@ from .binding import (  # noqa: F401
     attention_workspace_size,
     auto_chunk,
     build_tree_mask,
+    commit_accepted_kv,
     load,
     tree_attention,
 )

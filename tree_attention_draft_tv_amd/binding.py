@@ -28,7 +28,7 @@ STATUS = {
     -4: "TV_ERR_ALIGN", -5: "TV_ERR_WORKSPACE", -6: "TV_ERR_UNSUPPORTED", -7: "TV_ERR_HIP",
 }
 ROW_STATUS = {0: "TV_ROW_OK", 1: "TV_ROW_BAD_PARENT", 2: "TV_ROW_CTX_BOUND",
-              3: "TV_ROW_NNODES", 4: "TV_ROW_BAD_TOKEN"}
+              3: "TV_ROW_NNODES", 4: "TV_ROW_BAD_TOKEN", 5: "TV_ROW_BAD_PATH"}
 
 # Every exported symbol of include/tv.h with its (restype, argtypes).
 _P = ctypes.c_void_p
@@ -47,6 +47,8 @@ SIGNATURES = {
     "tv_accept_greedy": (_I, [_P, _L, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _S, _P, _P]),
     "tv_accept_sample": (_I, [_P, _L, _F, _P, _L, _P, _P, _P, _P, _I, _I, _I,
                               _P, _P, _P, _P, _P, _P, _S, _P, _P]),
+    "tv_commit_accepted_kv": (_I, [_P, _P, _L, _L, _L, _L, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                   _I, _P, _P, _P]),
     "tv_status_string": (ctypes.c_char_p, [_I]),
     "tv_version": (_I, []),
 }
@@ -292,3 +294,52 @@ def accept_sample(logits: torch.Tensor, temperature: float, q: torch.Tensor, u: 
                                 _ptr(decision), _ptr(ws), ws_bytes, _ptr(status), _stream(dev)),
            "tv_accept_sample")
     return acc_len, path, bonus, amask, decision, status
+
+
+# ------------------------------------------------------------ KV commit ---
+
+def commit_accepted_kv(k: torch.Tensor, v: torch.Tensor, ctx_len: torch.Tensor,
+                       n_nodes: torch.Tensor, accept_len: torch.Tensor, path: torch.Tensor,
+                       new_ctx_len: Optional[torch.Tensor] = None,
+                       row_status: Optional[torch.Tensor] = None):
+    """Move the accepted path's keys and values to the committed prefix, in place.
+
+    k, v: [B, Hkv, kv_capacity, D] or [layers, B, Hkv, kv_capacity, D]
+    (bfloat16, float16 or float32; D contiguous; k and v share strides);
+    ctx_len, n_nodes, accept_len: int32 [B]; path: int32 [B, T] from the
+    acceptance call. Returns (new_ctx_len int32 [B], row_status int32 [B]).
+    """
+    lib = load()
+    dev = k.device
+    sizes = {torch.bfloat16: 2, torch.float16: 2, torch.float32: 4}
+    if k.dtype not in sizes:
+        raise TypeError("k must be bfloat16, float16 or float32")
+    _need(k, "k", k.dtype)
+    _need(v, "v", k.dtype, dev)
+    for t, name in ((ctx_len, "ctx_len"), (n_nodes, "n_nodes"), (accept_len, "accept_len"),
+                    (path, "path")):
+        _need(t, name, torch.int32, dev)
+    if k.dim() == 4:
+        layers, kk, vv = 1, k.unsqueeze(0), v.unsqueeze(0)
+    elif k.dim() == 5:
+        layers, kk, vv = k.shape[0], k, v
+    else:
+        raise TVError("k, v must be [B, Hkv, capacity, D] or [layers, B, Hkv, capacity, D]")
+    if v.shape != k.shape or kk.stride() != vv.stride():
+        raise TVError("k and v must have the same shape and strides")
+    if kk.stride(4) != 1:
+        raise TVError("the head dimension must be contiguous")
+    _, B, Hkv, cap, D = kk.shape
+    if path.dim() != 2 or path.shape[0] != B or not path.is_contiguous():
+        raise TVError("path must be a contiguous [B, T] tensor")
+    T = path.shape[1]
+    if new_ctx_len is None:
+        new_ctx_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if row_status is None:
+        row_status = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(lib.tv_commit_accepted_kv(
+        _ptr(kk), _ptr(vv), kk.stride(0) if layers > 1 else 0, kk.stride(1), kk.stride(2),
+        kk.stride(3), _ptr(ctx_len), _ptr(n_nodes), _ptr(accept_len), _ptr(path), B, T, Hkv, D,
+        sizes[k.dtype], layers, cap, _ptr(new_ctx_len), _ptr(row_status), _stream(dev)),
+        "tv_commit_accepted_kv")
+    return new_ctx_len, row_status

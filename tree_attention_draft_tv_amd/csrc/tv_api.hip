@@ -15,6 +15,7 @@ extern "C" const char* tv_status_string(int code) {
     case TV_ROW_CTX_BOUND: return "row: context length outside its bounds";
     case TV_ROW_NNODES: return "row: n_nodes outside [0, T]";
     case TV_ROW_BAD_TOKEN: return "row: a draft token is outside the vocabulary";
+    case TV_ROW_BAD_PATH: return "row: the accepted path is not an increasing walk from the root";
     default: return "unknown status";
   }
 }
