@@ -27,6 +27,11 @@ throughput" unless noted):
 * ``accept.accept_sample`` — SpecInfer-style rejection sampling against the
   draft with a residual resample (same commit; "exact SpecInfer-style
   acceptance" in the page's summary).
+* ``block.build_block_mask`` and ``attention.masked_attention`` — draft
+  blocks instead of trees: a linear (causal) block, or a block whose rows all
+  see one another (the DFlash block attention on the FlashRT page "Alpamayo
+  1.5 on Thor: full-request engine with precision presets and FlashDrive
+  streaming backend").
 * ``commit.commit_accepted_kv`` — the accepted path's keys and values become
   contiguous committed context (commit "perf(activevln): lossless batched
   replay throughput options", item incremental_kv_commit; the IluvatarLabs/vllm
@@ -39,7 +44,8 @@ closed forms, textbook special cases and brute force (tests/test_oracle_*.py).
 """
 
 from .accept import accept_greedy, accept_sample, sample_probs  # noqa: F401
-from .attention import tree_attention  # noqa: F401
+from .attention import masked_attention, tree_attention  # noqa: F401
+from .block import BIDIRECTIONAL, CAUSAL, build_block_mask  # noqa: F401
 from .commit import ROW_BAD_PATH, commit_accepted_kv  # noqa: F401
 from .decode import decode  # noqa: F401
 from .tree import ROW_BAD_PARENT, ROW_BAD_TOKEN, ROW_CTX_BOUND, ROW_NNODES, ROW_OK  # noqa: F401

@@ -41,6 +41,41 @@ def tree_attention(q, k, v, dtype, ctx_len, n_nodes, parent, scale,
     [B]). Padding rows (i >= n_nodes[b]) and rows whose status is not OK get
     out = 0 and lse = -inf.
     """
+    def tree_keys(b, n):
+        # Tree node j lives in slot L + j; node i sees its ancestors-or-self.
+        if not parents_valid(parent[b], n):
+            raise ValueError("row %d: parent links are not a topologically ordered tree" % b)
+        vis = np.zeros((n, n), dtype=bool)
+        for i in range(n):
+            for j in ancestors(parent[b], i):
+                vis[i, j] = True
+        return vis
+
+    return _attention(q, k, v, dtype, ctx_len, n_nodes, tree_keys, scale, max_ctx, kv_capacity)
+
+
+def masked_attention(q, k, v, dtype, ctx_len, n_nodes, mask, scale,
+                     max_ctx=None, kv_capacity=None):
+    """Exact float64 attention with the draft rows' visibility given as bit
+    masks: row i of sequence b sees the whole committed context and block key
+    j (slot ctx_len + j, j < n_nodes) iff bit j of word j // 32 of
+    mask[b, i] is set. Same arguments and results as :func:`tree_attention`
+    otherwise (mask: uint32 [B, T, ceil(T / 32)])."""
+    mask = np.asarray(mask, dtype=np.uint32)
+
+    def mask_keys(b, n):
+        vis = np.zeros((n, n), dtype=bool)
+        for i in range(n):
+            for j in range(n):
+                vis[i, j] = bool((int(mask[b, i, j // 32]) >> (j % 32)) & 1)
+        return vis
+
+    return _attention(q, k, v, dtype, ctx_len, n_nodes, mask_keys, scale, max_ctx, kv_capacity)
+
+
+def _attention(q, k, v, dtype, ctx_len, n_nodes, draft_keys, scale, max_ctx, kv_capacity):
+    """The definition, with the draft-key visibility of sequence b given by
+    draft_keys(b, n) -> bool [n, n]."""
     B, T, Hq, D = q.shape
     Hkv = k.shape[1]
     Lcap = k.shape[2]
@@ -64,15 +99,11 @@ def tree_attention(q, k, v, dtype, ctx_len, n_nodes, parent, scale,
         if L < 0 or L > max_ctx or L + n > kv_capacity:
             status[b] = ROW_CTX_BOUND
             continue
-        if not parents_valid(parent[b], n):
-            raise ValueError("row %d: parent links are not a topologically ordered tree" % b)
-        # Visible keys of node i: the whole committed context, then the tree
-        # keys of its ancestors-or-self (tree node j lives in slot L + j).
+        # Visible keys of row i: the whole committed context, then the draft
+        # keys draft_keys allows (draft row j lives in slot L + j).
         visible = np.zeros((n, L + n), dtype=bool)
         visible[:, :L] = True
-        for i in range(n):
-            for j in ancestors(parent[b], i):
-                visible[i, L + j] = True
+        visible[:, L:] = draft_keys(b, n)
         for kv in range(Hkv):
             K = decode(k[b, kv, : L + n], dtype)
             Vv = decode(v[b, kv, : L + n], dtype)
