@@ -96,6 +96,31 @@ int tv_build_tree_mask(const int32_t* parent, const int32_t* n_nodes, int B, int
                        uint32_t* mask, int32_t* depth, int32_t* row_status,
                        hipStream_t stream);
 
+/* Draft-block visibility modes of tv_build_block_mask. */
+enum tv_block_mode {
+  TV_BLOCK_CAUSAL = 0,        /* row i sees block rows 0..i (a linear draft) */
+  TV_BLOCK_BIDIRECTIONAL = 1  /* every live row sees every live row */
+};
+
+/*
+ * tv_build_block_mask — visibility masks of a draft block instead of a tree,
+ * in the layout tv_tree_attention takes (bit j of word j / 32 of
+ * mask[b][i]: block key j, in cache slot ctx_len + j). (Page 4, the DFlash
+ * draft block: its rows attend over the context plus the block keys;
+ * TV_BLOCK_CAUSAL is the linear draft block, whose verification is causal.)
+ *
+ *   n_nodes  int32 [B]: live rows of each block (0: padded sequence)
+ *   mode     TV_BLOCK_CAUSAL or TV_BLOCK_BIDIRECTIONAL (else TV_ERR_UNSUPPORTED)
+ *   mask     uint32 [B][T][ceil(T/32)]; padding rows are all zero
+ *   position int32 [B][T]: i on live rows (position offset after the
+ *            committed context), -1 on padding rows and bad sequences
+ *   row_status int32 [B]: TV_ROW_OK or TV_ROW_NNODES (n outside [0, T]:
+ *            that sequence gets zero masks)
+ * 1 <= T <= TV_MAX_TREE; B >= 0 (B == 0 enqueues nothing).
+ */
+int tv_build_block_mask(const int32_t* n_nodes, int B, int T, int mode, uint32_t* mask,
+                        int32_t* position, int32_t* row_status, hipStream_t stream);
+
 /*
  * Workspace (bytes) tv_tree_attention needs for these sizes and chunk choice
  * on the current device (chunk_keys == 0: units balanced on the device).

@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.SIGNATURES) == names
@@ -54,6 +54,16 @@ def test_mask_validation(lib):
     assert lib.tv_build_tree_mask(P, P, 1, 129, P, P, P, STREAM) == -2
     assert lib.tv_build_tree_mask(P, P, -1, 4, P, P, P, STREAM) == -2
     assert lib.tv_build_tree_mask(P, P, 0, 4, P, P, P, STREAM) == 0  # nothing to do
+
+
+def test_block_mask_validation(lib):
+    assert lib.tv_build_block_mask(NULL, 1, 4, 0, P, P, P, STREAM) == -1
+    assert lib.tv_build_block_mask(P, 1, 4, 0, NULL, P, P, STREAM) == -1
+    assert lib.tv_build_block_mask(P, 1, 0, 0, P, P, P, STREAM) == -2
+    assert lib.tv_build_block_mask(P, 1, 129, 1, P, P, P, STREAM) == -2
+    assert lib.tv_build_block_mask(P, -1, 4, 0, P, P, P, STREAM) == -2
+    assert lib.tv_build_block_mask(P, 1, 4, 2, P, P, P, STREAM) == -6
+    assert lib.tv_build_block_mask(P, 0, 4, 1, P, P, P, STREAM) == 0
 
 
 def _attn(lib, **kw):

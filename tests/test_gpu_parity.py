@@ -434,6 +434,40 @@ def test_sample_draws_follow_target():
 
 # ----------------------------------------------------------- HIP graphs ---
 
+# ---------------------------------------------------------- draft blocks ---
+
+@pytest.mark.parametrize("T", [1, 16, 33, 100, 128])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_block_mask_matches_oracle(T, mode):
+    n = np.array([T, 0, T // 2, 1, -1, T + 1, max(T - 1, 0)], dtype=np.int32)
+    d = torch.from_numpy(n).to(torch.device("cuda:0"))
+    mask, pos, st = tv.build_block_mask(d, T, mode)
+    torch.cuda.synchronize()
+    m_ref, p_ref, s_ref = oracle.build_block_mask(n, T, mode)
+    assert np.array_equal(st.cpu().numpy(), s_ref)
+    assert np.array_equal(mask.cpu().numpy().view(np.uint32), m_ref)
+    assert np.array_equal(pos.cpu().numpy(), p_ref)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("chunk", [256, 0])
+def test_attention_draft_blocks(mode, chunk):
+    # A verification block of 16 rows per sequence (one padded sequence)
+    # over ragged contexts: causal (linear draft) or bidirectional (the
+    # DFlash block attention). The attention kernel is the tree kernel fed
+    # with the block mask.
+    w = make_custom(141 + mode, 4, 28, 4, 128, 50, "bf16", [1500, 600, 0, 2047], 15,
+                    tree="chain", trie_tokens=False, padded_rows=[1])
+    d = upload(w)
+    mask, pos, st = tv.build_block_mask(d["n_nodes"], w.T, mode)
+    torch.cuda.synchronize()
+    m_host = mask.cpu().numpy().view(np.uint32)
+    got = run_attention(w, d, mask, chunk_keys=chunk)
+    want = oracle.masked_attention(w.q, w.k, w.v, w.dtype, w.ctx_len, w.n_nodes, m_host, w.scale,
+                                   max_ctx=w.max_ctx, kv_capacity=w.kv_capacity)
+    check_attention(w, got, want, atol_out=bf16_p_bound(w))
+
+
 # ------------------------------------------------------------ KV commit ---
 
 def _bits(t):

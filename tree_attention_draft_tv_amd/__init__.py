@@ -1,7 +1,7 @@
 """Tree-draft verification for AMD MI355X (gfx950).
 
 Verifies a speculative draft token tree in one forward pass: ancestor masks
-(:func:`build_tree_mask`), tree-masked split-KV grouped-query attention
+(:func:`build_tree_mask`; :func:`build_block_mask` for draft blocks), tree-masked split-KV grouped-query attention
 (:func:`tree_attention`), exact acceptance (:func:`accept_greedy`,
 :func:`accept_sample`) and the commit of the accepted path's keys and values
 (:func:`commit_accepted_kv`). The compute runs in the HIP kernels of the in-tree
@@ -12,6 +12,8 @@ arguments.
 from .binding import (  # noqa: F401
     LIB_PATH,
     TV_BF16,
+    TV_BLOCK_BIDIRECTIONAL,
+    TV_BLOCK_CAUSAL,
     TV_F32,
     TV_MAX_GROUP,
     TV_MAX_TREE,
@@ -21,6 +23,7 @@ from .binding import (  # noqa: F401
     accept_workspace_size,
     attention_workspace_size,
     auto_chunk,
+    build_block_mask,
     build_tree_mask,
     commit_accepted_kv,
     load,

@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtv.so")
 
 TV_F32 = 0
 TV_BF16 = 1
+TV_BLOCK_CAUSAL = 0
+TV_BLOCK_BIDIRECTIONAL = 1
 TV_MAX_TREE = 128
 TV_MAX_GROUP = 16
 
@@ -38,6 +40,7 @@ _S = ctypes.c_size_t
 _F = ctypes.c_float
 SIGNATURES = {
     "tv_build_tree_mask": (_I, [_P, _P, _I, _I, _P, _P, _P, _P]),
+    "tv_build_block_mask": (_I, [_P, _I, _I, _I, _P, _P, _P, _P]),
     "tv_tree_attention_workspace_size": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "tv_tree_attention_auto_chunk": (_I, [_I, _I, _I, _I, _I]),
     "tv_tree_attention": (_I, [_P, _L, _L, _L, _P, _P, _L, _L, _L, _P, _P, _P,
@@ -136,6 +139,28 @@ def build_tree_mask(parent: torch.Tensor, n_nodes: torch.Tensor,
     _check(lib.tv_build_tree_mask(_ptr(parent), _ptr(n_nodes), B, T, _ptr(mask), _ptr(depth),
                                   _ptr(status), _stream(dev)), "tv_build_tree_mask")
     return mask, depth, status
+
+
+def build_block_mask(n_nodes: torch.Tensor, T: int, mode: int = TV_BLOCK_CAUSAL,
+                     out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Masks of a draft block (TV_BLOCK_CAUSAL or TV_BLOCK_BIDIRECTIONAL) in
+    the layout of :func:`build_tree_mask`: (mask, position, row_status)."""
+    lib = load()
+    dev = n_nodes.device
+    _need(n_nodes, "n_nodes", torch.int32)
+    if n_nodes.dim() != 1 or not n_nodes.is_contiguous():
+        raise TVError("n_nodes must be a contiguous [B] tensor")
+    B = n_nodes.shape[0]
+    W = (T + 31) // 32
+    if out is None:
+        mask = torch.empty((B, T, W), dtype=torch.int32, device=dev)
+        pos = torch.empty((B, T), dtype=torch.int32, device=dev)
+        status = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        mask, pos, status = out
+    _check(lib.tv_build_block_mask(_ptr(n_nodes), B, int(T), int(mode), _ptr(mask), _ptr(pos),
+                                   _ptr(status), _stream(dev)), "tv_build_block_mask")
+    return mask, pos, status
 
 
 # ------------------------------------------------------------ attention ---
