@@ -720,9 +720,15 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
     bool need_ref = (attempt == 0);
     issue_tile(0);
     if (ntile > 1) issue_tile(1);
-    if (nfull > 0) {
-      // Waves without live rows compute on zero queries here rather than
-      // branch: the loop body stays one straight-line block.
+    if (nfull > 0 && !wave_active) {
+      // A wave without live rows (small trees and blocks leave whole waves
+      // of a row group empty) only takes part in the copies and barriers.
+      need_ref = false;
+#pragma unroll 1
+      for (int t = 0; t < nfull; ++t) enter_tile(t);
+    } else if (nfull > 0) {
+      // Waves with some live rows compute every row of their tiles: the
+      // loop body stays one straight-line block.
       enter_tile(0);
       f32x4_t sa[2][kRT], sb[2][kRT];
       bf16x8_t pb[PARTS][kRT];
