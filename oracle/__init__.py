@@ -32,6 +32,10 @@ throughput" unless noted):
   see one another (the DFlash block attention on the FlashRT page "Alpamayo
   1.5 on Thor: full-request engine with precision presets and FlashDrive
   streaming backend").
+* ``linear.linear_rows`` and ``linear.swiglu_rows`` — the few-row
+  projections of the verification rows with one output rounding, and the
+  rounded SwiGLU of the gate and up projections (commit "perf(activevln):
+  batch-invariant Triton GEMMs for decode projections").
 * ``commit.commit_accepted_kv`` — the accepted path's keys and values become
   contiguous committed context (commit "perf(activevln): lossless batched
   replay throughput options", item incremental_kv_commit; the IluvatarLabs/vllm
@@ -47,6 +51,7 @@ from .accept import accept_greedy, accept_sample, sample_probs  # noqa: F401
 from .attention import masked_attention, tree_attention  # noqa: F401
 from .block import BIDIRECTIONAL, CAUSAL, build_block_mask  # noqa: F401
 from .commit import ROW_BAD_PATH, commit_accepted_kv  # noqa: F401
+from .linear import linear_rows, round_bf16, silu, swiglu_rows  # noqa: F401
 from .decode import decode  # noqa: F401
 from .tree import ROW_BAD_PARENT, ROW_BAD_TOKEN, ROW_CTX_BOUND, ROW_NNODES, ROW_OK  # noqa: F401
 from .tree import ancestors, build_tree_mask  # noqa: F401
