@@ -49,6 +49,8 @@ def parse():
                     help="target host time of the oracle baseline sample")
     ap.add_argument("--no-sampling", action="store_true",
                     help="skip the secondary sampling-acceptance measurement")
+    ap.add_argument("--no-projections", action="store_true",
+                    help="skip the few-row projection measurement")
     ap.add_argument("--commit-layers", type=int, default=28,
                     help="layers of the KV-commit measurement (0 skips it)")
     ap.add_argument("--graph", type=int, default=0,
@@ -363,12 +365,60 @@ def main():
 
     if not args.no_sampling and w.mode == "greedy":
         res["sampling"] = sampling_secondary(tv, torch, dev, args)
+    if not args.no_projections and w.dtype == "bf16":
+        res["projections"] = projections_secondary(tv, torch, dev, w, args)
     if args.commit_layers > 0 and w.mode == "greedy":
         res["kv_commit"] = commit_secondary(tv, torch, dev, w, sets[0], acc_out, args)
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def projections_secondary(tv, torch, dev, w, args):
+    """Batch-invariant few-row projections of the B*T verification rows:
+    the fused Q/K/V projection (hidden 3584 = 28 x 128 -> 28 + 4 + 4 heads of
+    128) and gate/up with the rounded SwiGLU (intermediate 18944), the sizes
+    of a Qwen2-7B-class decoder layer; random bf16 weights. torch.matmul
+    (hipBLASLt) on the same shapes is timed beside them as context. Warm."""
+    M, K = w.B * w.T, w.Hq * w.D
+    n_qkv, n_ffn = (w.Hq + 2 * w.Hkv) * w.D, 18944
+    g = torch.Generator(device=dev).manual_seed(11)
+    x = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+    wq = (torch.randn((n_qkv, K), generator=g, device=dev) / K ** 0.5).to(torch.bfloat16)
+    wg = (torch.randn((n_ffn, K), generator=g, device=dev) / K ** 0.5).to(torch.bfloat16)
+    wu = (torch.randn((n_ffn, K), generator=g, device=dev) / K ** 0.5).to(torch.bfloat16)
+    yq = torch.empty((M, n_qkv), dtype=torch.bfloat16, device=dev)
+    yf = torch.empty((M, n_ffn), dtype=torch.bfloat16, device=dev)
+    reps = max(20, args.steps)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t_qkv = timed(lambda: tv.linear_rows(x, wq, out=yq))
+    t_ffn = timed(lambda: tv.linear_swiglu_rows(x, wg, wu, out=yf))
+    t_qkv_ref = timed(lambda: torch.matmul(x, wq.t()))
+    t_ffn_ref = timed(lambda: torch.nn.functional.silu(torch.matmul(x, wg.t())) *
+                      torch.matmul(x, wu.t()))
+    b_qkv = 2 * (n_qkv * K + M * K + M * n_qkv)
+    b_ffn = 2 * (2 * n_ffn * K + M * K + M * n_ffn)
+    return {"rows": M, "hidden": K,
+            "qkv": {"N": n_qkv, "us": round(t_qkv * 1e6, 3), "alg_bytes": b_qkv,
+                    "GBps": round(b_qkv / t_qkv / 1e9, 1),
+                    "torch_matmul_us": round(t_qkv_ref * 1e6, 3)},
+            "gate_up_swiglu": {"N": n_ffn, "us": round(t_ffn * 1e6, 3), "alg_bytes": b_ffn,
+                               "GBps": round(b_ffn / t_ffn / 1e9, 1),
+                               "torch_matmul_silu_mul_us": round(t_ffn_ref * 1e6, 3)}}
 
 
 def commit_secondary(tv, torch, dev, w, s, acc_out, args):

@@ -265,6 +265,36 @@ int tv_accept_sample(const float* logits, int64_t logits_row_stride, float tempe
                      int32_t* row_status, hipStream_t stream);
 
 /*
+ * tv_linear_rows — y = x W^T on the few verification rows, batch-invariant.
+ * (Page 1, commit "perf(activevln): batch-invariant Triton GEMMs for decode
+ * projections": FP32 accumulation in sequential K order without split-K, so
+ * a row's result depends neither on the tiles nor on the row count; Q, K and
+ * V share one launch when W holds the three projections stacked.)
+ *
+ *   x  bf16 [M][K], row stride x_stride elements (a multiple of 8, >= K)
+ *   w  bf16 [N][K] (output features x input features, the layout of a
+ *      PyTorch Linear weight), row stride w_stride (a multiple of 8, >= K)
+ *   y  bf16 [M][N], row stride y_stride (a multiple of 4, >= N): each entry
+ *      is the fp32 sum over k = 0..K-1 in that order, rounded to nearest even
+ * Constraints: K a multiple of 64, N a multiple of 128 (else TV_ERR_SHAPE),
+ * 0 <= M <= 65536; pointers 16-byte aligned (else TV_ERR_ALIGN). Sized for a
+ * few hundred rows; nothing is allocated.
+ */
+int tv_linear_rows(const void* x, int64_t x_stride, const void* w, int64_t w_stride, int M,
+                   int K, int N, void* y, int64_t y_stride, hipStream_t stream);
+
+/*
+ * tv_linear_swiglu_rows — the gate and up projections in one launch with
+ * the rounded SwiGLU in the epilogue (same page and commit): g and u are
+ * each rounded to bf16 as tv_linear_rows would return them, then
+ * y = bf16(silu(g) * u) with silu(g) = g / (1 + exp(-g)) in fp32.
+ * Arguments as tv_linear_rows; w_gate and w_up share w_stride.
+ */
+int tv_linear_swiglu_rows(const void* x, int64_t x_stride, const void* w_gate, const void* w_up,
+                          int64_t w_stride, int M, int K, int N, void* y, int64_t y_stride,
+                          hipStream_t stream);
+
+/*
  * tv_commit_accepted_kv — accepted-path KV commit.
  * (Page 1, commit "perf(activevln): lossless batched replay throughput
  * options", item incremental_kv_commit: only the new turn is copied into the

@@ -70,8 +70,9 @@ def oracle_attention(w):
 
 def bf16_p_bound(w):
     """Worst-case output error of one-part bf16 probabilities: each P is
-    rounded with relative error <= 2^-9, so |out - exact| <= 2^-9 max|v|
-    over the visible values (plus fp32 accumulation slack). Used for the
+    rounded to nearest with relative error <= 2^-8 (the unit roundoff of an
+    8-bit significand), so |out - exact| <= 2^-8 max|v| over the visible
+    values (plus fp32 accumulation slack). Used for the
     tiny-context edge cases, where few keys carry all the weight; the
     measured workloads meet 2e-3 directly."""
     from oracle import decode
@@ -81,7 +82,7 @@ def bf16_p_bound(w):
         if n:
             live = decode(w.v[b, :, : int(w.ctx_len[b]) + n], w.dtype)
             vmax = max(vmax, float(np.abs(live).max()))
-    return max(ATOL_OUT, 2.0 ** -9 * vmax + 1e-5)
+    return max(ATOL_OUT, 2.0 ** -8 * vmax + 1e-5)
 
 
 def check_attention(w, got, want, atol_out=ATOL_OUT, atol_lse=ATOL_LSE):

@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.SIGNATURES) == names
@@ -189,3 +189,18 @@ def test_commit_validation(lib):
     assert _commit(lib, k=ctypes.c_void_p(0x100008)) == -4
     assert _commit(lib, new_ctx=P) == -2    # new_ctx_len may not be ctx_len
     assert _commit(lib, B=0) == 0           # nothing to do
+
+
+def test_linear_validation(lib):
+    f = lib.tv_linear_rows
+    assert f(NULL, 3584, P, 3584, 264, 3584, 4608, P2, 4608, STREAM) == -1
+    assert f(P, 3584, P, 3584, 264, 3584 + 32, 4608, P2, 4608, STREAM) == -2   # K % 64
+    assert f(P, 3584, P, 3584, 264, 3584, 4608 + 64, P2, 4608 + 64, STREAM) == -2  # N % 128
+    assert f(P, 3584, P, 3584, -1, 3584, 4608, P2, 4608, STREAM) == -2
+    assert f(P, 3580, P, 3584, 264, 3584, 4608, P2, 4608, STREAM) == -2     # x_stride < K
+    assert f(P, 3592 + 4, P, 3584, 264, 3584, 4608, P2, 4608, STREAM) == -4  # x_stride % 8
+    assert f(ctypes.c_void_p(0x100008), 3584, P, 3584, 264, 3584, 4608, P2, 4608, STREAM) == -4
+    assert f(P, 3584, P, 3584, 0, 3584, 4608, P2, 4608, STREAM) == 0
+    g = lib.tv_linear_swiglu_rows
+    assert g(P, 3584, P, NULL, 3584, 264, 3584, 18944, P2, 18944, STREAM) == -1
+    assert g(P, 3584, P, P, 3584, 0, 3584, 18944, P2, 18944, STREAM) == 0

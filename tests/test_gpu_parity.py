@@ -468,6 +468,82 @@ def test_attention_draft_blocks(mode, chunk):
     check_attention(w, got, want, atol_out=bf16_p_bound(w))
 
 
+# ------------------------------------------------------ few-row projections ---
+
+def _bf16_dev(a):
+    from oracle.linear import bf16_bits
+    bits = bf16_bits(oracle.round_bf16(a))
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.device("cuda:0")), bits
+
+
+def _linear_bound(x_bits, w_bits, K):
+    """Accumulation part of the bound: 2 K 2^-24 sum |x w| (fp32 sums of K
+    terms in any order, with slack); the output rounding adds 2^-8 |exact|
+    (unit roundoff of bfloat16's 8-bit significand)."""
+    xf = np.abs(decode(x_bits, "bf16"))
+    wf = np.abs(decode(w_bits, "bf16"))
+    return 2.0 * K * 2.0 ** -24 * (xf @ wf.T)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 64, 128), (7, 192, 256), (65, 320, 128), (130, 128, 384),
+                                   (264, 3584, 4608)])
+def test_linear_rows_parity(M, K, N):
+    rng = np.random.default_rng(M + K + N)
+    x, xb = _bf16_dev(rng.normal(size=(M, K)))
+    w, wb = _bf16_dev(rng.normal(size=(N, K)) / np.sqrt(K))
+    y = tv.linear_rows(x, w)
+    torch.cuda.synchronize()
+    yg = y.float().cpu().numpy().astype(np.float64)
+    exact, _ = oracle.linear_rows(xb, wb)
+    tol = 2.0 ** -8 * np.abs(exact) + _linear_bound(xb, wb, K) + 1e-30
+    assert (np.abs(yg - exact) <= tol).all(), np.abs(yg - exact).max()
+
+
+def test_linear_rows_batch_invariant():
+    # A row's bits depend neither on the row count nor on its place in the
+    # batch (sequential K order, no split-K, whatever the tile).
+    rng = np.random.default_rng(5)
+    M, K, N = 264, 3584, 4608
+    x, _ = _bf16_dev(rng.normal(size=(M, K)))
+    w, _ = _bf16_dev(rng.normal(size=(N, K)) / np.sqrt(K))
+    full = tv.linear_rows(x, w).cpu().view(torch.int16).numpy()
+    for lo, hi in ((0, 1), (5, 71), (100, 264), (263, 264)):
+        part = tv.linear_rows(x[lo:hi].contiguous(), w).cpu().view(torch.int16).numpy()
+        assert np.array_equal(part, full[lo:hi]), (lo, hi)
+    perm = torch.from_numpy(rng.permutation(M)).to(x.device)
+    shuffled = tv.linear_rows(x[perm].contiguous(), w).cpu().view(torch.int16).numpy()
+    assert np.array_equal(shuffled, full[perm.cpu().numpy()])
+    # Strided input rows (a view into a wider buffer) give the same bits.
+    wide = torch.zeros((M, K + 64), dtype=torch.bfloat16, device=x.device)
+    wide[:, 32:32 + K] = x
+    assert np.array_equal(tv.linear_rows(wide[:, 32:32 + K], w).cpu().view(torch.int16).numpy(),
+                          full)
+
+
+@pytest.mark.parametrize("M,K,N", [(9, 64, 128), (264, 3584, 1024)])
+def test_linear_swiglu_rows(M, K, N):
+    rng = np.random.default_rng(7 * M + K)
+    x, xb = _bf16_dev(rng.normal(size=(M, K)))
+    wg, wgb = _bf16_dev(rng.normal(size=(N, K)) * 2.0 / np.sqrt(K))
+    wu, wub = _bf16_dev(rng.normal(size=(N, K)) / np.sqrt(K))
+    y = tv.linear_swiglu_rows(x, wg, wu).float().cpu().numpy().astype(np.float64)
+    g = tv.linear_rows(x, wg).float().cpu().numpy().astype(np.float64)
+    u = tv.linear_rows(x, wu).float().cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    # The fused epilogue equals the rounded SwiGLU of the two projections
+    # (the same accumulation chains), up to the last bit of fp32 exp.
+    ref = oracle.round_bf16(oracle.silu(g) * u)
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    diff = np.abs(y - ref)
+    assert (diff <= ulp).all(), diff.max()
+    assert np.mean(diff == 0) > 0.99
+    # And the projections themselves against the oracle bound.
+    for got, wb in ((g, wgb), (u, wub)):
+        exact, _ = oracle.linear_rows(xb, wb)
+        tol = 2.0 ** -8 * np.abs(exact) + _linear_bound(xb, wb, K) + 1e-30
+        assert (np.abs(got - exact) <= tol).all()
+
+
 # ------------------------------------------------------------ KV commit ---
 
 def _bits(t):

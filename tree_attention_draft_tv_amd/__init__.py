@@ -4,7 +4,9 @@ Verifies a speculative draft token tree in one forward pass: ancestor masks
 (:func:`build_tree_mask`; :func:`build_block_mask` for draft blocks), tree-masked split-KV grouped-query attention
 (:func:`tree_attention`), exact acceptance (:func:`accept_greedy`,
 :func:`accept_sample`) and the commit of the accepted path's keys and values
-(:func:`commit_accepted_kv`). The compute runs in the HIP kernels of the in-tree
+(:func:`commit_accepted_kv`), plus the batch-invariant few-row projections
+of the verification rows (:func:`linear_rows`, :func:`linear_swiglu_rows`).
+The compute runs in the HIP kernels of the in-tree
 ``libtv.so`` (C ABI in ``include/tv.h``); this package only marshals
 arguments.
 """
@@ -26,6 +28,8 @@ from .binding import (  # noqa: F401
     build_block_mask,
     build_tree_mask,
     commit_accepted_kv,
+    linear_rows,
+    linear_swiglu_rows,
     load,
     tree_attention,
 )

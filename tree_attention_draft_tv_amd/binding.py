@@ -52,6 +52,8 @@ SIGNATURES = {
                               _P, _P, _P, _P, _P, _P, _S, _P, _P]),
     "tv_commit_accepted_kv": (_I, [_P, _P, _L, _L, _L, _L, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                    _I, _P, _P, _P]),
+    "tv_linear_rows": (_I, [_P, _L, _P, _L, _I, _I, _I, _P, _L, _P]),
+    "tv_linear_swiglu_rows": (_I, [_P, _L, _P, _P, _L, _I, _I, _I, _P, _L, _P]),
     "tv_status_string": (ctypes.c_char_p, [_I]),
     "tv_version": (_I, []),
 }
@@ -368,3 +370,52 @@ def commit_accepted_kv(k: torch.Tensor, v: torch.Tensor, ctx_len: torch.Tensor,
         sizes[k.dtype], layers, cap, _ptr(new_ctx_len), _ptr(row_status), _stream(dev)),
         "tv_commit_accepted_kv")
     return new_ctx_len, row_status
+
+
+# ---------------------------------------------------- few-row projections ---
+
+def _linear_args(x, w, name):
+    _need(x, "x", torch.bfloat16)
+    _need(w, name, torch.bfloat16, x.device)
+    if x.dim() != 2 or w.dim() != 2 or x.stride(1) != 1 or w.stride(1) != 1:
+        raise TVError("x must be [M, K] and %s [N, K], rows contiguous" % name)
+    if w.shape[1] != x.shape[1]:
+        raise TVError("x and %s disagree on K" % name)
+
+
+def linear_rows(x: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """y = x w^T (bfloat16 in and out, fp32 accumulation in sequential K
+    order): x [M, K], w [N, K] -> y [M, N]."""
+    lib = load()
+    _linear_args(x, w, "w")
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, x.device)
+    if tuple(out.shape) != (M, N) or out.stride(1) != 1:
+        raise TVError("out must be [M, N] with contiguous rows")
+    _check(lib.tv_linear_rows(_ptr(x), x.stride(0), _ptr(w), w.stride(0), M, K, N, _ptr(out),
+                              out.stride(0), _stream(x.device)), "tv_linear_rows")
+    return out
+
+
+def linear_swiglu_rows(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
+                       out: Optional[torch.Tensor] = None):
+    """bf16(silu(g) * u) of the bfloat16-rounded gate and up projections."""
+    lib = load()
+    _linear_args(x, w_gate, "w_gate")
+    _linear_args(x, w_up, "w_up")
+    if w_gate.shape != w_up.shape or w_gate.stride() != w_up.stride():
+        raise TVError("w_gate and w_up must have the same shape and strides")
+    M, K = x.shape
+    N = w_gate.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, x.device)
+    if tuple(out.shape) != (M, N) or out.stride(1) != 1:
+        raise TVError("out must be [M, N] with contiguous rows")
+    _check(lib.tv_linear_swiglu_rows(_ptr(x), x.stride(0), _ptr(w_gate), _ptr(w_up),
+                                     w_gate.stride(0), M, K, N, _ptr(out), out.stride(0),
+                                     _stream(x.device)), "tv_linear_swiglu_rows")
+    return out

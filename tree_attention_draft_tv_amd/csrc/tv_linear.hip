@@ -1,0 +1,254 @@
+// Few-row projections of the verification rows, batch-invariant.
+//
+// Page: EmbodiInfer "perf(activevln): grammar-trie speculation and lossless
+// throughput", commit "perf(activevln): batch-invariant Triton GEMMs for
+// decode projections": tree verification runs every linear layer on a few
+// dozen to a few hundred rows; the projections accumulate in FP32 in
+// sequential K order with no split-K, so a row's result depends neither on
+// the tiles nor on the row count and differs from the vendor GEMM only by
+// output rounding. Q, K and V share one launch (one weight matrix holding
+// the three, one output row per input row); gate and up share one launch
+// with the rounded SwiGLU in the epilogue.
+//
+// MI355X: y^T = W x^T on v_mfma_f32_16x16x32_bf16, so that each lane ends
+// with four consecutive output features of one row (one 8-byte store). A
+// workgroup (4 waves) owns 64 rows x 128 output features; wave w the features
+// [32 w, 32 w + 32) of all 64 rows (2 x 4 accumulator tiles). Every output
+// element is one accumulator chain over k = 0, 32, 64, ... in order, whatever
+// the tile and the row count. K is walked in chunks of 64: the input rows of
+// a chunk (8 KB) go through a three-stage LDS ring shared by the four waves,
+// written from registers loaded two chunks ahead; each wave's weight rows go
+// straight to registers, also two chunks ahead. Loads are plain (in-order)
+// vector loads, so the compiler's partial waits keep two chunks in flight.
+// Workgroups are numbered so that the row groups of one weight slice run on
+// the same XCD and share its L2.
+#include "tv_common.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kLinThreads = 256;
+constexpr int kLinRows = 64;    // rows per workgroup
+constexpr int kLinFeat = 128;   // output features per workgroup (32 per wave)
+constexpr int kLinKC = 64;      // K per chunk (two MFMA k-steps)
+constexpr int kLinStages = 3;
+
+struct LinParams {
+  const uint16_t* x;
+  const uint16_t* w0;  // weights, or the gate weights
+  const uint16_t* w1;  // the up weights (SwiGLU only)
+  int64_t x_stride, w_stride, y_stride;
+  int M, K, N;
+  int mgroups, work;
+  uint16_t* y;
+};
+
+__device__ __forceinline__ bf16x8_t load8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u16x8_t*>(p));
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
+
+// LDS layout of an input chunk: 64 rows of 64 k (128 B, eight 16-byte
+// pieces); piece c of row r sits at piece c ^ (r & 7), so the 16 rows an MFMA
+// operand read touches at one k-offset spread over the banks.
+__device__ __forceinline__ int x_slot(int row, int piece) { return row * 8 + (piece ^ (row & 7)); }
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(kLinThreads) void linear_rows_kernel(LinParams p) {
+  __shared__ __attribute__((aligned(16))) u16x8_t sX[kLinStages][kLinRows * 8];
+  // Work item -> (weight slice, row group): the workgroups sharing
+  // blockIdx mod 8 (one XCD) take one contiguous run of work items, and the
+  // row groups of a slice are consecutive work items.
+  const int per_xcd = gridDim.x >> 3;
+  const int work = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (work >= p.work) return;
+  const int slice = work / p.mgroups;
+  const int mg = work - slice * p.mgroups;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int i16 = lane & 15;
+  const int kg = lane >> 4;
+  const int n0 = slice * kLinFeat + wave * 32;
+  const int m0 = mg * kLinRows;
+  const int nchunks = p.K / kLinKC;
+
+  // Staging: thread t loads pieces t and t + 256 of a chunk (row = s / 8,
+  // piece = s % 8); rows past M re-read row M - 1.
+  const uint16_t* xs[2];
+  int xslot[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int sidx = tid + 256 * j;
+    const int row = sidx >> 3;
+    const int piece = sidx & 7;
+    xs[j] = p.x + static_cast<int64_t>(min(m0 + row, p.M - 1)) * p.x_stride + 8 * piece;
+    xslot[j] = x_slot(row, piece);
+  }
+  // Weight rows of this lane: n-tile nt, k-step s of a chunk, 16 bytes.
+  const uint16_t* wg[2];
+  const uint16_t* wu[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    wg[nt] = p.w0 + static_cast<int64_t>(n0 + 16 * nt + i16) * p.w_stride + 8 * kg;
+    wu[nt] = SWIGLU ? p.w1 + static_cast<int64_t>(n0 + 16 * nt + i16) * p.w_stride + 8 * kg
+                    : nullptr;
+  }
+
+  struct Stage {
+    u16x8_t x[2];
+    bf16x8_t g[2][2];  // [nt][k-step]
+    bf16x8_t u[2][2];
+  };
+  auto load_chunk = [&](Stage& st, int c) __attribute__((always_inline)) {
+    const int k0 = c * kLinKC;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) st.x[j] = *reinterpret_cast<const u16x8_t*>(xs[j] + k0);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        st.g[nt][s] = load8(wg[nt] + k0 + 32 * s);
+        if constexpr (SWIGLU) st.u[nt][s] = load8(wu[nt] + k0 + 32 * s);
+      }
+  };
+  auto store_x = [&](const Stage& st, int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sX[stage][xslot[j]] = st.x[j];
+  };
+
+  f32x4_t a0[2][4], a1[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      a0[nt][mt] = f32x4_t(0.f);
+      a1[nt][mt] = f32x4_t(0.f);
+    }
+  auto compute = [&](const Stage& st, int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8_t xf[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        xf[mt] = __builtin_bit_cast(bf16x8_t, sX[stage][x_slot(16 * mt + i16, 4 * s + kg)]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          a0[nt][mt] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.g[nt][s], xf[mt], a0[nt][mt], 0, 0, 0);
+          if constexpr (SWIGLU)
+            a1[nt][mt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.u[nt][s], xf[mt], a1[nt][mt], 0, 0, 0);
+        }
+    }
+  };
+
+  // Chunk c lives in register stage c % 3 and LDS stage c % 3. Iteration c:
+  // request chunk c + 2, put chunk c + 1's input rows into LDS, barrier,
+  // compute chunk c. A barrier per chunk keeps the waves within one chunk of
+  // each other, so the stage being written, (c + 1) % 3, is never the one a
+  // slower wave still reads, c % 3 or (c - 1) % 3... (c - 1) % 3 is done
+  // before that wave reached this chunk's barrier.
+  Stage r0, r1, r2;
+  load_chunk(r0, 0);
+  if (nchunks > 1) load_chunk(r1, 1);
+  store_x(r0, 0);
+  __syncthreads();
+  auto iter = [&](Stage& cur, Stage& nxt, Stage& far, int c, int scur, int snxt)
+                  __attribute__((always_inline)) {
+    if (c + 2 < nchunks) load_chunk(far, c + 2);
+    if (c + 1 < nchunks) store_x(nxt, snxt);
+    compute(cur, scur);
+    __syncthreads();
+  };
+  int c = 0;
+  for (; c + 3 <= nchunks; c += 3) {
+    iter(r0, r1, r2, c, 0, 1);
+    iter(r1, r2, r0, c + 1, 1, 2);
+    iter(r2, r0, r1, c + 2, 2, 0);
+  }
+  if (c < nchunks) iter(r0, r1, r2, c, 0, 1);
+  if (c + 1 < nchunks) iter(r1, r2, r0, c + 1, 1, 2);
+
+  // Lane holds output features n0 + 16 nt + 4 kg + e (e = 0..3) of row
+  // m0 + 16 mt + i16.
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int m = m0 + 16 * mt + i16;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v;
+        if constexpr (SWIGLU) {
+          // The two projections rounded as separate outputs, then SwiGLU.
+          const float gr = tv::bf16_to_f32(tv::f32_to_bf16_rne(a0[nt][mt][e]));
+          const float ur = tv::bf16_to_f32(tv::f32_to_bf16_rne(a1[nt][mt][e]));
+          v = silu(gr) * ur;
+        } else {
+          v = a0[nt][mt][e];
+        }
+        h[e] = tv::f32_to_bf16_rne(v);
+      }
+      *reinterpret_cast<uint2*>(p.y + static_cast<int64_t>(m) * p.y_stride + n0 + 16 * nt +
+                                4 * kg) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    }
+  }
+}
+
+int launch_linear(const void* x, int64_t x_stride, const void* w0, const void* w1,
+                  int64_t w_stride, int M, int K, int N, void* y, int64_t y_stride,
+                  bool swiglu, hipStream_t stream) {
+  if (!x || !w0 || !y || (swiglu && !w1)) return TV_ERR_NULL;
+  if (M < 0 || K < kLinKC || N < kLinFeat || K % kLinKC || N % kLinFeat) return TV_ERR_SHAPE;
+  if (M > 65536) return TV_ERR_SHAPE;
+  if (!tvh::aligned16(x) || !tvh::aligned16(w0) || (swiglu && !tvh::aligned16(w1)) ||
+      !tvh::aligned16(y))
+    return TV_ERR_ALIGN;
+  if (x_stride < K || w_stride < K || y_stride < N) return TV_ERR_SHAPE;
+  if (x_stride % 8 || w_stride % 8 || y_stride % 4) return TV_ERR_ALIGN;
+  if (M == 0) return TV_OK;
+  LinParams p;
+  p.x = static_cast<const uint16_t*>(x);
+  p.w0 = static_cast<const uint16_t*>(w0);
+  p.w1 = static_cast<const uint16_t*>(w1);
+  p.x_stride = x_stride;
+  p.w_stride = w_stride;
+  p.y_stride = y_stride;
+  p.M = M;
+  p.K = K;
+  p.N = N;
+  p.mgroups = (M + kLinRows - 1) / kLinRows;
+  const int64_t work = static_cast<int64_t>(p.mgroups) * (N / kLinFeat);
+  if (work > (int64_t(1) << 30)) return TV_ERR_SHAPE;
+  p.work = static_cast<int>(work);
+  p.y = static_cast<uint16_t*>(y);
+  const int grid = (p.work + 7) / 8 * 8;
+  if (swiglu)
+    hipLaunchKernelGGL(linear_rows_kernel<true>, dim3(grid), dim3(kLinThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(linear_rows_kernel<false>, dim3(grid), dim3(kLinThreads), 0, stream, p);
+  return tvh::launch_status();
+}
+
+}  // namespace
+
+extern "C" int tv_linear_rows(const void* x, int64_t x_stride, const void* w, int64_t w_stride,
+                              int M, int K, int N, void* y, int64_t y_stride,
+                              hipStream_t stream) {
+  return launch_linear(x, x_stride, w, nullptr, w_stride, M, K, N, y, y_stride, false, stream);
+}
+
+extern "C" int tv_linear_swiglu_rows(const void* x, int64_t x_stride, const void* w_gate,
+                                     const void* w_up, int64_t w_stride, int M, int K, int N,
+                                     void* y, int64_t y_stride, hipStream_t stream) {
+  return launch_linear(x, x_stride, w_gate, w_up, w_stride, M, K, N, y, y_stride, true, stream);
+}
