@@ -276,7 +276,7 @@ int tv_accept_sample(const float* logits, int64_t logits_row_stride, float tempe
  *      PyTorch Linear weight), row stride w_stride (a multiple of 8, >= K)
  *   y  bf16 [M][N], row stride y_stride (a multiple of 4, >= N): each entry
  *      is the fp32 sum over k = 0..K-1 in that order, rounded to nearest even
- * Constraints: K a multiple of 64, N a multiple of 128 (else TV_ERR_SHAPE),
+ * Constraints: K and N multiples of 64 (else TV_ERR_SHAPE),
  * 0 <= M <= 65536; pointers 16-byte aligned (else TV_ERR_ALIGN). Sized for a
  * few hundred rows; nothing is allocated.
  */

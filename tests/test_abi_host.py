@@ -195,7 +195,7 @@ def test_linear_validation(lib):
     f = lib.tv_linear_rows
     assert f(NULL, 3584, P, 3584, 264, 3584, 4608, P2, 4608, STREAM) == -1
     assert f(P, 3584, P, 3584, 264, 3584 + 32, 4608, P2, 4608, STREAM) == -2   # K % 64
-    assert f(P, 3584, P, 3584, 264, 3584, 4608 + 64, P2, 4608 + 64, STREAM) == -2  # N % 128
+    assert f(P, 3584, P, 3584, 264, 3584, 4608 + 32, P2, 4608 + 32, STREAM) == -2  # N % 64
     assert f(P, 3584, P, 3584, -1, 3584, 4608, P2, 4608, STREAM) == -2
     assert f(P, 3580, P, 3584, 264, 3584, 4608, P2, 4608, STREAM) == -2     # x_stride < K
     assert f(P, 3592 + 4, P, 3584, 264, 3584, 4608, P2, 4608, STREAM) == -4  # x_stride % 8

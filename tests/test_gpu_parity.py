@@ -485,8 +485,8 @@ def _linear_bound(x_bits, w_bits, K):
     return 2.0 * K * 2.0 ** -24 * (xf @ wf.T)
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 64, 128), (7, 192, 256), (65, 320, 128), (130, 128, 384),
-                                   (264, 3584, 4608)])
+@pytest.mark.parametrize("M,K,N", [(1, 64, 64), (7, 192, 256), (65, 320, 128), (130, 128, 384),
+                                   (200, 704, 192), (264, 3584, 4608)])
 def test_linear_rows_parity(M, K, N):
     rng = np.random.default_rng(M + K + N)
     x, xb = _bf16_dev(rng.normal(size=(M, K)))
@@ -520,7 +520,7 @@ def test_linear_rows_batch_invariant():
                           full)
 
 
-@pytest.mark.parametrize("M,K,N", [(9, 64, 128), (264, 3584, 1024)])
+@pytest.mark.parametrize("M,K,N", [(9, 64, 64), (100, 448, 320), (264, 3584, 1024)])
 def test_linear_swiglu_rows(M, K, N):
     rng = np.random.default_rng(7 * M + K)
     x, xb = _bf16_dev(rng.normal(size=(M, K)))

@@ -32,9 +32,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kLinThreads = 256;
 constexpr int kLinRows = 64;    // rows per workgroup
-constexpr int kLinFeat = 128;   // output features per workgroup (32 per wave)
+constexpr int kLinFeat = 64;    // output features per workgroup (16 per wave)
 constexpr int kLinKC = 64;      // K per chunk (two MFMA k-steps)
-constexpr int kLinStages = 3;
 
 struct LinParams {
   const uint16_t* x;
@@ -57,9 +56,13 @@ __device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
 // operand read touches at one k-offset spread over the banks.
 __device__ __forceinline__ int x_slot(int row, int piece) { return row * 8 + (piece ^ (row & 7)); }
 
-template <bool SWIGLU>
+// NST register stages: chunk c + NST - 1 is requested while chunk c is
+// computed. Input rows go registers -> LDS one chunk ahead (two LDS stages
+// suffice: the barrier closing every chunk keeps all waves on the same chunk,
+// which reads stage c % 2 while stage (c + 1) % 2 is written).
+template <bool SWIGLU, int NST>
 __global__ __launch_bounds__(kLinThreads) void linear_rows_kernel(LinParams p) {
-  __shared__ __attribute__((aligned(16))) u16x8_t sX[kLinStages][kLinRows * 8];
+  __shared__ __attribute__((aligned(16))) u16x8_t sX[2][kLinRows * 8];
   // Work item -> (weight slice, row group): the workgroups sharing
   // blockIdx mod 8 (one XCD) take one contiguous run of work items, and the
   // row groups of a slice are consecutive work items.
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_rows_kernel(LinParams p) {
   const int wave = tid >> 6;
   const int i16 = lane & 15;
   const int kg = lane >> 4;
-  const int n0 = slice * kLinFeat + wave * 32;
+  const int n0 = slice * kLinFeat + wave * 16;
   const int m0 = mg * kLinRows;
   const int nchunks = p.K / kLinKC;
 
@@ -89,46 +92,37 @@ __global__ __launch_bounds__(kLinThreads) void linear_rows_kernel(LinParams p) {
     xs[j] = p.x + static_cast<int64_t>(min(m0 + row, p.M - 1)) * p.x_stride + 8 * piece;
     xslot[j] = x_slot(row, piece);
   }
-  // Weight rows of this lane: n-tile nt, k-step s of a chunk, 16 bytes.
-  const uint16_t* wg[2];
-  const uint16_t* wu[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    wg[nt] = p.w0 + static_cast<int64_t>(n0 + 16 * nt + i16) * p.w_stride + 8 * kg;
-    wu[nt] = SWIGLU ? p.w1 + static_cast<int64_t>(n0 + 16 * nt + i16) * p.w_stride + 8 * kg
-                    : nullptr;
-  }
+  // This lane's weight row (feature n0 + i16), 16 bytes per k-step.
+  const uint16_t* wg = p.w0 + static_cast<int64_t>(n0 + i16) * p.w_stride + 8 * kg;
+  const uint16_t* wu =
+      SWIGLU ? p.w1 + static_cast<int64_t>(n0 + i16) * p.w_stride + 8 * kg : nullptr;
 
   struct Stage {
     u16x8_t x[2];
-    bf16x8_t g[2][2];  // [nt][k-step]
-    bf16x8_t u[2][2];
+    bf16x8_t g[2];  // [k-step]
+    bf16x8_t u[2];
   };
   auto load_chunk = [&](Stage& st, int c) __attribute__((always_inline)) {
     const int k0 = c * kLinKC;
 #pragma unroll
     for (int j = 0; j < 2; ++j) st.x[j] = *reinterpret_cast<const u16x8_t*>(xs[j] + k0);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        st.g[nt][s] = load8(wg[nt] + k0 + 32 * s);
-        if constexpr (SWIGLU) st.u[nt][s] = load8(wu[nt] + k0 + 32 * s);
-      }
+    for (int s = 0; s < 2; ++s) {
+      st.g[s] = load8(wg + k0 + 32 * s);
+      if constexpr (SWIGLU) st.u[s] = load8(wu + k0 + 32 * s);
+    }
   };
   auto store_x = [&](const Stage& st, int stage) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) sX[stage][xslot[j]] = st.x[j];
   };
 
-  f32x4_t a0[2][4], a1[2][4];
+  f32x4_t a0[4], a1[4];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      a0[nt][mt] = f32x4_t(0.f);
-      a1[nt][mt] = f32x4_t(0.f);
-    }
+  for (int mt = 0; mt < 4; ++mt) {
+    a0[mt] = f32x4_t(0.f);
+    a1[mt] = f32x4_t(0.f);
+  }
   auto compute = [&](const Stage& st, int stage) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -137,70 +131,62 @@ __global__ __launch_bounds__(kLinThreads) void linear_rows_kernel(LinParams p) {
       for (int mt = 0; mt < 4; ++mt)
         xf[mt] = __builtin_bit_cast(bf16x8_t, sX[stage][x_slot(16 * mt + i16, 4 * s + kg)]);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          a0[nt][mt] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.g[nt][s], xf[mt], a0[nt][mt], 0, 0, 0);
-          if constexpr (SWIGLU)
-            a1[nt][mt] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.u[nt][s], xf[mt], a1[nt][mt], 0, 0, 0);
-        }
+      for (int mt = 0; mt < 4; ++mt) {
+        a0[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.g[s], xf[mt], a0[mt], 0, 0, 0);
+        if constexpr (SWIGLU)
+          a1[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.u[s], xf[mt], a1[mt], 0, 0, 0);
+      }
     }
   };
 
-  // Chunk c lives in register stage c % 3 and LDS stage c % 3. Iteration c:
-  // request chunk c + 2, put chunk c + 1's input rows into LDS, barrier,
-  // compute chunk c. A barrier per chunk keeps the waves within one chunk of
-  // each other, so the stage being written, (c + 1) % 3, is never the one a
-  // slower wave still reads, c % 3 or (c - 1) % 3... (c - 1) % 3 is done
-  // before that wave reached this chunk's barrier.
-  Stage r0, r1, r2;
-  load_chunk(r0, 0);
-  if (nchunks > 1) load_chunk(r1, 1);
-  store_x(r0, 0);
+  // Chunk c lives in register stage c % NST and LDS stage c % 2.
+  Stage r[NST];
+#pragma unroll
+  for (int j = 0; j < NST - 1; ++j)
+    if (j < nchunks) load_chunk(r[j], j);
+  store_x(r[0], 0);
   __syncthreads();
-  auto iter = [&](Stage& cur, Stage& nxt, Stage& far, int c, int scur, int snxt)
-                  __attribute__((always_inline)) {
-    if (c + 2 < nchunks) load_chunk(far, c + 2);
-    if (c + 1 < nchunks) store_x(nxt, snxt);
-    compute(cur, scur);
-    __syncthreads();
-  };
   int c = 0;
-  for (; c + 3 <= nchunks; c += 3) {
-    iter(r0, r1, r2, c, 0, 1);
-    iter(r1, r2, r0, c + 1, 1, 2);
-    iter(r2, r0, r1, c + 2, 2, 0);
+  for (; c + NST <= nchunks; c += NST) {
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      if (c + j + NST - 1 < nchunks) load_chunk(r[(j + NST - 1) % NST], c + j + NST - 1);
+      if (c + j + 1 < nchunks) store_x(r[(j + 1) % NST], (j + 1) & 1 ^ (c & 1));
+      compute(r[j], (j & 1) ^ (c & 1));
+      __syncthreads();
+    }
   }
-  if (c < nchunks) iter(r0, r1, r2, c, 0, 1);
-  if (c + 1 < nchunks) iter(r1, r2, r0, c + 1, 1, 2);
+#pragma unroll
+  for (int j = 0; j < NST - 1; ++j) {
+    if (c + j < nchunks) {
+      if (c + j + NST - 1 < nchunks) load_chunk(r[(j + NST - 1) % NST], c + j + NST - 1);
+      if (c + j + 1 < nchunks) store_x(r[(j + 1) % NST], (j + 1) & 1 ^ (c & 1));
+      compute(r[j], (j & 1) ^ (c & 1));
+      __syncthreads();
+    }
+  }
 
-  // Lane holds output features n0 + 16 nt + 4 kg + e (e = 0..3) of row
-  // m0 + 16 mt + i16.
+  // Lane holds output features n0 + 4 kg + e (e = 0..3) of row m0 + 16 mt + i16.
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int m = m0 + 16 * mt + i16;
     if (m >= p.M) continue;
+    uint32_t h[4];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      uint32_t h[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float v;
-        if constexpr (SWIGLU) {
-          // The two projections rounded as separate outputs, then SwiGLU.
-          const float gr = tv::bf16_to_f32(tv::f32_to_bf16_rne(a0[nt][mt][e]));
-          const float ur = tv::bf16_to_f32(tv::f32_to_bf16_rne(a1[nt][mt][e]));
-          v = silu(gr) * ur;
-        } else {
-          v = a0[nt][mt][e];
-        }
-        h[e] = tv::f32_to_bf16_rne(v);
+    for (int e = 0; e < 4; ++e) {
+      float v;
+      if constexpr (SWIGLU) {
+        // The two projections rounded as separate outputs, then SwiGLU.
+        const float gr = tv::bf16_to_f32(tv::f32_to_bf16_rne(a0[mt][e]));
+        const float ur = tv::bf16_to_f32(tv::f32_to_bf16_rne(a1[mt][e]));
+        v = silu(gr) * ur;
+      } else {
+        v = a0[mt][e];
       }
-      *reinterpret_cast<uint2*>(p.y + static_cast<int64_t>(m) * p.y_stride + n0 + 16 * nt +
-                                4 * kg) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      h[e] = tv::f32_to_bf16_rne(v);
     }
+    *reinterpret_cast<uint2*>(p.y + static_cast<int64_t>(m) * p.y_stride + n0 + 4 * kg) =
+        make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
   }
 }
 
@@ -233,9 +219,10 @@ int launch_linear(const void* x, int64_t x_stride, const void* w0, const void* w
   p.y = static_cast<uint16_t*>(y);
   const int grid = (p.work + 7) / 8 * 8;
   if (swiglu)
-    hipLaunchKernelGGL(linear_rows_kernel<true>, dim3(grid), dim3(kLinThreads), 0, stream, p);
+    hipLaunchKernelGGL((linear_rows_kernel<true, 5>), dim3(grid), dim3(kLinThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(linear_rows_kernel<false>, dim3(grid), dim3(kLinThreads), 0, stream, p);
+    hipLaunchKernelGGL((linear_rows_kernel<false, 6>), dim3(grid), dim3(kLinThreads), 0, stream,
+                       p);
   return tvh::launch_status();
 }
 
