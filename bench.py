@@ -286,24 +286,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # Timed region 2: each call of the step on its own, run back to back
-    # `reps` times between two HIP events recorded on the stream the kernels
-    # are launched on (torch's current stream, which the binding passes to
-    # the library); the average includes the launch gaps inside a call.
+    # Timed region 2: each call of the step on its own, `reps` calls back to
+    # back between two HIP events recorded on the stream the kernels are
+    # launched on (torch's current stream, which the binding passes to the
+    # library); the average includes the launch gaps inside a call.
     reps = max(20, args.steps)
-
-    def timed(fn):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
-        e0.record()
-        for i in range(reps):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / reps
+    timed = lambda fn: time_calls(torch, fn, reps)
 
     t_mask = timed(do_mask)
     t_attn = timed(do_attention)
@@ -391,25 +379,11 @@ def projections_secondary(tv, torch, dev, w, args):
     yq = torch.empty((M, n_qkv), dtype=torch.bfloat16, device=dev)
     yf = torch.empty((M, n_ffn), dtype=torch.bfloat16, device=dev)
     reps = max(20, args.steps)
-
-    def timed(fn):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / reps
-
-    t_qkv = timed(lambda: tv.linear_rows(x, wq, out=yq))
-    t_ffn = timed(lambda: tv.linear_swiglu_rows(x, wg, wu, out=yf))
-    t_qkv_ref = timed(lambda: torch.matmul(x, wq.t()))
-    t_ffn_ref = timed(lambda: torch.nn.functional.silu(torch.matmul(x, wg.t())) *
-                      torch.matmul(x, wu.t()))
+    t_qkv = time_calls(torch, lambda i: tv.linear_rows(x, wq, out=yq), reps)
+    t_ffn = time_calls(torch, lambda i: tv.linear_swiglu_rows(x, wg, wu, out=yf), reps)
+    t_qkv_ref = time_calls(torch, lambda i: torch.matmul(x, wq.t()), reps)
+    t_ffn_ref = time_calls(torch, lambda i: torch.nn.functional.silu(torch.matmul(x, wg.t())) *
+                           torch.matmul(x, wu.t()), reps)
     b_qkv = 2 * (n_qkv * K + M * K + M * n_qkv)
     b_ffn = 2 * (2 * n_ffn * K + M * K + M * n_ffn)
     return {"rows": M, "hidden": K,
@@ -419,6 +393,37 @@ def projections_secondary(tv, torch, dev, w, args):
             "gate_up_swiglu": {"N": n_ffn, "us": round(t_ffn * 1e6, 3), "alg_bytes": b_ffn,
                                "GBps": round(b_ffn / t_ffn / 1e9, 1),
                                "torch_matmul_silu_mul_us": round(t_ffn_ref * 1e6, 3)}}
+
+
+def time_calls(torch, fn, reps):
+    """Average GPU time of fn(i) over `reps` back-to-back calls. The calls are
+    captured once in a HIP graph and replayed between two events, so that
+    the host's launch path (~10 us per call through the binding) does not
+    pace kernels shorter than it; eager launches if capture fails."""
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    graph = torch.cuda.CUDAGraph()
+    try:
+        with torch.cuda.graph(graph):
+            for i in range(reps):
+                fn(i)
+        graph.replay()
+        torch.cuda.synchronize()
+    except RuntimeError:
+        graph = None
+        torch.cuda.synchronize()
+    e0.record()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(reps):
+            fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
 
 
 def commit_secondary(tv, torch, dev, w, s, acc_out, args):
@@ -434,22 +439,11 @@ def commit_secondary(tv, torch, dev, w, s, acc_out, args):
     new_ctx = torch.empty((w.B,), dtype=torch.int32, device=dev)
     st = torch.empty((w.B,), dtype=torch.int32, device=dev)
 
-    def call():
+    def call(i):
         tv.commit_accepted_kv(k, v, s["ctx"], s["n"], acc_len, path, new_ctx_len=new_ctx,
                               row_status=st)
 
-    for _ in range(3):
-        call()
-    torch.cuda.synchronize()
-    reps = max(20, args.steps)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / reps
+    t = time_calls(torch, call, max(20, args.steps))
     moved = int(acc_len.sum().item())
     by = moved * w.Hkv * w.D * 2 * 2 * 2 * layers  # K and V rows, read + write, bf16
     return {"workload": "C3 greedy acceptance, %d layers" % layers, "accepted_nodes": moved,
