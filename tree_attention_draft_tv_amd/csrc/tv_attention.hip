@@ -77,6 +77,7 @@ struct AttnParams {
   const int32_t* n_nodes;
   const uint32_t* mask;
   int B, T, Hq, Hkv, G, R, W, max_ctx, kv_capacity, parts;
+  uint32_t g_mul;  // ceil(2^16 / G): packed row r -> tree row (r * g_mul) >> 16
   int kunit;    // keys per unit if fixed by the caller, 0 = balanced on the device
   int rows_wg;  // packed rows per workgroup (one row group)
   int RG;       // row groups per (sequence, KV head)
@@ -99,6 +100,24 @@ __device__ __forceinline__ int seq_status(const AttnParams& p, int n, int L) {
   if (L < 0 || L > p.max_ctx || static_cast<int64_t>(L) + n > p.kv_capacity)
     return TV_ROW_CTX_BOUND;
   return TV_ROW_OK;
+}
+
+// a / b for 0 <= a, 1 <= b (exact). Below 2^22 the float quotient through
+// the hardware reciprocal is within 1 of the true one and one correction
+// step finishes it (a few instructions instead of a long integer division
+// sequence); larger dividends divide exactly.
+__device__ __forceinline__ int div_fast(int a, int b) {
+  if (a >= (1 << 22)) return a / b;
+  int q = static_cast<int>(static_cast<float>(a) * __builtin_amdgcn_rcpf(static_cast<float>(b)));
+  const int r = a - q * b;
+  q += static_cast<int>(r >= b) - static_cast<int>(r < 0);
+  return q;
+}
+
+// Packed row r -> tree row r / G with the host's multiplier ceil(2^16 / G):
+// exact for r < 2048 and G <= 32, which TV_MAX_TREE * TV_MAX_GROUP keeps.
+__device__ __forceinline__ int row_node(const AttnParams& p, int r) {
+  return static_cast<int>((static_cast<uint32_t>(r) * p.g_mul) >> 16);
 }
 
 // Status of sequence b (see seq_status); also returns its n and L.
@@ -203,7 +222,7 @@ constexpr int kTreeExtra = 128;
 // Units of a pair with L committed keys and K keys per unit.
 __device__ __forceinline__ int pair_units(const AttnParams& p, int L, int K) {
   const int x = p.kunit > 0 ? 0 : kTreeExtra;
-  return L == 0 ? 1 : (L + x + K - 1) / K;
+  return L == 0 ? 1 : div_fast(L + x + K - 1, K);
 }
 // First committed key of unit c of a pair: c K for fixed chunks; in balanced
 // mode the units split L + kTreeExtra evenly, boundaries rounded down to
@@ -211,6 +230,10 @@ __device__ __forceinline__ int pair_units(const AttnParams& p, int L, int K) {
 // one committed key and every unit at most K + 63 keys.
 __device__ __forceinline__ int unit_start(const AttnParams& p, int L, int K, int nch, int c) {
   if (p.kunit > 0) return min(c * K, L);
+  // c <= nch <= 1024 units per pair, so below 2^22 the product fits 32 bits.
+  if (L < (1 << 22) - kTreeExtra)
+    return static_cast<int>(static_cast<uint32_t>(c) * static_cast<uint32_t>(L + kTreeExtra) /
+                            static_cast<uint32_t>(nch)) & ~63;
   return static_cast<int>(static_cast<int64_t>(c) * (L + kTreeExtra) / nch) & ~63;
 }
 
@@ -269,7 +292,7 @@ __device__ int choose_unit(const AttnParams& p, int len0) {
       int64_t cnt = 0;
       for (int b = 0; b < p.B; ++b) {
         const int L = __builtin_amdgcn_readlane(len0, b);
-        if (L >= 0) cnt += L == 0 ? 1 : (L + kTreeExtra + kc - 1) / kc;
+        if (L >= 0) cnt += L == 0 ? 1 : div_fast(L + kTreeExtra + kc - 1, kc);
       }
       const uint64_t fits = __ballot(kc <= hi && cnt * per <= p.nw);
       if (fits) return lo + 64 * static_cast<int>(__builtin_ctzll(fits));
@@ -512,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     const int r = row0 + rt * 16 + l16;
-    const int i = r / p.G;
+    const int i = row_node(p, r);
     const int node = (r < p.R && i < n) ? i : -1;
     node_rt[rt] = node;
     const int h = kvh * p.G + (r - i * p.G);
@@ -847,7 +870,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
     const int r = row0 + rt * 16 + l16;
     if (r >= p.R) continue;
     if (direct) {
-      const int i = r / p.G;
+      const int i = row_node(p, r);
       const int h = kvh * p.G + (r - i * p.G);
       const int64_t orow = (static_cast<int64_t>(b) * p.T + i) * p.Hq + h;
       float* dst = p.out + orow * D;
@@ -938,7 +961,7 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
   int node = -1;
   int h = 0;
   if (r < p.R) {
-    const int i = r / p.G;
+    const int i = row_node(p, r);
     h = kvh * p.G + (r - i * p.G);
     if (i < n) node = i;
   }
@@ -997,7 +1020,7 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
   }
 
   if (r >= p.R) return;
-  const int i = r / p.G;
+  const int i = row_node(p, r);
   if (nch == 1) {
     const int64_t orow = (static_cast<int64_t>(b) * p.T + i) * p.Hq + h;
     const bool live = node >= 0;
@@ -1059,7 +1082,7 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   if (seq_status(p, n, L) != TV_ROW_OK) return;  // padded / invalid: done by the split
   const int nch = pair_units(p, L, K);
   if (nch == 1) return;                           // written directly by the split
-  const int i = r / p.G;
+  const int i = row_node(p, r);
   const int h = kvh * p.G + (r - i * p.G);
   const int64_t orow = (static_cast<int64_t>(b) * p.T + i) * p.Hq + h;
   float4* dst = reinterpret_cast<float4*>(p.out + orow * D) + sub;
@@ -1289,6 +1312,7 @@ extern "C" int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int6
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.G = Hq / Hkv;
+  p.g_mul = (65536u + static_cast<uint32_t>(p.G) - 1u) / static_cast<uint32_t>(p.G);
   p.R = p.G * T;
   p.W = (T + 31) / 32;
   p.max_ctx = max_ctx;
