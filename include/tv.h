@@ -64,7 +64,8 @@ typedef enum tv_row_status {
   TV_ROW_CTX_BOUND = 2,  /* ctx_len < 0, ctx_len > max_ctx or ctx_len + n > kv_capacity */
   TV_ROW_NNODES = 3,     /* n_nodes outside [0, T] */
   TV_ROW_BAD_TOKEN = 4,  /* some live draft token outside [0, V) */
-  TV_ROW_BAD_PATH = 5    /* accepted path not 0 < path[1] < ... < path[a] < n, or a outside [0, n) */
+  TV_ROW_BAD_PATH = 5,   /* accepted path not 0 < path[1] < ... < path[a] < n, or a outside [0, n) */
+  TV_ROW_BAD_START = 6   /* packed rows: row_start < 0 or row_start + n > rows_total */
 } tv_row_status;
 
 typedef enum tv_dtype { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
@@ -194,6 +195,39 @@ int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
                       int probability_parts, int chunk_keys, float* out, float* lse,
                       void* workspace, size_t ws_bytes, int32_t* row_status,
                       hipStream_t stream);
+
+/*
+ * tv_tree_attention_packed — tv_tree_attention over packed query rows: the
+ * live rows of the sequences sit back to back instead of each sequence being
+ * padded to T rows. (Page 1, commit "perf(activevln): pack batched prefill
+ * turns back to back in CUDA graphs": the split-KV attention takes a table
+ * of per-row starts and a query extent equal to the padded length, so its
+ * split partition and its results are those of the padded launch, bit for
+ * bit.)
+ *
+ * Node i < n_nodes[b] of sequence b is packed row row_start[b] + i:
+ *   q        [rows_total][Hq][D]; element (row,h,d) at q + row*q_st + h*q_sh + d
+ *   out      float32 [rows_total][Hq][D] contiguous; lse float32 [rows_total][Hq]
+ *   row_start int32 [B]; the ranges [row_start[b], row_start[b] + n_nodes[b])
+ *            must not overlap (not checked: overlapping rows race)
+ * T is the query extent (the largest n_nodes the call accepts, as in the
+ * padded call); mask, ctx_len, n_nodes, k, v, the workspace and every other
+ * argument are as in tv_tree_attention, and the workspace size is the same.
+ * For the same inputs each live row gets exactly the bits tv_tree_attention
+ * writes for it. Rows that belong to no live sequence are not written; a
+ * sequence with TV_ROW_CTX_BOUND gets out = 0, lse = -inf on its own rows.
+ * row_status adds TV_ROW_BAD_START (row_start[b] < 0 or row_start[b] + n >
+ * rows_total; nothing of that sequence is written). Errors as tv_tree_attention,
+ * plus TV_ERR_NULL for a NULL row_start and TV_ERR_SHAPE for rows_total < 0.
+ */
+int tv_tree_attention_packed(const void* q, int64_t q_st, int64_t q_sh, const void* k,
+                             const void* v, int64_t kv_sb, int64_t kv_sh, int64_t kv_ss,
+                             const int32_t* ctx_len, const int32_t* n_nodes,
+                             const uint32_t* mask, const int32_t* row_start, int rows_total,
+                             int B, int T, int Hq, int Hkv, int D, int max_ctx, int kv_capacity,
+                             float scale, int in_dtype, int probability_parts, int chunk_keys,
+                             float* out, float* lse, void* workspace, size_t ws_bytes,
+                             int32_t* row_status, hipStream_t stream);
 
 /*
  * Workspace (bytes) of tv_accept_greedy (mode 0) or tv_accept_sample
@@ -328,6 +362,38 @@ int tv_commit_accepted_kv(void* k, void* v, int64_t layer_stride, int64_t kv_sb,
                           const int32_t* accept_len, const int32_t* path, int B, int T, int Hkv,
                           int D, int elem_bytes, int layers, int kv_capacity,
                           int32_t* new_ctx_len, int32_t* row_status, hipStream_t stream);
+
+/*
+ * tv_adapt_tree_budget — adaptive draft budget and the next step's packed
+ * row table, on the device. (Page 3, the adaptive mode: the number of
+ * speculative tokens follows recent acceptance ratios toward a target ratio;
+ * page 1, commit "perf(activevln): pack batched prefill turns back to back
+ * in CUDA graphs": per-row starts of packed rows.)
+ *
+ * For each sequence b whose verified step had n = n_nodes[b] >= 2 rows,
+ * a = accept_len[b] in [0, n - 1] and (if row_status is not NULL)
+ * row_status[b] == TV_ROW_OK, in fp32 with every operation rounded to nearest
+ * and none fused:
+ *   ratio = a / (n - 1);  ratio_ema[b] = ratio_ema[b] + alpha * (ratio - ratio_ema[b]);
+ *   budget[b] += 1 if ratio_ema[b] > target, -= 1 if below, unchanged if equal;
+ * other sequences keep their ratio_ema. Every budget[b] is then clamped to
+ * [n_min, n_max], and row_start[b] = sum over c < b of (budget[c] + 1) (the
+ * draft nodes plus the root of the next step), rows_total[0] = that sum over
+ * all b. ratio_ema and budget are read and updated in place (the caller
+ * initialises them, e.g. to target and n_max).
+ *
+ *   accept_len, n_nodes int32 [B] (from the verification of the last step)
+ *   row_status int32 [B] or NULL
+ *   target   in [0, 1]; alpha in (0, 1]; 1 <= n_min <= n_max <= TV_MAX_TREE - 1
+ *   ratio_ema float32 [B]; budget, row_start int32 [B]; rows_total int32 [1]
+ * B >= 0 (B == 0 writes rows_total = 0; the [B] pointers may then be NULL).
+ * Errors: TV_ERR_NULL, TV_ERR_SHAPE.
+ * One workgroup; every write goes through device memory, nothing is read back.
+ */
+int tv_adapt_tree_budget(const int32_t* accept_len, const int32_t* n_nodes,
+                         const int32_t* row_status, int B, float target, float alpha, int n_min,
+                         int n_max, float* ratio_ema, int32_t* budget, int32_t* row_start,
+                         int32_t* rows_total, hipStream_t stream);
 
 /* Static, human-readable name of a tv_status or tv_row_status value. */
 const char* tv_status_string(int code);

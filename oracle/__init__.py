@@ -36,6 +36,12 @@ throughput" unless noted):
   projections of the verification rows with one output rounding, and the
   rounded SwiGLU of the gate and up projections (commit "perf(activevln):
   batch-invariant Triton GEMMs for decode projections").
+* ``attention.tree_attention_packed`` — the same attention over query rows
+  packed back to back, located by per-row starts (commit "perf(activevln):
+  pack batched prefill turns back to back in CUDA graphs").
+* ``budget.adapt_tree_budget`` — the adaptive draft budget (the IluvatarLabs/vllm
+  page "Introduce SCV vectorized masking with graph/adaptive modes", its
+  adaptive mode) and the packed row starts of the next step.
 * ``commit.commit_accepted_kv`` — the accepted path's keys and values become
   contiguous committed context (commit "perf(activevln): lossless batched
   replay throughput options", item incremental_kv_commit; the IluvatarLabs/vllm
@@ -48,7 +54,9 @@ closed forms, textbook special cases and brute force (tests/test_oracle_*.py).
 """
 
 from .accept import accept_greedy, accept_sample, sample_probs  # noqa: F401
-from .attention import masked_attention, tree_attention  # noqa: F401
+from .attention import ROW_BAD_START, masked_attention, tree_attention  # noqa: F401
+from .attention import tree_attention_packed  # noqa: F401
+from .budget import adapt_tree_budget  # noqa: F401
 from .block import BIDIRECTIONAL, CAUSAL, build_block_mask  # noqa: F401
 from .commit import ROW_BAD_PATH, commit_accepted_kv  # noqa: F401
 from .linear import linear_rows, round_bf16, silu, swiglu_rows  # noqa: F401

@@ -73,6 +73,64 @@ def masked_attention(q, k, v, dtype, ctx_len, n_nodes, mask, scale,
     return _attention(q, k, v, dtype, ctx_len, n_nodes, mask_keys, scale, max_ctx, kv_capacity)
 
 
+ROW_BAD_START = 6
+
+
+def tree_attention_packed(q, k, v, dtype, ctx_len, n_nodes, parent, row_start, T, scale,
+                          max_ctx=None, kv_capacity=None):
+    """Exact float64 tree attention over packed query rows (the packed mode of
+    the EmbodiInfer page's commit "perf(activevln): pack batched prefill
+    turns back to back in CUDA graphs": the rows of the batch sit back to
+    back, located by per-row starts, with a query extent equal to the padded
+    length T).
+
+    q: [rows, Hq, D] stored values; node i of sequence b is row
+    row_start[b] + i. parent: int [B, T] (the tree stays per sequence).
+    Statuses, in this order: n outside [0, T] -> ROW_NNODES; n == 0 ->
+    padded (OK, no rows); row_start < 0 or row_start + n > rows ->
+    ROW_BAD_START; the context bounds of :func:`tree_attention` ->
+    ROW_CTX_BOUND (its n rows get out = 0, lse = -inf). Live rows get the
+    definition's values. Rows that belong to no written sequence are NaN
+    here (the caller's memory, left as it is).
+
+    Returns (out float64 [rows, Hq, D], lse float64 [rows, Hq], status).
+    """
+    rows, Hq, D = q.shape
+    B = len(n_nodes)
+    out = np.full((rows, Hq, D), np.nan)
+    lse = np.full((rows, Hq), np.nan)
+    status = np.zeros(B, dtype=np.int32)
+    cap = k.shape[2] if kv_capacity is None else kv_capacity
+    mc = cap if max_ctx is None else max_ctx
+    for b in range(B):
+        n = int(n_nodes[b])
+        s0 = int(row_start[b])
+        if n < 0 or n > T:
+            status[b] = ROW_NNODES
+            continue
+        if n == 0:
+            continue
+        if s0 < 0 or s0 + n > rows:
+            status[b] = ROW_BAD_START
+            continue
+        L = int(ctx_len[b])
+        if L < 0 or L > mc or L + n > cap:
+            status[b] = ROW_CTX_BOUND
+            out[s0:s0 + n] = 0.0
+            lse[s0:s0 + n] = -np.inf
+            continue
+        # This sequence alone, in the one-sequence padded layout.
+        qb = np.zeros((1, T) + q.shape[1:], dtype=q.dtype)
+        qb[0, :n] = q[s0:s0 + n]
+        o1, l1, st1 = tree_attention(qb, k[b:b + 1], v[b:b + 1], dtype, ctx_len[b:b + 1],
+                                     n_nodes[b:b + 1], parent[b:b + 1], scale, max_ctx=mc,
+                                     kv_capacity=cap)
+        out[s0:s0 + n] = o1[0, :n]
+        lse[s0:s0 + n] = l1[0, :n]
+        status[b] = st1[0]
+    return out, lse, status
+
+
 def _attention(q, k, v, dtype, ctx_len, n_nodes, draft_keys, scale, max_ctx, kv_capacity):
     """The definition, with the draft-key visibility of sequence b given by
     draft_keys(b, n) -> bool [n, n]."""

@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.SIGNATURES) == names
@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.tv_version() == 100
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, 1, 2, 3, 4, 5):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, 1, 2, 3, 4, 5, 6):
         s = lib.tv_status_string(code).decode()
         assert s and s != "unknown status", code
     assert lib.tv_status_string(99).decode() == "unknown status"
@@ -99,6 +99,56 @@ def test_attention_validation(lib):
     assert _attn(lib, ws_bytes=16) == -5
     assert _attn(lib, ws=ctypes.c_void_p(0x100010)) == -5  # not 256-byte aligned
     assert _attn(lib, B=0) == 0
+
+
+def _attn_packed(lib, **kw):
+    a = dict(q=P, q_st=28 * 128, q_sh=128, k=P, v=P2, kv_sb=4 * 4096 * 128, kv_sh=4096 * 128,
+             kv_ss=128, ctx=P, n=P, mask=P, start=P, rows=100, B=2, T=33, Hq=28, Hkv=4, D=128,
+             max_ctx=4000, cap=4096, scale=0.088, dtype=1, parts=1, chunk=0, out=P, lse=P,
+             ws=P, ws_bytes=1 << 40, st=P)
+    a.update(kw)
+    return lib.tv_tree_attention_packed(
+        a["q"], a["q_st"], a["q_sh"], a["k"], a["v"], a["kv_sb"], a["kv_sh"], a["kv_ss"],
+        a["ctx"], a["n"], a["mask"], a["start"], a["rows"], a["B"], a["T"], a["Hq"], a["Hkv"],
+        a["D"], a["max_ctx"], a["cap"], a["scale"], a["dtype"], a["parts"], a["chunk"], a["out"],
+        a["lse"], a["ws"], a["ws_bytes"], a["st"], STREAM)
+
+
+def test_attention_packed_validation(lib):
+    assert _attn_packed(lib, start=NULL) == -1
+    assert _attn_packed(lib, q=NULL) == -1
+    assert _attn_packed(lib, rows=-1) == -2
+    assert _attn_packed(lib, T=129) == -2
+    assert _attn_packed(lib, dtype=7) == -3
+    assert _attn_packed(lib, q_st=28 * 128 + 4) == -4   # row stride not 16 bytes
+    assert _attn_packed(lib, D=80) == -6
+    assert _attn_packed(lib, ws=NULL, ws_bytes=0) == -5
+    assert _attn_packed(lib, B=0) == 0
+    assert _attn_packed(lib, B=0, rows=0) == 0
+
+
+def _budget(lib, **kw):
+    a = dict(acc=P, n=P, st=NULL, B=4, target=0.5, alpha=0.25, n_min=1, n_max=64, ema=P,
+             budget=P, start=P, total=P)
+    a.update(kw)
+    return lib.tv_adapt_tree_budget(a["acc"], a["n"], a["st"], a["B"], a["target"], a["alpha"],
+                                    a["n_min"], a["n_max"], a["ema"], a["budget"], a["start"],
+                                    a["total"], STREAM)
+
+
+def test_budget_validation(lib):
+    assert _budget(lib, acc=NULL) == -1
+    assert _budget(lib, ema=NULL) == -1
+    assert _budget(lib, total=NULL) == -1
+    assert _budget(lib, B=0, total=NULL) == -1
+    assert _budget(lib, B=-1) == -2
+    assert _budget(lib, target=1.5) == -2 and _budget(lib, target=-0.1) == -2
+    assert _budget(lib, target=float("nan")) == -2
+    assert _budget(lib, alpha=0.0) == -2 and _budget(lib, alpha=1.01) == -2
+    assert _budget(lib, n_min=0) == -2
+    assert _budget(lib, n_min=5, n_max=4) == -2
+    assert _budget(lib, n_max=128) == -2                 # at most TV_MAX_TREE - 1 draft nodes
+    assert _budget(lib, B=1 << 24) == -2                 # row table would overflow int32
 
 
 def test_attention_workspace_size(lib):

@@ -644,6 +644,164 @@ def test_commit_status_and_untouched_sequences():
     assert list(st) == [0, oracle.ROW_BAD_PATH, oracle.ROW_BAD_PATH, oracle.ROW_BAD_PATH, 0]
 
 
+# --------------------------------------------------------- packed rows ---
+
+def _packed_layout(w, seed, gap=3):
+    """Row starts for the live rows of w in a shuffled sequence order with a
+    few spare rows between sequences, and q packed accordingly."""
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(w.B)
+    start = np.zeros(w.B, np.int32)
+    pos = 1
+    for b in order:
+        start[b] = pos
+        pos += int(w.n_nodes[b]) + int(rng.integers(0, gap + 1))
+    rows = pos + 2
+    qp = np.zeros((rows,) + w.q.shape[2:], w.q.dtype)
+    for b in range(w.B):
+        n = int(w.n_nodes[b])
+        qp[start[b]:start[b] + n] = w.q[b, :n]
+    return qp, start, rows
+
+
+def _run_packed(w, d, mask, qp, start, chunk=0, parts=1, sentinel=12345.0):
+    qd = torch.from_numpy(qp.view(np.int16)).view(torch.bfloat16).cuda() if w.dtype == "bf16" \
+        else torch.from_numpy(qp).cuda()
+    rows = qp.shape[0]
+    out = torch.full((rows, w.Hq, w.D), sentinel, dtype=torch.float32, device="cuda")
+    lse = torch.full((rows, w.Hq), sentinel, dtype=torch.float32, device="cuda")
+    st_d = torch.from_numpy(start).cuda()
+    o, l, st = tv.tree_attention_packed(qd, d["k"], d["v"], d["ctx_len"], d["n_nodes"], mask,
+                                        st_d, w.max_ctx, scale=float(w.scale),
+                                        probability_parts=parts, chunk_keys=chunk, out=out,
+                                        lse=lse)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), l.cpu().numpy(), st.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,chunk,parts", [("C3", 0, 1), ("C3", 512, 1), ("C2", 0, 3),
+                                              ("C1", 0, 1)])
+def test_attention_packed_bitwise_equals_padded(name, chunk, parts):
+    # The packed launch keeps the padded launch's split partition, so every
+    # live row carries exactly the padded call's bits; spare rows between the
+    # sequences keep what they held.
+    w = make_config(name)
+    d = upload(w)
+    mask = _mask_check(w, d)
+    o_pad, l_pad, st_pad = run_attention(w, d, mask, chunk_keys=chunk, parts=parts)
+    qp, start, rows = _packed_layout(w, 5)
+    o, l, st = _run_packed(w, d, mask, qp, start, chunk=chunk, parts=parts)
+    assert np.array_equal(st, st_pad)
+    owned = np.zeros(rows, bool)
+    for b in range(w.B):
+        n = int(w.n_nodes[b])
+        s0 = int(start[b])
+        owned[s0:s0 + n] = True
+        assert np.array_equal(o[s0:s0 + n].view(np.uint32), o_pad[b, :n].view(np.uint32)), b
+        assert np.array_equal(l[s0:s0 + n].view(np.uint32), l_pad[b, :n].view(np.uint32)), b
+    assert np.all(o[~owned] == 12345.0) and np.all(l[~owned] == 12345.0)
+    # And against the oracle over packed rows.
+    o_ref, l_ref, st_ref = oracle.tree_attention_packed(
+        qp, w.k, w.v, w.dtype, w.ctx_len, w.n_nodes, w.parent, start, w.T, w.scale,
+        max_ctx=w.max_ctx, kv_capacity=w.kv_capacity)
+    assert np.array_equal(st, st_ref)
+    live = ~np.isnan(l_ref)
+    assert np.array_equal(live, owned[:, None] & np.ones((1, w.Hq), bool))
+    assert np.abs(o[live] - o_ref[live]).max() <= 2e-3
+    assert np.abs(l[live] - l_ref[live]).max() <= 1e-4
+
+
+@pytest.mark.parametrize("dtype,D,chunk", [("f32", 64, 128), ("bf16", 64, 0), ("bf16", 128, 64)])
+def test_attention_packed_ragged_and_statuses(dtype, D, chunk):
+    # Ragged trees and contexts, G = 3; one sequence over its context bound
+    # (its own rows get 0 / -inf), one with a start past the rows (nothing
+    # written), one padded (nothing written).
+    w = make_custom(77 + D, 6, 9, 3, D, 50, dtype, [300, 0, 77, 1000, 129, 64], 20,
+                    n_nodes=[21, 21, 13, 0, 1, 9], trie_tokens=False)
+    d = upload(w)
+    mask = _mask_check(w, d)
+    qp, start, rows = _packed_layout(w, 9)
+    ctx = w.ctx_len.copy()
+    ctx[4] = w.max_ctx + 1                      # context bound
+    start[5] = rows - 3                         # 9 rows do not fit
+    d["ctx_len"] = torch.from_numpy(ctx.astype(np.int32)).cuda()
+    o, l, st = _run_packed(w, d, mask, qp, start, chunk=chunk)
+    o_ref, l_ref, st_ref = oracle.tree_attention_packed(
+        qp, w.k, w.v, w.dtype, ctx, w.n_nodes, w.parent, start, w.T, w.scale,
+        max_ctx=w.max_ctx, kv_capacity=w.kv_capacity)
+    assert st.tolist() == st_ref.tolist()
+    assert st_ref[4] == oracle.ROW_CTX_BOUND and st_ref[5] == oracle.ROW_BAD_START
+    untouched = np.isnan(l_ref)
+    assert np.all(l[untouched] == 12345.0) and np.all(o[untouched] == 12345.0)
+    live = ~untouched
+    assert not np.isnan(o[live]).any()
+    tol = bf16_p_bound(w) if dtype == "bf16" else 2e-3
+    assert np.abs(o[live] - o_ref[live]).max() <= tol
+    dead = live & (l_ref == -np.inf)            # the context-bound sequence's rows
+    assert dead.sum() == int(w.n_nodes[4]) * w.Hq and np.all(l[dead] == -np.inf)
+    fin = live & ~dead
+    assert np.abs(l[fin] - l_ref[fin]).max() <= 1e-4
+
+
+# ------------------------------------------------------- adaptive budget ---
+
+def _budget_gpu(acc, n, ema, bud, target, alpha, n_min, n_max, status=None):
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dt)).cuda()
+    ema_d = t(ema, np.float32)
+    bud_d = t(bud, np.int32)
+    st_d = None if status is None else t(status, np.int32)
+    start, total = tv.adapt_tree_budget(t(acc, np.int32), t(n, np.int32), ema_d, bud_d, target,
+                                        alpha, n_min, n_max, row_status=st_d)
+    torch.cuda.synchronize()
+    return (ema_d.cpu().numpy(), bud_d.cpu().numpy(), start.cpu().numpy(),
+            int(total.cpu().numpy()[0]))
+
+
+def test_budget_golden_trajectory(golden_dir):
+    import json
+    import os
+    with open(os.path.join(golden_dir, "budget_hand.json")) as f:
+        g = json.load(f)
+    ema = np.array(g["ema0"], np.float32)
+    bud = np.array(g["budget0"], np.int32)
+    for step in g["steps"]:
+        ema, bud, start, total = _budget_gpu(step["accept_len"], step["n_nodes"], ema, bud,
+                                             g["target"], g["alpha"], g["n_min"], g["n_max"],
+                                             step["row_status"])
+        assert ema.tolist() == step["ema"] and bud.tolist() == step["budget"], step["why"]
+        assert start.tolist() == step["row_start"] and total == step["rows_total"]
+
+
+@pytest.mark.parametrize("B", [1, 64, 1000, 3000])
+def test_budget_matches_oracle_bitwise(B):
+    # Random acceptance over 25 steps (invalid lengths, bad statuses, padded
+    # and root-only steps included); float32 state and budgets bit for bit.
+    rng = np.random.default_rng(B)
+    target, alpha, n_min, n_max = 0.37, 0.2, 2, 100
+    ema_g = ema_o = rng.random(B).astype(np.float32)
+    bud_g = bud_o = rng.integers(n_min, n_max + 1, B).astype(np.int32)
+    for step in range(25):
+        n = np.minimum(bud_o + 1, 128).astype(np.int32)
+        n[rng.random(B) < 0.05] = 0
+        n[rng.random(B) < 0.05] = 1
+        acc = (rng.random(B) * n).astype(np.int32)
+        acc[rng.random(B) < 0.02] = 200
+        status = (rng.random(B) < 0.03).astype(np.int32) * 2
+        ema_g, bud_g, start_g, tot_g = _budget_gpu(acc, n, ema_g, bud_g, target, alpha, n_min,
+                                                   n_max, status)
+        ema_o, bud_o, start_o, tot_o = oracle.adapt_tree_budget(acc, n, ema_o, bud_o, target,
+                                                                alpha, n_min, n_max, status)
+        assert np.array_equal(ema_g.view(np.uint32), ema_o.view(np.uint32)), step
+        assert np.array_equal(bud_g, bud_o) and np.array_equal(start_g, start_o), step
+        assert tot_g == tot_o
+
+
+def test_budget_empty_batch():
+    ema, bud, start, total = _budget_gpu(np.zeros(0), np.zeros(0), np.zeros(0), np.zeros(0),
+                                         0.5, 0.5, 1, 8)
+    assert total == 0 and start.size == 0
+
+
 def test_graph_capture_replays_match_eager():
     w = make_config("C2")
     d = upload(w)
@@ -673,3 +831,71 @@ def test_graph_capture_replays_match_eager():
         got = [out.cpu(), lse.cpu()] + [a.cpu() for a in acc]
         for a, b in zip(got, ref):
             assert torch.equal(a, b), rep
+
+
+def test_graph_capture_whole_step_with_next_rows():
+    # One captured step over every other entry point: block masks, packed
+    # attention, greedy acceptance, KV commit, the budget controller and a
+    # projection. The commit and the controller update state in place, so the
+    # state is restored (outside the graph) before each replay; every replay
+    # must reproduce the eager results bit for bit.
+    w = make_config("C2")
+    d = upload(w)
+    qp, start, rows = _packed_layout(w, 11)
+    qd = torch.from_numpy(qp.view(np.int16)).view(torch.bfloat16).cuda()
+    start_d = torch.from_numpy(start).cuda()
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(w.B * w.T, 256, generator=g).to(torch.bfloat16).cuda()
+    wt = torch.randn(128, 256, generator=g).to(torch.bfloat16).cuda()
+    k0, v0 = d["k"].clone(), d["v"].clone()
+    ema0 = torch.full((w.B,), 0.5, dtype=torch.float32, device="cuda")
+    bud0 = torch.full((w.B,), w.T - 1, dtype=torch.int32, device="cuda")
+    k, v, ema, bud = k0.clone(), v0.clone(), ema0.clone(), bud0.clone()
+
+    def step():
+        bm, pos, _ = tv.build_block_mask(d["n_nodes"], w.T, tv.TV_BLOCK_CAUSAL)
+        mask, _, _ = tv.build_tree_mask(d["parent"], d["n_nodes"])
+        o, l, _ = tv.tree_attention_packed(qd, k, v, d["ctx_len"], d["n_nodes"], mask, start_d,
+                                           w.max_ctx, scale=float(w.scale))
+        acc = tv.accept_greedy(d["logits"], d["tokens"], d["parent"], d["n_nodes"])
+        new_ctx, _ = tv.commit_accepted_kv(k, v, d["ctx_len"], d["n_nodes"], acc[0], acc[1])
+        rs, rt = tv.adapt_tree_budget(acc[0], d["n_nodes"], ema, bud, 0.6, 0.25, 2, 64)
+        y = tv.linear_rows(x, wt)
+        return [bm, pos, o, l] + list(acc) + [new_ctx, rs, rt, y]
+
+    owned = torch.zeros(rows, dtype=torch.bool)
+    for b in range(w.B):
+        owned[int(start[b]):int(start[b]) + int(w.n_nodes[b])] = True
+    eager = step()
+    torch.cuda.synchronize()
+    ref = [t.cpu() for t in eager] + [k.cpu(), v.cpu(), ema.cpu(), bud.cpu()]
+
+    k.copy_(k0); v.copy_(v0); ema.copy_(ema0); bud.copy_(bud0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph):
+            outs = step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        k.copy_(k0); v.copy_(v0); ema.copy_(ema0); bud.copy_(bud0)
+        for t in outs:
+            t.fill_(3)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.cpu() for t in outs] + [k.cpu(), v.cpu(), ema.cpu(), bud.cpu()]
+        for i, (a, b) in enumerate(zip(got, ref)):
+            if i in (2, 3):  # packed out / lse: only the sequences' own rows are written
+                a, b = a[owned], b[owned]
+            assert torch.equal(_raw_bits(a), _raw_bits(b)), (rep, i)
+
+
+def _raw_bits(t):
+    # Raw bits of a host tensor, so that NaN (dead cache slots) equals itself.
+    if t.is_floating_point():
+        return t.view({2: torch.int16, 4: torch.int32}[t.element_size()])
+    return t

@@ -2,10 +2,12 @@
 
 Verifies a speculative draft token tree in one forward pass: ancestor masks
 (:func:`build_tree_mask`; :func:`build_block_mask` for draft blocks), tree-masked split-KV grouped-query attention
-(:func:`tree_attention`), exact acceptance (:func:`accept_greedy`,
-:func:`accept_sample`) and the commit of the accepted path's keys and values
-(:func:`commit_accepted_kv`), plus the batch-invariant few-row projections
-of the verification rows (:func:`linear_rows`, :func:`linear_swiglu_rows`).
+(:func:`tree_attention`; :func:`tree_attention_packed` over packed rows),
+exact acceptance (:func:`accept_greedy`, :func:`accept_sample`), the commit of
+the accepted path's keys and values (:func:`commit_accepted_kv`) and the
+device-side adaptive draft budget (:func:`adapt_tree_budget`), plus the
+batch-invariant few-row projections of the verification rows
+(:func:`linear_rows`, :func:`linear_swiglu_rows`).
 The compute runs in the HIP kernels of the in-tree
 ``libtv.so`` (C ABI in ``include/tv.h``); this package only marshals
 arguments.
@@ -23,6 +25,7 @@ from .binding import (  # noqa: F401
     accept_greedy,
     accept_sample,
     accept_workspace_size,
+    adapt_tree_budget,
     attention_workspace_size,
     auto_chunk,
     build_block_mask,
@@ -32,4 +35,5 @@ from .binding import (  # noqa: F401
     linear_swiglu_rows,
     load,
     tree_attention,
+    tree_attention_packed,
 )

@@ -30,7 +30,8 @@ STATUS = {
     -4: "TV_ERR_ALIGN", -5: "TV_ERR_WORKSPACE", -6: "TV_ERR_UNSUPPORTED", -7: "TV_ERR_HIP",
 }
 ROW_STATUS = {0: "TV_ROW_OK", 1: "TV_ROW_BAD_PARENT", 2: "TV_ROW_CTX_BOUND",
-              3: "TV_ROW_NNODES", 4: "TV_ROW_BAD_TOKEN", 5: "TV_ROW_BAD_PATH"}
+              3: "TV_ROW_NNODES", 4: "TV_ROW_BAD_TOKEN", 5: "TV_ROW_BAD_PATH",
+              6: "TV_ROW_BAD_START"}
 
 # Every exported symbol of include/tv.h with its (restype, argtypes).
 _P = ctypes.c_void_p
@@ -46,6 +47,10 @@ SIGNATURES = {
     "tv_tree_attention": (_I, [_P, _L, _L, _L, _P, _P, _L, _L, _L, _P, _P, _P,
                                _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
                                _P, _P, _P, _S, _P, _P]),
+    "tv_tree_attention_packed": (_I, [_P, _L, _L, _P, _P, _L, _L, _L, _P, _P, _P, _P, _I,
+                                      _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
+                                      _P, _P, _P, _S, _P, _P]),
+    "tv_adapt_tree_budget": (_I, [_P, _P, _P, _I, _F, _F, _I, _I, _P, _P, _P, _P, _P]),
     "tv_accept_workspace_size": (_S, [_I, _I, _I, _I]),
     "tv_accept_greedy": (_I, [_P, _L, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _S, _P, _P]),
     "tv_accept_sample": (_I, [_P, _L, _F, _P, _L, _P, _P, _P, _P, _I, _I, _I,
@@ -237,6 +242,110 @@ def tree_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ctx_len: t
         int(chunk_keys), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _ptr(row_status),
         _stream(dev)), "tv_tree_attention")
     return out, lse, row_status
+
+
+def tree_attention_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          ctx_len: torch.Tensor, n_nodes: torch.Tensor, mask: torch.Tensor,
+                          row_start: torch.Tensor, max_ctx: int, scale: Optional[float] = None,
+                          probability_parts: int = 1, chunk_keys: int = 0,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          row_status: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None):
+    """:func:`tree_attention` over packed query rows: node i of sequence b is
+    row row_start[b] + i of q [rows, Hq, D], out [rows, Hq, D] and lse
+    [rows, Hq]; the query extent T (largest n_nodes accepted) is the mask's
+    second dimension (mask: [B, T, ceil(T/32)], as for the padded call).
+    Rows of no live sequence are left as they are (``out``/``lse`` given) or
+    uninitialised. Returns (out, lse, row_status)."""
+    lib = load()
+    dev = q.device
+    if q.dtype == torch.bfloat16:
+        dt = TV_BF16
+    elif q.dtype == torch.float32:
+        dt = TV_F32
+    else:
+        raise TypeError("q must be float32 or bfloat16")
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    _need(ctx_len, "ctx_len", torch.int32, dev)
+    _need(n_nodes, "n_nodes", torch.int32, dev)
+    _need(mask, "mask", torch.int32, dev)
+    _need(row_start, "row_start", torch.int32, dev)
+    if q.dim() != 3 or k.dim() != 4 or v.shape != k.shape:
+        raise TVError("q must be [rows, Hq, D] and k, v [B, Hkv, capacity, D]")
+    rows, Hq, D = q.shape
+    B, Hkv, cap, Dk = k.shape
+    if Dk != D:
+        raise TVError("q and k disagree on D")
+    if q.stride(2) != 1 or k.stride(3) != 1 or v.stride(3) != 1:
+        raise TVError("the head dimension must be contiguous")
+    if k.stride() != v.stride():
+        raise TVError("k and v must share strides")
+    if mask.dim() != 3 or mask.shape[0] != B or not mask.is_contiguous():
+        raise TVError("mask must be a contiguous [B, T, ceil(T/32)] tensor")
+    T = mask.shape[1]
+    if mask.shape[2] != (T + 31) // 32:
+        raise TVError("mask must be a contiguous [B, T, ceil(T/32)] tensor")
+    if tuple(row_start.shape) != (B,) or tuple(ctx_len.shape) != (B,) or \
+            tuple(n_nodes.shape) != (B,):
+        raise TVError("ctx_len, n_nodes and row_start must be [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((rows, Hq, D), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((rows, Hq), dtype=torch.float32, device=dev)
+    if row_status is None:
+        row_status = torch.empty((B,), dtype=torch.int32, device=dev)
+    if not out.is_contiguous() or not lse.is_contiguous() or \
+            tuple(out.shape) != (rows, Hq, D) or tuple(lse.shape) != (rows, Hq):
+        raise TVError("out and lse must be contiguous [rows, Hq, D] and [rows, Hq]")
+    nbytes = attention_workspace_size(B, T, Hq, Hkv, D, max_ctx, chunk_keys)
+    ws, ws_bytes = _workspace(nbytes, dev, workspace)
+    _check(lib.tv_tree_attention_packed(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0), k.stride(1),
+        k.stride(2), _ptr(ctx_len), _ptr(n_nodes), _ptr(mask), _ptr(row_start), rows,
+        B, T, Hq, Hkv, D, int(max_ctx), cap, float(scale), dt, int(probability_parts),
+        int(chunk_keys), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _ptr(row_status),
+        _stream(dev)), "tv_tree_attention_packed")
+    return out, lse, row_status
+
+
+def adapt_tree_budget(accept_len: torch.Tensor, n_nodes: torch.Tensor,
+                      ratio_ema: torch.Tensor, budget: torch.Tensor, target: float,
+                      alpha: float, n_min: int, n_max: int,
+                      row_status: Optional[torch.Tensor] = None,
+                      row_start: Optional[torch.Tensor] = None,
+                      rows_total: Optional[torch.Tensor] = None):
+    """Device-side adaptive draft budget: updates ``ratio_ema`` (float32 [B])
+    and ``budget`` (int32 [B]) in place from the last step's acceptance and
+    returns (row_start int32 [B], rows_total int32 [1]), the packed row table
+    of the next step (budget + 1 rows per sequence)."""
+    lib = load()
+    dev = accept_len.device
+    _need(accept_len, "accept_len", torch.int32)
+    _need(n_nodes, "n_nodes", torch.int32, dev)
+    _need(ratio_ema, "ratio_ema", torch.float32, dev)
+    _need(budget, "budget", torch.int32, dev)
+    B = accept_len.shape[0]
+    for t, name in ((accept_len, "accept_len"), (n_nodes, "n_nodes"), (ratio_ema, "ratio_ema"),
+                    (budget, "budget")):
+        if tuple(t.shape) != (B,) or not t.is_contiguous():
+            raise TVError(name + " must be a contiguous [B] tensor")
+    if row_status is not None:
+        _need(row_status, "row_status", torch.int32, dev)
+        if tuple(row_status.shape) != (B,):
+            raise TVError("row_status must be [B]")
+    if row_start is None:
+        row_start = torch.empty((B,), dtype=torch.int32, device=dev)
+    if rows_total is None:
+        rows_total = torch.empty((1,), dtype=torch.int32, device=dev)
+    _check(lib.tv_adapt_tree_budget(
+        _ptr(accept_len), _ptr(n_nodes), _ptr(row_status), B, float(target), float(alpha),
+        int(n_min), int(n_max), _ptr(ratio_ema), _ptr(budget), _ptr(row_start),
+        _ptr(rows_total), _stream(dev)), "tv_adapt_tree_budget")
+    return row_start, rows_total
 
 
 # ----------------------------------------------------------- acceptance ---

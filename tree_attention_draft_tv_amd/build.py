@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libtv.so")
 
 SOURCES = ("tv_api.hip", "tv_mask.hip", "tv_attention.hip", "tv_accept.hip", "tv_commit.hip",
-           "tv_linear.hip")
+           "tv_linear.hip", "tv_budget.hip")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are kept out of the device code on purpose.

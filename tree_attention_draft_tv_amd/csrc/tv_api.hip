@@ -16,6 +16,7 @@ extern "C" const char* tv_status_string(int code) {
     case TV_ROW_NNODES: return "row: n_nodes outside [0, T]";
     case TV_ROW_BAD_TOKEN: return "row: a draft token is outside the vocabulary";
     case TV_ROW_BAD_PATH: return "row: the accepted path is not an increasing walk from the root";
+    case TV_ROW_BAD_START: return "row: packed rows outside [0, rows_total)";
     default: return "unknown status";
   }
 }

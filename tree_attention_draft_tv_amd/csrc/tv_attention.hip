@@ -76,6 +76,8 @@ struct AttnParams {
   const int32_t* ctx_len;
   const int32_t* n_nodes;
   const uint32_t* mask;
+  const int32_t* row_start;  // packed rows: first row of sequence b (null: row b T + i)
+  int rows_total;            // packed rows: rows of q / out / lse
   int B, T, Hq, Hkv, G, R, W, max_ctx, kv_capacity, parts;
   uint32_t g_mul;  // ceil(2^16 / G): packed row r -> tree row (r * g_mul) >> 16
   int kunit;    // keys per unit if fixed by the caller, 0 = balanced on the device
@@ -92,14 +94,20 @@ struct AttnParams {
   int32_t* row_status;
 };
 
-// Status of a sequence with n live rows and L committed keys: TV_ROW_OK
-// (live), -1 (padded: n == 0) or an error.
-__device__ __forceinline__ int seq_status(const AttnParams& p, int n, int L) {
+// Status of a sequence with n live rows, L committed keys and (packed rows
+// only) first row start: TV_ROW_OK (live), -1 (padded: n == 0) or an error.
+__device__ __forceinline__ int seq_status(const AttnParams& p, int n, int L, int start) {
   if (n < 0 || n > p.T) return TV_ROW_NNODES;
   if (n == 0) return -1;
+  if (p.row_start && (start < 0 || start > p.rows_total - n)) return TV_ROW_BAD_START;
   if (L < 0 || L > p.max_ctx || static_cast<int64_t>(L) + n > p.kv_capacity)
     return TV_ROW_CTX_BOUND;
   return TV_ROW_OK;
+}
+
+// First output row of sequence b: its packed start, else b T.
+__device__ __forceinline__ int64_t seq_row0(const AttnParams& p, int b, int start) {
+  return p.row_start ? static_cast<int64_t>(start) : static_cast<int64_t>(b) * p.T;
 }
 
 // a / b for 0 <= a, 1 <= b (exact). Below 2^22 the float quotient through
@@ -120,39 +128,46 @@ __device__ __forceinline__ int row_node(const AttnParams& p, int r) {
   return static_cast<int>((static_cast<uint32_t>(r) * p.g_mul) >> 16);
 }
 
-// Status of sequence b (see seq_status); also returns its n and L.
-__device__ __forceinline__ int seq_check(const AttnParams& p, int b, int& n, int& L) {
+// Status of sequence b (see seq_status); also returns its n, L and packed
+// start (0 without packed rows).
+__device__ __forceinline__ int seq_check(const AttnParams& p, int b, int& n, int& L, int& start) {
   n = p.n_nodes[b];
   L = p.ctx_len[b];
-  return seq_status(p, n, L);
+  start = p.row_start ? p.row_start[b] : 0;
+  return seq_status(p, n, L, start);
 }
 
 
 // Padded (n == 0) and invalid sequences: every output row gets the padding
 // values (O = 0, lse = -inf) and every sequence its status, spread over the
-// whole grid. st0 holds the statuses of the first 64 sequences (lane b:
+// whole grid. With packed rows a sequence owns only its n rows, written when
+// n and its start are valid (a bounds error writes nothing). st0 holds the statuses of the first 64 sequences (lane b:
 // sequence b); later blocks of 64 are read in one round before their stores
 // (a load placed after the stores would wait for them: the compiler cannot
 // rule out that they alias the length arrays).
 template <int D>
-__device__ void finish_non_live(const AttnParams& p, int st0) {
+__device__ void finish_non_live(const AttnParams& p, int st0, int n0, int s0) {
   constexpr int D4 = D / 4;
   const int nthreads = gridDim.x * blockDim.x;
   const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
   const int lane = threadIdx.x & 63;
-  const int per_seq = p.T * p.Hq * D4;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     const bool has = b0 + lane < p.B;
-    int st = st0;
-    if (b0 > 0 && has) {
-      int n, L;
-      st = seq_check(p, b0 + lane, n, L);
-    }
+    int st = st0, n = n0, L, start = s0;
+    if (b0 > 0 && has) st = seq_check(p, b0 + lane, n, L, start);
     if (gtid < 64 && has) p.row_status[b0 + lane] = (st == -1) ? TV_ROW_OK : st;
-    for (uint64_t m = __ballot(has && st != TV_ROW_OK); m; m &= m - 1) {
-      const int b = b0 + __builtin_ctzll(m);
-      float4* o = reinterpret_cast<float4*>(p.out + static_cast<int64_t>(b) * p.T * p.Hq * D);
-      float* l = p.lse + static_cast<int64_t>(b) * p.T * p.Hq;
+    // Rows to clear: all T in the padded layout, the sequence's own n rows
+    // when packed (none if n or the start is out of bounds).
+    const int nclr = !p.row_start ? p.T
+                     : (st == TV_ROW_CTX_BOUND ? n : 0);
+    for (uint64_t m = __ballot(has && st != TV_ROW_OK && nclr > 0); m; m &= m - 1) {
+      const int bl = __builtin_ctzll(m);
+      const int b = b0 + bl;
+      const int rows = __shfl(nclr, bl);
+      const int64_t r0 = seq_row0(p, b, __shfl(start, bl));
+      float4* o = reinterpret_cast<float4*>(p.out + r0 * p.Hq * D);
+      float* l = p.lse + r0 * p.Hq;
+      const int per_seq = rows * p.Hq * D4;
       for (int idx = gtid; idx < per_seq; idx += nthreads) {
         o[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (idx % D4 == 0) l[idx / D4] = -INFINITY;
@@ -174,8 +189,8 @@ constexpr int kMinUnit = 256;  // smallest balanced unit (keys)
 
 // Committed length of sequence b if it is live, else -1.
 __device__ __forceinline__ int live_len(const AttnParams& p, int b) {
-  int n, L;
-  return seq_check(p, b, n, L) == TV_ROW_OK ? L : -1;
+  int n, L, start;
+  return seq_check(p, b, n, L, start) == TV_ROW_OK ? L : -1;
 }
 
 __device__ __forceinline__ int wave_sum_i(int x) {
@@ -185,30 +200,36 @@ __device__ __forceinline__ int wave_sum_i(int x) {
 }
 
 // Every wave loads the committed lengths of the first 64 sequences once
-// (lane b holds sequence b, -1 if not live, and its status in st0); longer
-// batches re-read the rest from memory (L2) in each pass.
-__device__ __forceinline__ int lane_len(const AttnParams& p, int& n0, int& st0) {
+// (lane b holds sequence b, -1 if not live, its n in n0, packed start in s0
+// and status in st0); longer batches re-read the rest from memory (L2) in
+// each pass.
+__device__ __forceinline__ int lane_len(const AttnParams& p, int& n0, int& s0, int& st0) {
   const int lane = threadIdx.x & 63;
   int L = -1;
   n0 = 0;
+  s0 = 0;
   st0 = TV_ROW_OK;
   if (lane < p.B) {
-    int n;
-    st0 = seq_check(p, lane, n, L);
+    int n, start;
+    st0 = seq_check(p, lane, n, L, start);
     if (st0 != TV_ROW_OK) L = -1;
     n0 = n;
+    s0 = start;
   }
   return L;
 }
-// (n, L) of live sequence b: from the lane cache for b < 64.
-__device__ __forceinline__ void unit_seq(const AttnParams& p, int b, int len0, int n0, int& n,
-                                         int& L) {
+// (n, L, first output row) of live sequence b: from the lane cache for b < 64.
+__device__ __forceinline__ void unit_seq(const AttnParams& p, int b, int len0, int n0, int s0,
+                                         int& n, int& L, int64_t& row0) {
+  int start;
   if (b < 64) {
     n = __builtin_amdgcn_readlane(n0, b);
     L = __builtin_amdgcn_readlane(len0, b);
+    start = __builtin_amdgcn_readlane(s0, b);
   } else {
-    seq_check(p, b, n, L);
+    seq_check(p, b, n, L, start);
   }
+  row0 = seq_row0(p, b, start);
 }
 __device__ __forceinline__ int block_len(const AttnParams& p, int b0, int len0) {
   const int b = b0 + (threadIdx.x & 63);
@@ -509,8 +530,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int n0, st0;
-  const int len0 = lane_len(p, n0, st0);
+  int n0, s0, st0;
+  const int len0 = lane_len(p, n0, s0, st0);
   const int K = choose_unit(p, len0);
   if (p.sched && blockIdx.x == 0 && wave == 0) write_sched(p, len0, K);
 
@@ -518,7 +539,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   auto run_unit = [&](int u, int b, int kvh, int rg, int c, int nch)
                       __attribute__((always_inline)) {
   int n, L;
-  unit_seq(p, b, len0, n0, n, L);
+  int64_t srow0;  // output row of tree row 0
+  unit_seq(p, b, len0, n0, s0, n, L, srow0);
   const bool last = (c == nch - 1);
   const int kbeg = unit_start(p, L, K, nch, c);
   const int kend = last ? L + n : unit_start(p, L, K, nch, c + 1);
@@ -530,6 +552,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   const int l16 = lane & 15;
   const int row0 = rg * kRowsWG + wave * kRowsWave;
   const bool wave_active = row0 < p.R;
+  // Packed rows: q row of tree row 0 is the sequence's start (no batch stride).
+  const int64_t qseq = p.row_start ? srow0 * p.q_st : b * p.q_sb;
   bf16x8_t qf[kRT][KS];
   int node_rt[kRT];
 #pragma unroll
@@ -539,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
     const int node = (r < p.R && i < n) ? i : -1;
     node_rt[rt] = node;
     const int h = kvh * p.G + (r - i * p.G);
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + b * p.q_sb +
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + qseq +
                            (node < 0 ? 0 : node) * p.q_st + (node < 0 ? 0 : h) * p.q_sh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -870,11 +894,12 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
     const int r = row0 + rt * 16 + l16;
     if (r >= p.R) continue;
     if (direct) {
+      const bool live = node_rt[rt] >= 0;
+      if (p.row_start && !live) continue;  // packed: rows past n do not exist
       const int i = row_node(p, r);
       const int h = kvh * p.G + (r - i * p.G);
-      const int64_t orow = (static_cast<int64_t>(b) * p.T + i) * p.Hq + h;
+      const int64_t orow = (srow0 + i) * p.Hq + h;
       float* dst = p.out + orow * D;
-      const bool live = node_rt[rt] >= 0;
       const float inv = live ? 1.f / l_tot[rt] : 0.f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -912,7 +937,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   };
 
   // Padding outputs first: their stores drain while the first tiles load.
-  finish_non_live<D>(p, st0);
+  finish_non_live<D>(p, st0, n0, s0);
   const int u0 = first_unit(p);
   for (int u = u0;; u += p.nw) {
     int b, kvh, rg, c, nch;
@@ -936,15 +961,16 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
   __shared__ uint32_t sMask[TV_MAX_TREE * (TV_MAX_TREE / 32)];
 
   const int tid = threadIdx.x;
-  int n0, st0;
-  const int len0 = lane_len(p, n0, st0);
+  int n0, s0, st0;
+  const int len0 = lane_len(p, n0, s0, st0);
   const int K = choose_unit(p, len0);
   if (p.sched && blockIdx.x == 0 && tid < tv::kWave) write_sched(p, len0, K);
 
   auto run_unit = [&](int u, int b, int kvh, int rg, int c, int nch)
                       __attribute__((always_inline)) {
   int n, L;
-  unit_seq(p, b, len0, n0, n, L);
+  int64_t srow0;  // output row of tree row 0
+  unit_seq(p, b, len0, n0, s0, n, L, srow0);
   const bool last = (c == nch - 1);
   const int kbeg = unit_start(p, L, K, nch, c);
   const int kend = last ? L + n : unit_start(p, L, K, nch, c + 1);
@@ -968,7 +994,8 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
   float qv[DQ];
   float ov[DQ];
   if (node >= 0) {
-    const float* qrow = static_cast<const float*>(p.q) + b * p.q_sb + node * p.q_st + h * p.q_sh;
+    const float* qrow = static_cast<const float*>(p.q) +
+                        (p.row_start ? srow0 * p.q_st : b * p.q_sb) + node * p.q_st + h * p.q_sh;
 #pragma unroll
     for (int d = 0; d < DQ; ++d) qv[d] = qrow[quarter * DQ + d];
   } else {
@@ -1022,8 +1049,9 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
   if (r >= p.R) return;
   const int i = row_node(p, r);
   if (nch == 1) {
-    const int64_t orow = (static_cast<int64_t>(b) * p.T + i) * p.Hq + h;
     const bool live = node >= 0;
+    if (p.row_start && !live) return;  // packed: rows past n do not exist
+    const int64_t orow = (srow0 + i) * p.Hq + h;
     const float inv = live ? 1.f / l_run : 0.f;
 #pragma unroll
     for (int d = 0; d < DQ; ++d) p.out[orow * D + quarter * DQ + d] = live ? ov[d] * inv : 0.f;
@@ -1039,7 +1067,7 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
   };
 
   // Padding outputs first: their stores drain while the first tiles load.
-  finish_non_live<D>(p, st0);
+  finish_non_live<D>(p, st0, n0, s0);
   const int u0 = first_unit(p);
   for (int u = u0;; u += p.nw) {
     int b, kvh, rg, c, nch;
@@ -1074,17 +1102,19 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   const int L = p.ctx_len[b];
   const int K = p.sched[0];
   const int first = p.sched[1 + b];
-  // Keeps the four loads ahead of the branches below (the compiler would
+  const int start = p.row_start ? p.row_start[b] : 0;
+  // Keeps the loads ahead of the branches below (the compiler would
   // otherwise sink each one into the branch that first needs it and wait
   // for them one by one).
-  asm volatile("" ::"s"(n), "s"(L), "s"(K), "s"(first));
+  asm volatile("" ::"s"(n), "s"(L), "s"(K), "s"(first), "s"(start));
   if (r >= p.R) return;
-  if (seq_status(p, n, L) != TV_ROW_OK) return;  // padded / invalid: done by the split
+  if (seq_status(p, n, L, start) != TV_ROW_OK) return;  // padded / invalid: done by the split
   const int nch = pair_units(p, L, K);
   if (nch == 1) return;                           // written directly by the split
   const int i = row_node(p, r);
   const int h = kvh * p.G + (r - i * p.G);
-  const int64_t orow = (static_cast<int64_t>(b) * p.T + i) * p.Hq + h;
+  if (i >= n && p.row_start) return;  // packed: rows past n do not exist
+  const int64_t orow = (seq_row0(p, b, start) + i) * p.Hq + h;
   float4* dst = reinterpret_cast<float4*>(p.out + orow * D) + sub;
   if (i >= n) {
     *dst = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1264,14 +1294,16 @@ extern "C" size_t tv_tree_attention_workspace_size(int B, int T, int Hq, int Hkv
   return workspace_layout(B, T, Hq, Hkv, D, max_ctx, chunk_keys).total;
 }
 
-extern "C" int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
-                                 const void* k, const void* v, int64_t kv_sb, int64_t kv_sh,
-                                 int64_t kv_ss, const int32_t* ctx_len, const int32_t* n_nodes,
-                                 const uint32_t* mask, int B, int T, int Hq, int Hkv, int D,
-                                 int max_ctx, int kv_capacity, float scale, int in_dtype,
-                                 int probability_parts, int chunk_keys, float* out, float* lse,
-                                 void* workspace, size_t ws_bytes, int32_t* row_status,
-                                 hipStream_t stream) {
+namespace {
+
+// Both layouts: row_start == nullptr is the padded [B][T] layout.
+int attention_call(const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh, const void* k,
+                   const void* v, int64_t kv_sb, int64_t kv_sh, int64_t kv_ss,
+                   const int32_t* ctx_len, const int32_t* n_nodes, const uint32_t* mask,
+                   const int32_t* row_start, int rows_total, int B, int T, int Hq, int Hkv, int D,
+                   int max_ctx, int kv_capacity, float scale, int in_dtype, int probability_parts,
+                   int chunk_keys, float* out, float* lse, void* workspace, size_t ws_bytes,
+                   int32_t* row_status, hipStream_t stream) {
   if (!q || !k || !v || !ctx_len || !n_nodes || !mask || !out || !lse || !row_status)
     return TV_ERR_NULL;
   if (in_dtype != TV_F32 && in_dtype != TV_BF16) return TV_ERR_DTYPE;
@@ -1307,6 +1339,8 @@ extern "C" int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int6
   p.ctx_len = ctx_len;
   p.n_nodes = n_nodes;
   p.mask = mask;
+  p.row_start = row_start;
+  p.rows_total = rows_total;
   p.B = B;
   p.T = T;
   p.Hq = Hq;
@@ -1340,4 +1374,38 @@ extern "C" int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int6
   else
     launch_all<64>(p, in_dtype, ws.total > 0, stream);
   return tvh::launch_status();
+}
+
+}  // namespace
+
+extern "C" int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
+                                 const void* k, const void* v, int64_t kv_sb, int64_t kv_sh,
+                                 int64_t kv_ss, const int32_t* ctx_len, const int32_t* n_nodes,
+                                 const uint32_t* mask, int B, int T, int Hq, int Hkv, int D,
+                                 int max_ctx, int kv_capacity, float scale, int in_dtype,
+                                 int probability_parts, int chunk_keys, float* out, float* lse,
+                                 void* workspace, size_t ws_bytes, int32_t* row_status,
+                                 hipStream_t stream) {
+  return attention_call(q, q_sb, q_st, q_sh, k, v, kv_sb, kv_sh, kv_ss, ctx_len, n_nodes, mask,
+                        nullptr, 0, B, T, Hq, Hkv, D, max_ctx, kv_capacity, scale, in_dtype,
+                        probability_parts, chunk_keys, out, lse, workspace, ws_bytes, row_status,
+                        stream);
+}
+
+extern "C" int tv_tree_attention_packed(const void* q, int64_t q_st, int64_t q_sh, const void* k,
+                                        const void* v, int64_t kv_sb, int64_t kv_sh,
+                                        int64_t kv_ss, const int32_t* ctx_len,
+                                        const int32_t* n_nodes, const uint32_t* mask,
+                                        const int32_t* row_start, int rows_total, int B, int T,
+                                        int Hq, int Hkv, int D, int max_ctx, int kv_capacity,
+                                        float scale, int in_dtype, int probability_parts,
+                                        int chunk_keys, float* out, float* lse, void* workspace,
+                                        size_t ws_bytes, int32_t* row_status,
+                                        hipStream_t stream) {
+  if (!row_start) return TV_ERR_NULL;
+  if (rows_total < 0) return TV_ERR_SHAPE;
+  return attention_call(q, 0, q_st, q_sh, k, v, kv_sb, kv_sh, kv_ss, ctx_len, n_nodes, mask,
+                        row_start, rows_total, B, T, Hq, Hkv, D, max_ctx, kv_capacity, scale,
+                        in_dtype, probability_parts, chunk_keys, out, lse, workspace, ws_bytes,
+                        row_status, stream);
 }
