@@ -94,20 +94,29 @@ struct AttnParams {
   int32_t* row_status;
 };
 
+// The kernels' parameter type: the packed-row layout is a compile-time
+// choice, so the padded kernels carry none of its address arithmetic.
+template <bool PK>
+struct AttnParamsT : AttnParams {
+  static constexpr bool kPacked = PK;
+};
+
 // Status of a sequence with n live rows, L committed keys and (packed rows
 // only) first row start: TV_ROW_OK (live), -1 (padded: n == 0) or an error.
-__device__ __forceinline__ int seq_status(const AttnParams& p, int n, int L, int start) {
+template <class P>
+__device__ __forceinline__ int seq_status(const P& p, int n, int L, int start) {
   if (n < 0 || n > p.T) return TV_ROW_NNODES;
   if (n == 0) return -1;
-  if (p.row_start && (start < 0 || start > p.rows_total - n)) return TV_ROW_BAD_START;
+  if (P::kPacked && (start < 0 || start > p.rows_total - n)) return TV_ROW_BAD_START;
   if (L < 0 || L > p.max_ctx || static_cast<int64_t>(L) + n > p.kv_capacity)
     return TV_ROW_CTX_BOUND;
   return TV_ROW_OK;
 }
 
 // First output row of sequence b: its packed start, else b T.
-__device__ __forceinline__ int64_t seq_row0(const AttnParams& p, int b, int start) {
-  return p.row_start ? static_cast<int64_t>(start) : static_cast<int64_t>(b) * p.T;
+template <class P>
+__device__ __forceinline__ int64_t seq_row0(const P& p, int b, int start) {
+  return P::kPacked ? static_cast<int64_t>(start) : static_cast<int64_t>(b) * p.T;
 }
 
 // a / b for 0 <= a, 1 <= b (exact). Below 2^22 the float quotient through
@@ -130,10 +139,11 @@ __device__ __forceinline__ int row_node(const AttnParams& p, int r) {
 
 // Status of sequence b (see seq_status); also returns its n, L and packed
 // start (0 without packed rows).
-__device__ __forceinline__ int seq_check(const AttnParams& p, int b, int& n, int& L, int& start) {
+template <class P>
+__device__ __forceinline__ int seq_check(const P& p, int b, int& n, int& L, int& start) {
   n = p.n_nodes[b];
   L = p.ctx_len[b];
-  start = p.row_start ? p.row_start[b] : 0;
+  start = P::kPacked ? p.row_start[b] : 0;
   return seq_status(p, n, L, start);
 }
 
@@ -145,8 +155,8 @@ __device__ __forceinline__ int seq_check(const AttnParams& p, int b, int& n, int
 // sequence b); later blocks of 64 are read in one round before their stores
 // (a load placed after the stores would wait for them: the compiler cannot
 // rule out that they alias the length arrays).
-template <int D>
-__device__ void finish_non_live(const AttnParams& p, int st0, int n0, int s0) {
+template <int D, class P>
+__device__ void finish_non_live(const P& p, int st0, int n0, int s0) {
   constexpr int D4 = D / 4;
   const int nthreads = gridDim.x * blockDim.x;
   const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
@@ -158,7 +168,7 @@ __device__ void finish_non_live(const AttnParams& p, int st0, int n0, int s0) {
     if (gtid < 64 && has) p.row_status[b0 + lane] = (st == -1) ? TV_ROW_OK : st;
     // Rows to clear: all T in the padded layout, the sequence's own n rows
     // when packed (none if n or the start is out of bounds).
-    const int nclr = !p.row_start ? p.T
+    const int nclr = !P::kPacked ? p.T
                      : (st == TV_ROW_CTX_BOUND ? n : 0);
     for (uint64_t m = __ballot(has && st != TV_ROW_OK && nclr > 0); m; m &= m - 1) {
       const int bl = __builtin_ctzll(m);
@@ -188,7 +198,8 @@ __device__ void finish_non_live(const AttnParams& p, int st0, int n0, int s0) {
 constexpr int kMinUnit = 256;  // smallest balanced unit (keys)
 
 // Committed length of sequence b if it is live, else -1.
-__device__ __forceinline__ int live_len(const AttnParams& p, int b) {
+template <class P>
+__device__ __forceinline__ int live_len(const P& p, int b) {
   int n, L, start;
   return seq_check(p, b, n, L, start) == TV_ROW_OK ? L : -1;
 }
@@ -203,7 +214,8 @@ __device__ __forceinline__ int wave_sum_i(int x) {
 // (lane b holds sequence b, -1 if not live, its n in n0, packed start in s0
 // and status in st0); longer batches re-read the rest from memory (L2) in
 // each pass.
-__device__ __forceinline__ int lane_len(const AttnParams& p, int& n0, int& s0, int& st0) {
+template <class P>
+__device__ __forceinline__ int lane_len(const P& p, int& n0, int& s0, int& st0) {
   const int lane = threadIdx.x & 63;
   int L = -1;
   n0 = 0;
@@ -219,7 +231,8 @@ __device__ __forceinline__ int lane_len(const AttnParams& p, int& n0, int& s0, i
   return L;
 }
 // (n, L, first output row) of live sequence b: from the lane cache for b < 64.
-__device__ __forceinline__ void unit_seq(const AttnParams& p, int b, int len0, int n0, int s0,
+template <class P>
+__device__ __forceinline__ void unit_seq(const P& p, int b, int len0, int n0, int s0,
                                          int& n, int& L, int64_t& row0) {
   int start;
   if (b < 64) {
@@ -231,7 +244,8 @@ __device__ __forceinline__ void unit_seq(const AttnParams& p, int b, int len0, i
   }
   row0 = seq_row0(p, b, start);
 }
-__device__ __forceinline__ int block_len(const AttnParams& p, int b0, int len0) {
+template <class P>
+__device__ __forceinline__ int block_len(const P& p, int b0, int len0) {
   const int b = b0 + (threadIdx.x & 63);
   return b0 == 0 ? len0 : (b < p.B ? live_len(p, b) : -1);
 }
@@ -263,7 +277,8 @@ __device__ __forceinline__ int units_of(const AttnParams& p, int L, int K) {
 }
 
 // Units of the whole launch (wave-uniform; every lane must call).
-__device__ int total_units(const AttnParams& p, int len0, int K) {
+template <class P>
+__device__ int total_units(const P& p, int len0, int K) {
   int acc = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) acc += units_of(p, block_len(p, b0, len0), K);
   return wave_sum_i(acc);
@@ -272,7 +287,8 @@ __device__ int total_units(const AttnParams& p, int len0, int K) {
 // Keys per unit: the caller's fixed chunk, else the smallest multiple of 64
 // (at least kMinUnit) that cuts the launch into at most nw units, so that a
 // single pass of the nw workgroups covers it with the least work per unit.
-__device__ int choose_unit(const AttnParams& p, int len0) {
+template <class P>
+__device__ int choose_unit(const P& p, int len0) {
   if (p.kunit > 0) return p.kunit;
   int maxl = 0, keys = 0;
   if (p.B <= 64) {
@@ -338,7 +354,8 @@ __device__ int choose_unit(const AttnParams& p, int len0) {
 
 // Unit u -> (b, kvh, rg, c) and the pair's unit count nch; false past the
 // last unit (wave-uniform; every lane must call).
-__device__ bool decode_unit(const AttnParams& p, int len0, int K, int u, int& b, int& kvh, int& rg,
+template <class P>
+__device__ bool decode_unit(const P& p, int len0, int K, int u, int& b, int& kvh, int& rg,
                             int& c, int& nch) {
   const int lane = threadIdx.x & 63;
   if (p.B <= 64) {
@@ -391,7 +408,8 @@ __device__ bool decode_unit(const AttnParams& p, int len0, int K, int u, int& b,
 }
 
 // Table for the combine kernel: K, then the first unit of every sequence.
-__device__ void write_sched(const AttnParams& p, int len0, int K) {
+template <class P>
+__device__ void write_sched(const P& p, int len0, int K) {
   const int lane = threadIdx.x & 63;
   if (lane == 0) p.sched[0] = K;
   if (p.B <= 64) {
@@ -504,17 +522,8 @@ __device__ __forceinline__ float row_sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// max(a, b, c) in one v_max3_f32. fmaxf on MFMA results makes the compiler
-// quieten each input first (one extra v_max per value); the scores here are
-// never NaN, so that step is not needed.
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-template <int D, int PARTS>
-__global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p) {
+template <int D, int PARTS, bool PACKED>
+__global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<PACKED> p) {
   constexpr int CH16 = D / 8;                    // 16-byte chunks per key row
   constexpr int KS = D / 32;                     // MFMA k-steps along D
   constexpr int DT = D / 16;                     // 16-wide d tiles of O
@@ -553,7 +562,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
   const int row0 = rg * kRowsWG + wave * kRowsWave;
   const bool wave_active = row0 < p.R;
   // Packed rows: q row of tree row 0 is the sequence's start (no batch stride).
-  const int64_t qseq = p.row_start ? srow0 * p.q_st : b * p.q_sb;
+  const int64_t qseq = PACKED ? srow0 * p.q_st : b * p.q_sb;
   bf16x8_t qf[kRT][KS];
   int node_rt[kRT];
 #pragma unroll
@@ -895,7 +904,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
     if (r >= p.R) continue;
     if (direct) {
       const bool live = node_rt[rt] >= 0;
-      if (p.row_start && !live) continue;  // packed: rows past n do not exist
+      if (PACKED && !live) continue;  // packed: rows past n do not exist
       const int i = row_node(p, r);
       const int h = kvh * p.G + (r - i * p.G);
       const int64_t orow = (srow0 + i) * p.Hq + h;
@@ -952,8 +961,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParams p)
 // alone would move the log-sum-exp by ~1e-3). Four lanes share a packed row,
 // each holding a quarter of D; keys are staged through LDS 32 at a time.
 
-template <int D>
-__global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams p) {
+template <int D, bool PACKED>
+__global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParamsT<PACKED> p) {
   constexpr int DQ = D / 4;
   constexpr int D4 = D / 4;  // float4 per key row
   __shared__ __attribute__((aligned(16))) float sK[kKBf32 * D];
@@ -995,7 +1004,7 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
   float ov[DQ];
   if (node >= 0) {
     const float* qrow = static_cast<const float*>(p.q) +
-                        (p.row_start ? srow0 * p.q_st : b * p.q_sb) + node * p.q_st + h * p.q_sh;
+                        (PACKED ? srow0 * p.q_st : b * p.q_sb) + node * p.q_st + h * p.q_sh;
 #pragma unroll
     for (int d = 0; d < DQ; ++d) qv[d] = qrow[quarter * DQ + d];
   } else {
@@ -1050,7 +1059,7 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
   const int i = row_node(p, r);
   if (nch == 1) {
     const bool live = node >= 0;
-    if (p.row_start && !live) return;  // packed: rows past n do not exist
+    if (PACKED && !live) return;  // packed: rows past n do not exist
     const int64_t orow = (srow0 + i) * p.Hq + h;
     const float inv = live ? 1.f / l_run : 0.f;
 #pragma unroll
@@ -1087,8 +1096,8 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParams 
 // reduction. Up to 16 units per round are requested at once. Q16: the
 // partial rows are int16 fixed point, entry = q * scale / 32767.
 
-template <int D, bool Q16>
-__global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParams p) {
+template <int D, bool Q16, bool PACKED>
+__global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParamsT<PACKED> p) {
   constexpr int LPR = D / 4;                                     // lanes per packed row
   constexpr int RPB = kThreadsCombine / LPR;                     // packed rows per block
   constexpr int U = 16;
@@ -1102,7 +1111,7 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   const int L = p.ctx_len[b];
   const int K = p.sched[0];
   const int first = p.sched[1 + b];
-  const int start = p.row_start ? p.row_start[b] : 0;
+  const int start = PACKED ? p.row_start[b] : 0;
   // Keeps the loads ahead of the branches below (the compiler would
   // otherwise sink each one into the branch that first needs it and wait
   // for them one by one).
@@ -1113,7 +1122,7 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   if (nch == 1) return;                           // written directly by the split
   const int i = row_node(p, r);
   const int h = kvh * p.G + (r - i * p.G);
-  if (i >= n && p.row_start) return;  // packed: rows past n do not exist
+  if (i >= n && PACKED) return;  // packed: rows past n do not exist
   const int64_t orow = (seq_row0(p, b, start) + i) * p.Hq + h;
   float4* dst = reinterpret_cast<float4*>(p.out + orow * D) + sub;
   if (i >= n) {
@@ -1259,25 +1268,29 @@ WsLayout workspace_layout(int B, int T, int Hq, int Hkv, int D, int max_ctx, int
   return w;
 }
 
-template <int D>
-void launch_all(const AttnParams& p, int in_dtype, bool combine, hipStream_t stream) {
+template <int D, bool PACKED>
+void launch_all(const AttnParams& p0, int in_dtype, bool combine, hipStream_t stream) {
+  AttnParamsT<PACKED> p;
+  static_cast<AttnParams&>(p) = p0;
   const dim3 grid(p.nw);
   if (in_dtype == TV_BF16) {
     if (p.parts == 1)
-      hipLaunchKernelGGL((attn_split_bf16_kernel<D, 1>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((attn_split_bf16_kernel<D, 1, PACKED>), grid, dim3(kThreads), 0, stream, p);
     else if (p.parts == 2)
-      hipLaunchKernelGGL((attn_split_bf16_kernel<D, 2>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((attn_split_bf16_kernel<D, 2, PACKED>), grid, dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_split_bf16_kernel<D, 3>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((attn_split_bf16_kernel<D, 3, PACKED>), grid, dim3(kThreads), 0, stream, p);
   } else
-    hipLaunchKernelGGL(attn_split_f32_kernel<D>, grid, dim3(kThreadsF32), 0, stream, p);
+    hipLaunchKernelGGL((attn_split_f32_kernel<D, PACKED>), grid, dim3(kThreadsF32), 0, stream, p);
   if (combine) {
     const dim3 cgrid((p.R + kThreadsCombine / (D / 4) - 1) / (kThreadsCombine / (D / 4)),
                      p.B * p.Hkv);
     if (in_dtype == TV_BF16 && p.parts == 1)
-      hipLaunchKernelGGL((attn_combine_kernel<D, true>), cgrid, dim3(kThreadsCombine), 0, stream, p);
+      hipLaunchKernelGGL((attn_combine_kernel<D, true, PACKED>), cgrid, dim3(kThreadsCombine), 0,
+                         stream, p);
     else
-      hipLaunchKernelGGL((attn_combine_kernel<D, false>), cgrid, dim3(kThreadsCombine), 0, stream, p);
+      hipLaunchKernelGGL((attn_combine_kernel<D, false, PACKED>), cgrid, dim3(kThreadsCombine), 0,
+                         stream, p);
   }
 }
 
@@ -1369,10 +1382,13 @@ int attention_call(const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh, cons
     p.part_ml = reinterpret_cast<float4*>(base + ws.part_ml);
   }
   p.row_status = row_status;
+  const bool combine = ws.total > 0;
   if (D == 128)
-    launch_all<128>(p, in_dtype, ws.total > 0, stream);
+    row_start ? launch_all<128, true>(p, in_dtype, combine, stream)
+              : launch_all<128, false>(p, in_dtype, combine, stream);
   else
-    launch_all<64>(p, in_dtype, ws.total > 0, stream);
+    row_start ? launch_all<64, true>(p, in_dtype, combine, stream)
+              : launch_all<64, false>(p, in_dtype, combine, stream);
   return tvh::launch_status();
 }
 
