@@ -51,6 +51,8 @@ def parse():
                     help="skip the secondary sampling-acceptance measurement")
     ap.add_argument("--no-projections", action="store_true",
                     help="skip the few-row projection measurement")
+    ap.add_argument("--no-packed", action="store_true",
+                    help="skip the packed-row attention and budget-controller measurement")
     ap.add_argument("--commit-layers", type=int, default=28,
                     help="layers of the KV-commit measurement (0 skips it)")
     ap.add_argument("--graph", type=int, default=0,
@@ -357,6 +359,9 @@ def main():
         res["projections"] = projections_secondary(tv, torch, dev, w, args)
     if args.commit_layers > 0 and w.mode == "greedy":
         res["kv_commit"] = commit_secondary(tv, torch, dev, w, sets[0], acc_out, args)
+    if not args.no_packed:
+        res["packed_rows"] = packed_secondary(tv, torch, dev, w, sets, bufs, ws_attn, acc_out,
+                                              t_attn, args)
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
@@ -448,6 +453,52 @@ def commit_secondary(tv, torch, dev, w, s, acc_out, args):
     by = moved * w.Hkv * w.D * 2 * 2 * 2 * layers  # K and V rows, read + write, bf16
     return {"workload": "C3 greedy acceptance, %d layers" % layers, "accepted_nodes": moved,
             "commit_us": round(t * 1e6, 3), "alg_bytes": by, "GBps": round(by / t / 1e9, 1)}
+
+
+def packed_secondary(tv, torch, dev, w, sets, bufs, ws_attn, acc_out, t_padded, args):
+    """The same attention over packed query rows (live rows back to back, one
+    spare row between sequences), cold like the headline call, and the
+    device-side budget controller fed by the step's acceptance."""
+    n = w.n_nodes.astype(np.int64)
+    start = np.zeros(w.B, np.int32)
+    pos = 0
+    for b in range(w.B):
+        start[b] = pos
+        pos += int(n[b]) + 1
+    rows = pos
+    start_d = torch.from_numpy(start).to(dev)
+    packed = []
+    for s in sets:
+        q = torch.empty((rows, w.Hq, w.D), dtype=s["q"].dtype, device=dev)
+        for b in range(w.B):
+            q[int(start[b]):int(start[b]) + int(n[b])] = s["q"][b, :int(n[b])]
+        packed.append(q)
+    out = torch.empty((rows, w.Hq, w.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((rows, w.Hq), dtype=torch.float32, device=dev)
+    st = torch.empty((w.B,), dtype=torch.int32, device=dev)
+
+    def call(i):
+        s = sets[i % len(sets)]
+        tv.tree_attention_packed(packed[i % len(sets)], s["k"], s["v"], s["ctx"], s["n"],
+                                 bufs[i % len(bufs)]["mask"][0], start_d, w.max_ctx,
+                                 scale=float(w.scale), probability_parts=args.parts,
+                                 chunk_keys=args.chunk, out=out, lse=lse, row_status=st,
+                                 workspace=ws_attn)
+
+    t = time_calls(torch, call, max(20, args.steps))
+    ema = torch.full((w.B,), 0.5, dtype=torch.float32, device=dev)
+    bud = torch.full((w.B,), w.T - 1, dtype=torch.int32, device=dev)
+    rs = torch.empty((w.B,), dtype=torch.int32, device=dev)
+    rt = torch.empty((1,), dtype=torch.int32, device=dev)
+
+    def ctl(i):
+        tv.adapt_tree_budget(acc_out[0], sets[0]["n"], ema, bud, 0.5, 0.25, 2, w.T - 1,
+                             row_start=rs, rows_total=rt)
+
+    tc = time_calls(torch, ctl, max(20, args.steps))
+    return {"rows": rows, "padded_rows": w.B * w.T, "attention_us": round(t * 1e6, 3),
+            "padded_attention_us": round(t_padded * 1e6, 3),
+            "budget_controller_us": round(tc * 1e6, 3)}
 
 
 def sampling_secondary(tv, torch, dev, args):

@@ -12,16 +12,19 @@
 //
 // MI355X: y^T = W x^T on v_mfma_f32_16x16x32_bf16, so that each lane ends
 // with four consecutive output features of one row (one 8-byte store). A
-// workgroup (4 waves) owns 64 rows x 128 output features; wave w the features
-// [32 w, 32 w + 32) of all 64 rows (2 x 4 accumulator tiles). Every output
-// element is one accumulator chain over k = 0, 32, 64, ... in order, whatever
-// the tile and the row count. K is walked in chunks of 64: the input rows of
-// a chunk (8 KB) go through a three-stage LDS ring shared by the four waves,
-// written from registers loaded two chunks ahead; each wave's weight rows go
-// straight to registers, also two chunks ahead. Loads are plain (in-order)
-// vector loads, so the compiler's partial waits keep two chunks in flight.
-// Workgroups are numbered so that the row groups of one weight slice run on
-// the same XCD and share its L2.
+// workgroup (4 waves) owns 64 rows x 64 output features; wave w the features
+// [16 w, 16 w + 16) of all 64 rows (4 accumulator tiles, 8 with SwiGLU).
+// Every output element is one accumulator chain over k = 0, 32, 64, ... in
+// order, whatever the tile and the row count. K is walked in chunks of 64:
+// the input rows of a chunk (8 KB) are loaded into registers NST - 1 chunks
+// ahead and written to a two-stage LDS ring shared by the four waves one
+// chunk ahead; each wave's weight rows go straight to registers, also
+// NST - 1 chunks ahead. Loads are plain (in-order) vector loads, so the
+// compiler's partial waits keep those chunks in flight; the barrier that
+// closes a chunk waits for LDS operations only (a full __syncthreads would
+// also wait for every load in flight and serialise the chunks). Workgroups
+// are numbered so that the row groups of one weight slice run on the same
+// XCD and share its L2.
 #include "tv_common.h"
 
 namespace {
@@ -50,6 +53,12 @@ __device__ __forceinline__ bf16x8_t load8(const uint16_t* p) {
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
+
+// Workgroup barrier for the LDS ring: this wave's LDS operations complete
+// (lgkmcnt(0)), then s_barrier; global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // LDS layout of an input chunk: 64 rows of 64 k (128 B, eight 16-byte
 // pieces); piece c of row r sits at piece c ^ (r & 7), so the 16 rows an MFMA
@@ -142,27 +151,32 @@ __global__ __launch_bounds__(kLinThreads) void linear_rows_kernel(LinParams p) {
   // Chunk c lives in register stage c % NST and LDS stage c % 2.
   Stage r[NST];
 #pragma unroll
-  for (int j = 0; j < NST - 1; ++j)
-    if (j < nchunks) load_chunk(r[j], j);
+  for (int j = 0; j < NST - 1; ++j) load_chunk(r[j], min(j, nchunks - 1));
   store_x(r[0], 0);
   __syncthreads();
   int c = 0;
+  // No branches around the loads, here or in the prologue: the compiler then
+  // counts the loads in flight exactly (a path that skipped some would make
+  // it wait for nearly all of them in every iteration). Near the end the
+  // chunk index is clamped, so the last chunk is re-read into stages that
+  // are never computed, and the LDS stage past the last chunk receives data
+  // nobody reads.
   for (; c + NST <= nchunks; c += NST) {
 #pragma unroll
     for (int j = 0; j < NST; ++j) {
-      if (c + j + NST - 1 < nchunks) load_chunk(r[(j + NST - 1) % NST], c + j + NST - 1);
-      if (c + j + 1 < nchunks) store_x(r[(j + 1) % NST], (j + 1) & 1 ^ (c & 1));
+      load_chunk(r[(j + NST - 1) % NST], min(c + j + NST - 1, nchunks - 1));
+      store_x(r[(j + 1) % NST], ((j + 1) & 1) ^ (c & 1));
       compute(r[j], (j & 1) ^ (c & 1));
-      __syncthreads();
+      lds_barrier();
     }
   }
 #pragma unroll
   for (int j = 0; j < NST - 1; ++j) {
     if (c + j < nchunks) {
       if (c + j + NST - 1 < nchunks) load_chunk(r[(j + NST - 1) % NST], c + j + NST - 1);
-      if (c + j + 1 < nchunks) store_x(r[(j + 1) % NST], (j + 1) & 1 ^ (c & 1));
+      if (c + j + 1 < nchunks) store_x(r[(j + 1) % NST], ((j + 1) & 1) ^ (c & 1));
       compute(r[j], (j & 1) ^ (c & 1));
-      __syncthreads();
+      lds_barrier();
     }
   }
 
