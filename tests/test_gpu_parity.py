@@ -899,3 +899,61 @@ def _raw_bits(t):
     if t.is_floating_point():
         return t.view({2: torch.int16, 4: torch.int32}[t.element_size()])
     return t
+
+
+# ------------------------------------------------------- more than 64 seqs ---
+
+def _many_seqs(seed, dtype, B=150):
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(0, 400, B)
+    n = rng.integers(1, 10, B)
+    n[rng.random(B) < 0.1] = 0          # padded sequences, also past 64
+    return make_custom(seed, B, 4, 2, 64, 50, dtype, ctx.tolist(), 8, n_nodes=n.tolist(),
+                       trie_tokens=False)
+
+
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 0), ("bf16", 128), ("f32", 0)])
+def test_attention_more_than_64_sequences(dtype, chunk):
+    # Sequences past the first 64 take the block-scan paths of the schedule
+    # (unit size, unit decode, the combine's table) and the memory loads of
+    # their lengths; one of them is over its context bound.
+    w = _many_seqs(300 + chunk, dtype)
+    w.ctx_len[100] = w.max_ctx + 5 if w.n_nodes[100] else w.ctx_len[100]
+    d = upload(w)
+    mask = _mask_check(w, d)
+    got = run_attention(w, d, mask, chunk_keys=chunk)
+    tol = bf16_p_bound(w) if dtype == "bf16" else 2e-3
+    check_attention(w, got, oracle_attention(w), atol_out=tol)
+
+
+def test_attention_packed_more_than_64_sequences():
+    w = _many_seqs(401, "bf16")
+    d = upload(w)
+    mask = _mask_check(w, d)
+    qp, start, rows = _packed_layout(w, 13)
+    ctx = w.ctx_len.copy()
+    live_late = [b for b in range(70, w.B) if w.n_nodes[b] > 0]
+    ctx[live_late[0]] = w.max_ctx + 1          # context bound past 64
+    start[live_late[1]] = rows                 # start past the rows, past 64
+    d["ctx_len"] = torch.from_numpy(ctx.astype(np.int32)).cuda()
+    o, l, st = _run_packed(w, d, mask, qp, start)
+    o_ref, l_ref, st_ref = oracle.tree_attention_packed(
+        qp, w.k, w.v, w.dtype, ctx, w.n_nodes, w.parent, start, w.T, w.scale,
+        max_ctx=w.max_ctx, kv_capacity=w.kv_capacity)
+    assert st.tolist() == st_ref.tolist()
+    assert st_ref[live_late[0]] == oracle.ROW_CTX_BOUND
+    assert st_ref[live_late[1]] == oracle.ROW_BAD_START
+    untouched = np.isnan(l_ref)
+    assert np.all(l[untouched] == 12345.0) and np.all(o[untouched] == 12345.0)
+    live = ~untouched
+    assert np.abs(o[live] - o_ref[live]).max() <= bf16_p_bound(w)
+    fin = live & (l_ref > -np.inf)
+    assert np.all(l[live & ~fin] == -np.inf)
+    assert np.abs(l[fin] - l_ref[fin]).max() <= 1e-4
+    # And bitwise equal to the padded call for every live sequence.
+    o_pad, l_pad, _ = run_attention(w, d, mask)
+    for b in range(w.B):
+        n = int(w.n_nodes[b])
+        if st_ref[b] == 0 and n:
+            s0 = int(start[b])
+            assert np.array_equal(o[s0:s0 + n].view(np.uint32), o_pad[b, :n].view(np.uint32)), b
