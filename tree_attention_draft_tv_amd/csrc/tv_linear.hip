@@ -12,11 +12,12 @@
 //
 // MI355X: y^T = W x^T on v_mfma_f32_16x16x32_bf16, so that each lane ends
 // with four consecutive output features of one row (one 8-byte store). A
-// workgroup (4 waves) owns 64 rows x 64 output features; wave w the features
-// [16 w, 16 w + 16) of all 64 rows (4 accumulator tiles, 8 with SwiGLU).
-// Every output element is one accumulator chain over k = 0, 32, 64, ... in
-// order, whatever the tile and the row count. K is walked in chunks of 64:
-// the input rows of a chunk (8 KB) are loaded into registers NST - 1 chunks
+// workgroup (4 waves) owns ROWS rows x 64 output features; wave w the
+// features [16 w, 16 w + 16) of all ROWS rows (ROWS / 16 accumulator tiles,
+// twice that with SwiGLU). Every output element is one accumulator chain over
+// k = 0, 32, 64, ... in order, whatever the tile, the chunk depth and the row
+// count (the variants give the same bits; tested). K is walked in chunks of
+// KC: the input rows of a chunk are loaded into registers NST - 1 chunks
 // ahead and written to a two-stage LDS ring shared by the four waves one
 // chunk ahead; each wave's weight rows go straight to registers, also
 // NST - 1 chunks ahead. Loads are plain (in-order) vector loads, so the
@@ -34,9 +35,15 @@ typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kLinThreads = 256;
-constexpr int kLinRows = 64;    // rows per workgroup
 constexpr int kLinFeat = 64;    // output features per workgroup (16 per wave)
-constexpr int kLinKC = 64;      // K per chunk (two MFMA k-steps)
+constexpr int kLinKC = 64;      // K granularity of the arguments (two MFMA k-steps)
+// Rows per workgroup: 96 keeps a 264-row batch (three row groups) at 216
+// workgroups for the QKV shape, one per compute unit; with 64 rows the 360
+// workgroups put two on 104 units and take 1.6x as long (measured). Chunk
+// depth and register stages were measured per kernel: 64-deep chunks for the
+// plain projection, 128-deep for gate/up where K allows.
+constexpr int kRows = 96;
+constexpr int kDeepKC = 128;
 
 struct LinParams {
   const uint16_t* x;
@@ -60,18 +67,26 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// LDS layout of an input chunk: 64 rows of 64 k (128 B, eight 16-byte
-// pieces); piece c of row r sits at piece c ^ (r & 7), so the 16 rows an MFMA
-// operand read touches at one k-offset spread over the banks.
-__device__ __forceinline__ int x_slot(int row, int piece) { return row * 8 + (piece ^ (row & 7)); }
+// LDS layout of an input chunk of KC k: 64 rows of P = KC / 8 16-byte
+// pieces; piece c of row r sits at piece c ^ (r & (P - 1)), so the 16 rows an
+// MFMA operand read touches at one k-offset spread over the banks.
+template <int P>
+__device__ __forceinline__ int x_slot(int row, int piece) {
+  return row * P + (piece ^ (row & (P - 1)));
+}
 
 // NST register stages: chunk c + NST - 1 is requested while chunk c is
 // computed. Input rows go registers -> LDS one chunk ahead (two LDS stages
 // suffice: the barrier closing every chunk keeps all waves on the same chunk,
 // which reads stage c % 2 while stage (c + 1) % 2 is written).
-template <bool SWIGLU, int NST>
+template <bool SWIGLU, int NST, int KC, int ROWS>
 __global__ __launch_bounds__(kLinThreads) void linear_rows_kernel(LinParams p) {
-  __shared__ __attribute__((aligned(16))) u16x8_t sX[2][kLinRows * 8];
+  constexpr int P = KC / 8;                     // 16-byte pieces per row of a chunk
+  constexpr int XL = ROWS * P / kLinThreads;    // input pieces per thread per chunk
+  constexpr int KS = KC / 32;                   // MFMA k-steps per chunk
+  constexpr int MT = ROWS / 16;                 // row tiles per wave
+  static_assert(ROWS * P % kLinThreads == 0, "staging must divide evenly");
+  __shared__ __attribute__((aligned(16))) u16x8_t sX[2][ROWS * P];
   // Work item -> (weight slice, row group): the workgroups sharing
   // blockIdx mod 8 (one XCD) take one contiguous run of work items, and the
   // row groups of a slice are consecutive work items.
@@ -86,20 +101,20 @@ __global__ __launch_bounds__(kLinThreads) void linear_rows_kernel(LinParams p) {
   const int i16 = lane & 15;
   const int kg = lane >> 4;
   const int n0 = slice * kLinFeat + wave * 16;
-  const int m0 = mg * kLinRows;
-  const int nchunks = p.K / kLinKC;
+  const int m0 = mg * ROWS;
+  const int nchunks = p.K / KC;
 
-  // Staging: thread t loads pieces t and t + 256 of a chunk (row = s / 8,
-  // piece = s % 8); rows past M re-read row M - 1.
-  const uint16_t* xs[2];
-  int xslot[2];
+  // Staging: thread t loads pieces t, t + 256, ... of a chunk (row = s / P,
+  // piece = s % P); rows past M re-read row M - 1.
+  const uint16_t* xs[XL];
+  int xslot[XL];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int sidx = tid + 256 * j;
-    const int row = sidx >> 3;
-    const int piece = sidx & 7;
+  for (int j = 0; j < XL; ++j) {
+    const int sidx = tid + kLinThreads * j;
+    const int row = sidx / P;
+    const int piece = sidx % P;
     xs[j] = p.x + static_cast<int64_t>(min(m0 + row, p.M - 1)) * p.x_stride + 8 * piece;
-    xslot[j] = x_slot(row, piece);
+    xslot[j] = x_slot<P>(row, piece);
   }
   // This lane's weight row (feature n0 + i16), 16 bytes per k-step.
   const uint16_t* wg = p.w0 + static_cast<int64_t>(n0 + i16) * p.w_stride + 8 * kg;
@@ -107,40 +122,40 @@ __global__ __launch_bounds__(kLinThreads) void linear_rows_kernel(LinParams p) {
       SWIGLU ? p.w1 + static_cast<int64_t>(n0 + i16) * p.w_stride + 8 * kg : nullptr;
 
   struct Stage {
-    u16x8_t x[2];
-    bf16x8_t g[2];  // [k-step]
-    bf16x8_t u[2];
+    u16x8_t x[XL];
+    bf16x8_t g[KS];  // [k-step]
+    bf16x8_t u[SWIGLU ? KS : 1];
   };
   auto load_chunk = [&](Stage& st, int c) __attribute__((always_inline)) {
-    const int k0 = c * kLinKC;
+    const int k0 = c * KC;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) st.x[j] = *reinterpret_cast<const u16x8_t*>(xs[j] + k0);
+    for (int j = 0; j < XL; ++j) st.x[j] = *reinterpret_cast<const u16x8_t*>(xs[j] + k0);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < KS; ++s) {
       st.g[s] = load8(wg + k0 + 32 * s);
       if constexpr (SWIGLU) st.u[s] = load8(wu + k0 + 32 * s);
     }
   };
   auto store_x = [&](const Stage& st, int stage) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) sX[stage][xslot[j]] = st.x[j];
+    for (int j = 0; j < XL; ++j) sX[stage][xslot[j]] = st.x[j];
   };
 
-  f32x4_t a0[4], a1[4];
+  f32x4_t a0[MT], a1[SWIGLU ? MT : 1];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     a0[mt] = f32x4_t(0.f);
-    a1[mt] = f32x4_t(0.f);
+    if constexpr (SWIGLU) a1[mt] = f32x4_t(0.f);
   }
   auto compute = [&](const Stage& st, int stage) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8_t xf[4];
+    for (int s = 0; s < KS; ++s) {
+      bf16x8_t xf[MT];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        xf[mt] = __builtin_bit_cast(bf16x8_t, sX[stage][x_slot(16 * mt + i16, 4 * s + kg)]);
+      for (int mt = 0; mt < MT; ++mt)
+        xf[mt] = __builtin_bit_cast(bf16x8_t, sX[stage][x_slot<P>(16 * mt + i16, 4 * s + kg)]);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         a0[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.g[s], xf[mt], a0[mt], 0, 0, 0);
         if constexpr (SWIGLU)
           a1[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.u[s], xf[mt], a1[mt], 0, 0, 0);
@@ -182,7 +197,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_rows_kernel(LinParams p) {
 
   // Lane holds output features n0 + 4 kg + e (e = 0..3) of row m0 + 16 mt + i16.
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     const int m = m0 + 16 * mt + i16;
     if (m >= p.M) continue;
     uint32_t h[4];
@@ -226,17 +241,24 @@ int launch_linear(const void* x, int64_t x_stride, const void* w0, const void* w
   p.M = M;
   p.K = K;
   p.N = N;
-  p.mgroups = (M + kLinRows - 1) / kLinRows;
-  const int64_t work = static_cast<int64_t>(p.mgroups) * (N / kLinFeat);
-  if (work > (int64_t(1) << 30)) return TV_ERR_SHAPE;
-  p.work = static_cast<int>(work);
   p.y = static_cast<uint16_t*>(y);
-  const int grid = (p.work + 7) / 8 * 8;
-  if (swiglu)
-    hipLaunchKernelGGL((linear_rows_kernel<true, 5>), dim3(grid), dim3(kLinThreads), 0, stream, p);
+  auto launch = [&](auto kernel, int rows) {
+    p.mgroups = (M + rows - 1) / rows;
+    const int64_t work = static_cast<int64_t>(p.mgroups) * (N / kLinFeat);
+    if (work > (int64_t(1) << 30)) return TV_ERR_SHAPE;
+    p.work = static_cast<int>(work);
+    const int grid = (p.work + 7) / 8 * 8;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kLinThreads), 0, stream, p);
+    return TV_OK;
+  };
+  int rc;
+  if (!swiglu)
+    rc = launch(linear_rows_kernel<false, 6, 64, kRows>, kRows);
+  else if (K % kDeepKC == 0)
+    rc = launch(linear_rows_kernel<true, 3, kDeepKC, kRows>, kRows);
   else
-    hipLaunchKernelGGL((linear_rows_kernel<false, 6>), dim3(grid), dim3(kLinThreads), 0, stream,
-                       p);
+    rc = launch(linear_rows_kernel<true, 5, 64, kRows>, kRows);
+  if (rc != TV_OK) return rc;
   return tvh::launch_status();
 }
 
