@@ -34,8 +34,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kLinThreads = 256;
-constexpr int kLinFeat = 64;    // output features per workgroup (16 per wave)
+constexpr int kLinFeat = 64;    // N granularity of the arguments (16 features per wave)
 constexpr int kLinKC = 64;      // K granularity of the arguments (two MFMA k-steps)
 // Rows per workgroup: 96 keeps a 264-row batch (three row groups) at 216
 // workgroups for the QKV shape, one per compute unit; with 64 rows the 360
@@ -44,6 +43,7 @@ constexpr int kLinKC = 64;      // K granularity of the arguments (two MFMA k-st
 // plain projection, 128-deep for gate/up where K allows.
 constexpr int kRows = 96;
 constexpr int kDeepKC = 128;
+constexpr int kWavesWide = 8;
 
 struct LinParams {
   const uint16_t* x;
@@ -79,13 +79,15 @@ __device__ __forceinline__ int x_slot(int row, int piece) {
 // computed. Input rows go registers -> LDS one chunk ahead (two LDS stages
 // suffice: the barrier closing every chunk keeps all waves on the same chunk,
 // which reads stage c % 2 while stage (c + 1) % 2 is written).
-template <bool SWIGLU, int NST, int KC, int ROWS>
-__global__ __launch_bounds__(kLinThreads) void linear_rows_kernel(LinParams p) {
+template <bool SWIGLU, int NST, int KC, int ROWS, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void linear_rows_kernel(LinParams p) {
+  constexpr int THREADS = 64 * WAVES;
+  constexpr int FEAT = 16 * WAVES;              // output features per workgroup
   constexpr int P = KC / 8;                     // 16-byte pieces per row of a chunk
-  constexpr int XL = ROWS * P / kLinThreads;    // input pieces per thread per chunk
+  constexpr int XL = ROWS * P / THREADS;        // input pieces per thread per chunk
   constexpr int KS = KC / 32;                   // MFMA k-steps per chunk
   constexpr int MT = ROWS / 16;                 // row tiles per wave
-  static_assert(ROWS * P % kLinThreads == 0, "staging must divide evenly");
+  static_assert(ROWS * P % THREADS == 0, "staging must divide evenly");
   __shared__ __attribute__((aligned(16))) u16x8_t sX[2][ROWS * P];
   // Work item -> (weight slice, row group): the workgroups sharing
   // blockIdx mod 8 (one XCD) take one contiguous run of work items, and the
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_rows_kernel(LinParams p) {
   const int wave = tid >> 6;
   const int i16 = lane & 15;
   const int kg = lane >> 4;
-  const int n0 = slice * kLinFeat + wave * 16;
+  const int n0 = slice * FEAT + wave * 16;
   const int m0 = mg * ROWS;
   const int nchunks = p.K / KC;
 
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_rows_kernel(LinParams p) {
   int xslot[XL];
 #pragma unroll
   for (int j = 0; j < XL; ++j) {
-    const int sidx = tid + kLinThreads * j;
+    const int sidx = tid + THREADS * j;
     const int row = sidx / P;
     const int piece = sidx % P;
     xs[j] = p.x + static_cast<int64_t>(min(m0 + row, p.M - 1)) * p.x_stride + 8 * piece;
@@ -242,22 +244,22 @@ int launch_linear(const void* x, int64_t x_stride, const void* w0, const void* w
   p.K = K;
   p.N = N;
   p.y = static_cast<uint16_t*>(y);
-  auto launch = [&](auto kernel, int rows) {
+  auto launch = [&](auto kernel, int rows, int waves) {
     p.mgroups = (M + rows - 1) / rows;
-    const int64_t work = static_cast<int64_t>(p.mgroups) * (N / kLinFeat);
+    const int64_t work = static_cast<int64_t>(p.mgroups) * (N / (16 * waves));
     if (work > (int64_t(1) << 30)) return TV_ERR_SHAPE;
     p.work = static_cast<int>(work);
     const int grid = (p.work + 7) / 8 * 8;
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kLinThreads), 0, stream, p);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * waves), 0, stream, p);
     return TV_OK;
   };
   int rc;
   if (!swiglu)
-    rc = launch(linear_rows_kernel<false, 6, 64, kRows>, kRows);
-  else if (K % kDeepKC == 0)
-    rc = launch(linear_rows_kernel<true, 3, kDeepKC, kRows>, kRows);
+    rc = launch(linear_rows_kernel<false, 6, 64, kRows, 4>, kRows, 4);
+  else if (K % kDeepKC == 0 && N % (16 * kWavesWide) == 0)
+    rc = launch(linear_rows_kernel<true, 3, kDeepKC, kRows, kWavesWide>, kRows, kWavesWide);
   else
-    rc = launch(linear_rows_kernel<true, 5, 64, kRows>, kRows);
+    rc = launch(linear_rows_kernel<true, 5, 64, kRows, 4>, kRows, 4);
   if (rc != TV_OK) return rc;
   return tvh::launch_status();
 }
