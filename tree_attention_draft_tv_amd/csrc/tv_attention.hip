@@ -485,19 +485,30 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // 16-byte HBM -> LDS copy per lane (global_load_lds_dwordx4): lane i's bytes
-// land at lds_base + 16 i. Issued as inline assembly so that the compiler
-// does not serialise it against unrelated LDS reads of other ring stages;
-// completion is awaited explicitly with TV_WAIT_VMCNT before the barrier
-// that publishes the tile.
-__device__ __forceinline__ void lds_copy16(const void* gptr, const void* lds_base) {
+// land at lds_base + 16 i, read from sbase + voff (a wave-uniform base in
+// SGPRs plus a 32-bit byte offset per lane: one VGPR per address instead of
+// a 64-bit pair, which keeps the kernel's VGPRs from spilling). Issued as
+// inline assembly so that the compiler does not serialise it against
+// unrelated LDS reads of other ring stages; completion is awaited explicitly
+// with TV_WAIT_VMCNT before the barrier that publishes the tile.
+__device__ __forceinline__ void lds_copy16(const void* sbase, uint32_t voff, const void* lds_base) {
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) const void*)lds_base));
   asm volatile(
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
+      "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(gptr), "{m0}"(lds)
+      : "v"(voff), "s"(sbase), "{m0}"(lds)
       : "memory");
+}
+
+// A wave-uniform pointer, moved to SGPRs (the unit being processed is the
+// same in every lane, but the compiler cannot prove it).
+__device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 template <int V>
@@ -591,8 +602,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
   // A thread's chunk is the same in every load round. Keys at or past kend
   // are never read: their slots re-read key kend - 1 (finite data that the
   // softmax gives probability 0). Tile t lives in ring stage t mod kRing. ----
-  const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + b * p.kv_sb + kvh * p.kv_sh;
-  const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + b * p.kv_sb + kvh * p.kv_sh;
+  const void* kbase =
+      uniform_ptr(static_cast<const uint16_t*>(p.k) + b * p.kv_sb + kvh * p.kv_sh);
+  const void* vbase =
+      uniform_ptr(static_cast<const uint16_t*>(p.v) + b * p.kv_sb + kvh * p.kv_sh);
   const int ld_key = tid / CH16;
   const int ld_pch = tid - ld_key * CH16;
   const int ld_kch = ld_pch ^ k_swz<D>(ld_key);
@@ -603,10 +616,12 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
     uint16_t* dV = sV + (t & (kRing - 1)) * TILE;
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
-      const int row = min(key0 + it * KEYS_PER_LOAD, kend - 1) * kv_ss;
+      // Byte offsets below 2^32: the host bounds capacity * stride + D by 2^31 elements.
+      const uint32_t row = static_cast<uint32_t>(min(key0 + it * KEYS_PER_LOAD, kend - 1)) *
+                           static_cast<uint32_t>(kv_ss) * 2u;
       const int lds_off = (it * kThreads + wave * tv::kWave) * 8;
-      lds_copy16(kbase + row + ld_kch * 8, dK + lds_off);
-      lds_copy16(vbase + row + ld_vch * 8, dV + lds_off);
+      lds_copy16(kbase, row + static_cast<uint32_t>(ld_kch * 16), dK + lds_off);
+      lds_copy16(vbase, row + static_cast<uint32_t>(ld_vch * 16), dV + lds_off);
     }
   };
   // Tile t becomes readable: wait for all of this thread's copies, publish
