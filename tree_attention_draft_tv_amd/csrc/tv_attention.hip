@@ -1105,11 +1105,12 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParamsT
 // Merges the unit partials of pairs with more than one unit:
 // m* = max m_c, l* = sum l_c 2^(m_c - m*), O = sum O_c 2^(m_c - m*) / l*,
 // lse = (m* + log2 l*) ln 2. D/4 lanes share a packed row, four entries of
-// it each. The (m, l) of a row's units are contiguous (the split kernel
-// writes them as [row][unit] per pair), so every lane of the row reads them
-// all with a broadcast load and computes the weights itself: no cross-lane
-// reduction. Up to 16 units per round are requested at once. Q16: the
-// partial rows are int16 fixed point, entry = q * scale / 32767.
+// it each. The (m, l, scale) of a row's units are contiguous (the split
+// kernel writes them as [row][unit] per pair); lane k of the row reads unit
+// k's, the row max and the weighted sum of l are lane reductions, and each
+// unit's weight is broadcast to the row's lanes by a shuffle. Up to 16 units
+// per round are requested at once. Q16: the partial rows are int16 fixed
+// point, entry = q * scale / 32767.
 
 template <int D, bool Q16, bool PACKED>
 __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParamsT<PACKED> p) {
@@ -1154,14 +1155,18 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   float mstar = -INFINITY, lstar = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c0 = 0; c0 < nch; c0 += U) {
-    // Unconditional loads (units past the last re-read it, with weight 0),
-    // so that all of them are in flight together.
-    float4 ml[U];
+    // Lane k of the row loads the (m, l, scale) of unit c0 + k and computes
+    // its weight; the weights reach the other lanes by shuffles (one load
+    // of the unit records per lane instead of U broadcast loads). The
+    // partial rows are loaded unconditionally (units past the last re-read
+    // it, with weight 0), so that all of them are in flight together.
+    const int kl = sub & (U - 1);
+    const bool valid = sub < U && c0 + kl < nch;
+    const float4 mine = pml[min(c0 + kl, nch - 1)];
     float4 v[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const int kk = min(c0 + k, nch - 1);
-      ml[k] = pml[kk];
       const int64_t off = row_elem + kk * ustride;
       if constexpr (Q16) {
         const uint2 raw =
@@ -1174,25 +1179,28 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
         v[k] = *reinterpret_cast<const float4*>(p.part_o + off);
       }
     }
-    float m = mstar;
+    float m = valid ? mine.x : -INFINITY;
 #pragma unroll
-    for (int k = 0; k < U; ++k) m = fmaxf(m, ml[k].x);
-    // Units with finite m only (a live row's reference always is).
+    for (int o = 1; o < LPR; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, LPR));
+    m = fmaxf(m, mstar);  // units with finite m only (a live row's reference always is)
     const float sc = mstar == -INFINITY ? 0.f : exp2f(mstar - m);
-    lstar *= sc;
+    const float wk = valid ? exp2f(mine.x - m) : 0.f;
+    float ls = mine.y * wk;
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) ls += __shfl_xor(ls, o, LPR);
+    lstar = fmaf(lstar, sc, ls);
+    const float wo = Q16 ? wk * (mine.z * (1.f / 32767.f)) : wk;
     acc.x *= sc;
     acc.y *= sc;
     acc.z *= sc;
     acc.w *= sc;
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      const float wk = c0 + k < nch ? exp2f(ml[k].x - m) : 0.f;
-      lstar = fmaf(ml[k].y, wk, lstar);
-      const float wo = Q16 ? wk * (ml[k].z * (1.f / 32767.f)) : wk;
-      acc.x = fmaf(v[k].x, wo, acc.x);
-      acc.y = fmaf(v[k].y, wo, acc.y);
-      acc.z = fmaf(v[k].z, wo, acc.z);
-      acc.w = fmaf(v[k].w, wo, acc.w);
+      const float w = __shfl(wo, k, LPR);
+      acc.x = fmaf(v[k].x, w, acc.x);
+      acc.y = fmaf(v[k].y, w, acc.y);
+      acc.z = fmaf(v[k].z, w, acc.z);
+      acc.w = fmaf(v[k].w, w, acc.w);
     }
     mstar = m;
   }
