@@ -1104,19 +1104,33 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParamsT
 // ----------------------------------------------------- log-sum-exp merge ---
 // Merges the unit partials of pairs with more than one unit:
 // m* = max m_c, l* = sum l_c 2^(m_c - m*), O = sum O_c 2^(m_c - m*) / l*,
-// lse = (m* + log2 l*) ln 2. D/4 lanes share a packed row, four entries of
-// it each. The (m, l, scale) of a row's units are contiguous (the split
-// kernel writes them as [row][unit] per pair); lane k of the row reads unit
-// k's, the row max and the weighted sum of l are lane reductions, and each
-// unit's weight is broadcast to the row's lanes by a shuffle. Up to 16 units
-// per round are requested at once. Q16: the partial rows are int16 fixed
-// point, entry = q * scale / 32767.
+// lse = (m* + log2 l*) ln 2. The (m, l, scale) of a row's units are
+// contiguous (the split kernel writes them as [row][unit] per pair); lane k
+// of the row reads unit k's, the row max and the weighted sum of l are lane
+// reductions, and each unit's weight is broadcast to the row's lanes by a
+// shuffle. A lane holds eight entries of the row (one 16-byte load per unit)
+// with 16-bit partials, four with fp32 ones. Up to 16 units per round are
+// requested at once. Q16: the partial rows are int16 fixed point,
+// entry = q * scale / 32767.
+
+// Entries of a packed row per combine lane: eight 16-bit partials (one
+// 16-byte load per unit), or four fp32 ones.
+template <bool Q16>
+constexpr int combine_epl() {
+  return Q16 ? 8 : 4;
+}
+template <int D, bool Q16>
+constexpr int combine_rows_per_block() {
+  return kThreadsCombine / (D / combine_epl<Q16>());
+}
 
 template <int D, bool Q16, bool PACKED>
 __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParamsT<PACKED> p) {
-  constexpr int LPR = D / 4;                                     // lanes per packed row
-  constexpr int RPB = kThreadsCombine / LPR;                     // packed rows per block
-  constexpr int U = 16;
+  constexpr int EPL = combine_epl<Q16>();                        // entries per lane
+  constexpr int LPR = D / EPL;                                   // lanes per packed row
+  constexpr int RPB = combine_rows_per_block<D, Q16>();          // packed rows per block
+  constexpr int U = 16;                                          // units per round
+  constexpr int MPL = U > LPR ? U / LPR : 1;                     // unit records per lane
   const int bk = blockIdx.y;
   const int b = bk / p.Hkv;
   const int kvh = bk - b * p.Hkv;
@@ -1140,72 +1154,96 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   const int h = kvh * p.G + (r - i * p.G);
   if (i >= n && PACKED) return;  // packed: rows past n do not exist
   const int64_t orow = (seq_row0(p, b, start) + i) * p.Hq + h;
-  float4* dst = reinterpret_cast<float4*>(p.out + orow * D) + sub;
+  float4* dst = reinterpret_cast<float4*>(p.out + orow * D + EPL * sub);
   if (i >= n) {
-    *dst = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int e = 0; e < EPL / 4; ++e) dst[e] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (sub == 0) p.lse[orow] = -INFINITY;
     return;
   }
   const int rg = r / p.rows_wg;
   const int rl = r - rg * p.rows_wg;
   const int64_t u0 = first + static_cast<int64_t>(kvh * p.RG + rg) * nch;
-  const int64_t row_elem = (u0 * p.rows_wg + rl) * D + 4 * sub;  // entry offset of unit 0
-  const int64_t ustride = static_cast<int64_t>(p.rows_wg) * D;    // entries between units
+  const int64_t row_elem = (u0 * p.rows_wg + rl) * D + EPL * sub;  // entry offset of unit 0
+  const int64_t ustride = static_cast<int64_t>(p.rows_wg) * D;      // entries between units
   const float4* pml = p.part_ml + u0 * p.rows_wg + static_cast<int64_t>(rl) * nch;
   float mstar = -INFINITY, lstar = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
   for (int c0 = 0; c0 < nch; c0 += U) {
-    // Lane k of the row loads the (m, l, scale) of unit c0 + k and computes
-    // its weight; the weights reach the other lanes by shuffles (one load
-    // of the unit records per lane instead of U broadcast loads). The
-    // partial rows are loaded unconditionally (units past the last re-read
-    // it, with weight 0), so that all of them are in flight together.
-    const int kl = sub & (U - 1);
-    const bool valid = sub < U && c0 + kl < nch;
-    const float4 mine = pml[min(c0 + kl, nch - 1)];
-    float4 v[U];
+    // Lane k of the row loads the (m, l, scale) of unit c0 + k (and of
+    // c0 + k + LPR ... when a round has more units than the row has lanes)
+    // and computes its weight; the weights reach the other lanes by
+    // shuffles. The partial rows are loaded unconditionally (units past the
+    // last re-read it, with weight 0), so that all of them are in flight
+    // together.
+    float4 mine[MPL];
+    bool valid[MPL];
+#pragma unroll
+    for (int j = 0; j < MPL; ++j) {
+      const int kl = sub + j * LPR;
+      valid[j] = kl < U && c0 + kl < nch;
+      mine[j] = pml[min(c0 + kl, nch - 1)];
+    }
+    using Raw = typename std::conditional<Q16, uint4, float4>::type;
+    Raw v[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const int kk = min(c0 + k, nch - 1);
       const int64_t off = row_elem + kk * ustride;
-      if constexpr (Q16) {
-        const uint2 raw =
-            *reinterpret_cast<const uint2*>(reinterpret_cast<const int16_t*>(p.part_o) + off);
-        v[k] = make_float4(static_cast<float>(static_cast<int16_t>(raw.x & 0xFFFFu)),
-                           static_cast<float>(static_cast<int16_t>(raw.x >> 16)),
-                           static_cast<float>(static_cast<int16_t>(raw.y & 0xFFFFu)),
-                           static_cast<float>(static_cast<int16_t>(raw.y >> 16)));
-      } else {
+      if constexpr (Q16)
+        v[k] = *reinterpret_cast<const uint4*>(reinterpret_cast<const int16_t*>(p.part_o) + off);
+      else
         v[k] = *reinterpret_cast<const float4*>(p.part_o + off);
-      }
     }
-    float m = valid ? mine.x : -INFINITY;
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < MPL; ++j) m = fmaxf(m, valid[j] ? mine[j].x : -INFINITY);
 #pragma unroll
     for (int o = 1; o < LPR; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, LPR));
     m = fmaxf(m, mstar);  // units with finite m only (a live row's reference always is)
     const float sc = mstar == -INFINITY ? 0.f : exp2f(mstar - m);
-    const float wk = valid ? exp2f(mine.x - m) : 0.f;
-    float ls = mine.y * wk;
+    float wo[MPL];
+    float ls = 0.f;
+#pragma unroll
+    for (int j = 0; j < MPL; ++j) {
+      const float wk = valid[j] ? exp2f(mine[j].x - m) : 0.f;
+      ls = fmaf(mine[j].y, wk, ls);
+      wo[j] = Q16 ? wk * (mine[j].z * (1.f / 32767.f)) : wk;
+    }
 #pragma unroll
     for (int o = 1; o < LPR; o <<= 1) ls += __shfl_xor(ls, o, LPR);
     lstar = fmaf(lstar, sc, ls);
-    const float wo = Q16 ? wk * (mine.z * (1.f / 32767.f)) : wk;
-    acc.x *= sc;
-    acc.y *= sc;
-    acc.z *= sc;
-    acc.w *= sc;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= sc;
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      const float w = __shfl(wo, k, LPR);
-      acc.x = fmaf(v[k].x, w, acc.x);
-      acc.y = fmaf(v[k].y, w, acc.y);
-      acc.z = fmaf(v[k].z, w, acc.z);
-      acc.w = fmaf(v[k].w, w, acc.w);
+      const float w = __shfl(wo[k / LPR], k % LPR, LPR);
+      float x[EPL];
+      if constexpr (Q16) {
+        const uint32_t q[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = static_cast<float>(static_cast<int16_t>(q[e] & 0xFFFFu));
+          x[2 * e + 1] = static_cast<float>(static_cast<int16_t>(q[e] >> 16));
+        }
+      } else {
+        x[0] = v[k].x;
+        x[1] = v[k].y;
+        x[2] = v[k].z;
+        x[3] = v[k].w;
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(x[e], w, acc[e]);
     }
     mstar = m;
   }
   const float inv = 1.f / lstar;
-  *dst = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+#pragma unroll
+  for (int e = 0; e < EPL / 4; ++e)
+    dst[e] = make_float4(acc[4 * e] * inv, acc[4 * e + 1] * inv, acc[4 * e + 2] * inv,
+                         acc[4 * e + 3] * inv);
   if (sub == 0) p.lse[orow] = (mstar + __log2f(lstar)) * kLn2;
 }
 
@@ -1306,14 +1344,17 @@ void launch_all(const AttnParams& p0, int in_dtype, bool combine, hipStream_t st
   } else
     hipLaunchKernelGGL((attn_split_f32_kernel<D, PACKED>), grid, dim3(kThreadsF32), 0, stream, p);
   if (combine) {
-    const dim3 cgrid((p.R + kThreadsCombine / (D / 4) - 1) / (kThreadsCombine / (D / 4)),
-                     p.B * p.Hkv);
-    if (in_dtype == TV_BF16 && p.parts == 1)
-      hipLaunchKernelGGL((attn_combine_kernel<D, true, PACKED>), cgrid, dim3(kThreadsCombine), 0,
+    if (in_dtype == TV_BF16 && p.parts == 1) {
+      constexpr int rpb = combine_rows_per_block<D, true>();
+      hipLaunchKernelGGL((attn_combine_kernel<D, true, PACKED>),
+                         dim3((p.R + rpb - 1) / rpb, p.B * p.Hkv), dim3(kThreadsCombine), 0,
                          stream, p);
-    else
-      hipLaunchKernelGGL((attn_combine_kernel<D, false, PACKED>), cgrid, dim3(kThreadsCombine), 0,
+    } else {
+      constexpr int rpb = combine_rows_per_block<D, false>();
+      hipLaunchKernelGGL((attn_combine_kernel<D, false, PACKED>),
+                         dim3((p.R + rpb - 1) / rpb, p.B * p.Hkv), dim3(kThreadsCombine), 0,
                          stream, p);
+    }
   }
 }
 
