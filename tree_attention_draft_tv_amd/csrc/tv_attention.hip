@@ -88,7 +88,8 @@ struct AttnParams {
   float* out;
   float* lse;
   int32_t* sched;   // [0] keys per unit, [1 + b] first unit of sequence b
-  float* part_o;    // [unit][rows_wg][D], un-normalised: fp32, or int16 fixed point (q16)
+  float* part_o;    // [unit][rows_wg][D], un-normalised: fp32 in d order, or int16 fixed
+                    // point (q16) with each row as [g][dt][e] (d = 16 dt + 4 g + e)
   float4* part_ml;  // per pair [rows_wg][unit of the pair]: (reference max in log2 units, sum,
                     // int16 scale, 0)
   int32_t* row_status;
@@ -934,16 +935,21 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
     } else {
       const int64_t prow = static_cast<int64_t>(u) * p.rows_wg + (r - rg * kRowsWG);
       if constexpr (kQ16) {
-        int16_t* dst = reinterpret_cast<int16_t*>(p.part_o) + prow * D;
+        // Row layout [g][dt][e] (the lane's 4 DT entries contiguous: 16-byte
+        // stores); entry (g, dt, e) is d = 16 dt + 4 g + e.
+        int16_t* dst = reinterpret_cast<int16_t*>(p.part_o) + prow * D + g * (4 * DT);
         const float qs = amax[rt] > 0.f ? 32767.f / amax[rt] : 0.f;
+        auto pack2 = [&](float a, float c) __attribute__((always_inline)) {
+          return static_cast<uint32_t>(static_cast<uint16_t>(__float2int_rn(a * qs))) |
+                 (static_cast<uint32_t>(static_cast<uint16_t>(__float2int_rn(c * qs))) << 16);
+        };
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const f32x4_t v = o[dt][rt];
-          const uint32_t q0 = static_cast<uint16_t>(__float2int_rn(v[0] * qs));
-          const uint32_t q1 = static_cast<uint16_t>(__float2int_rn(v[1] * qs));
-          const uint32_t q2 = static_cast<uint16_t>(__float2int_rn(v[2] * qs));
-          const uint32_t q3 = static_cast<uint16_t>(__float2int_rn(v[3] * qs));
-          *reinterpret_cast<uint2*>(dst + 16 * dt + 4 * g) = make_uint2(q0 | (q1 << 16), q2 | (q3 << 16));
+        for (int dp = 0; dp < DT / 2; ++dp) {
+          const f32x4_t v0 = o[2 * dp][rt];
+          const f32x4_t v1 = o[2 * dp + 1][rt];
+          *reinterpret_cast<uint4*>(dst + 8 * dp) =
+              make_uint4(pack2(v0[0], v0[1]), pack2(v0[2], v0[3]), pack2(v1[0], v1[1]),
+                         pack2(v1[2], v1[3]));
         }
       } else {
         float* dst = p.part_o + prow * D;
@@ -1154,10 +1160,23 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   const int h = kvh * p.G + (r - i * p.G);
   if (i >= n && PACKED) return;  // packed: rows past n do not exist
   const int64_t orow = (seq_row0(p, b, start) + i) * p.Hq + h;
-  float4* dst = reinterpret_cast<float4*>(p.out + orow * D + EPL * sub);
+  // Output entries of this lane, four per float4: with 16-bit partials the
+  // lane's eight entries are (g, dt = 2 dp and 2 dp + 1, e) of the split's
+  // row layout [g][dt][e], i.e. d = 16 dt + 4 g + e; fp32 partials are in
+  // plain d order.
+  float4* dst[EPL / 4];
+  if constexpr (Q16) {
+    constexpr int HALF = D / 32;  // dt pairs per g
+    const int g = sub / HALF;
+    const int dp = sub - g * HALF;
+    dst[0] = reinterpret_cast<float4*>(p.out + orow * D + 32 * dp + 4 * g);
+    dst[1] = reinterpret_cast<float4*>(p.out + orow * D + 32 * dp + 16 + 4 * g);
+  } else {
+    dst[0] = reinterpret_cast<float4*>(p.out + orow * D + EPL * sub);
+  }
   if (i >= n) {
 #pragma unroll
-    for (int e = 0; e < EPL / 4; ++e) dst[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int e = 0; e < EPL / 4; ++e) *dst[e] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (sub == 0) p.lse[orow] = -INFINITY;
     return;
   }
@@ -1242,8 +1261,8 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   const float inv = 1.f / lstar;
 #pragma unroll
   for (int e = 0; e < EPL / 4; ++e)
-    dst[e] = make_float4(acc[4 * e] * inv, acc[4 * e + 1] * inv, acc[4 * e + 2] * inv,
-                         acc[4 * e + 3] * inv);
+    *dst[e] = make_float4(acc[4 * e] * inv, acc[4 * e + 1] * inv, acc[4 * e + 2] * inv,
+                          acc[4 * e + 3] * inv);
   if (sub == 0) p.lse[orow] = (mstar + __log2f(lstar)) * kLn2;
 }
 
@@ -1296,7 +1315,8 @@ bool valid_sizes(int B, int T, int Hq, int Hkv, int D, int max_ctx, int chunk_ke
 }
 
 // Workspace layout: the schedule table ((1 + B) int32), then partial O
-// [unit][rows_wg][D] (fp32, or int16 fixed point in the same space), then
+// [unit][rows_wg][D] (fp32, or int16 fixed point in the same space, each
+// row in the split lanes' order), then
 // (m, l, scale, 0) per pair as [rows_wg][unit of the pair]. Sized for the larger
 // of the bf16 (256 rows per unit) and fp32 (64 rows per unit) kernels. No
 // workspace when every pair is a single unit (written directly).
