@@ -957,3 +957,39 @@ def test_attention_packed_more_than_64_sequences():
         if st_ref[b] == 0 and n:
             s0 = int(start[b])
             assert np.array_equal(o[s0:s0 + n].view(np.uint32), o_pad[b, :n].view(np.uint32)), b
+
+
+# ----------------------------------------------------------- largest trees ---
+
+@pytest.mark.parametrize("dtype,D,chunk", [("bf16", 128, 0), ("bf16", 64, 64), ("f32", 128, 0),
+                                           ("f32", 64, 256)])
+def test_attention_largest_tree_and_group(dtype, D, chunk):
+    # T = TV_MAX_TREE rows and G = TV_MAX_GROUP query heads per KV head:
+    # 2048 packed rows per (sequence, KV head), the last one the edge of the
+    # row -> node multiplier; several row groups per pair; a full, a partial
+    # and a root-only tree over ragged contexts (one empty).
+    w = make_custom(501 + D, 3, 16, 1, D, 50, dtype, [700, 0, 129], 127,
+                    n_nodes=[128, 100, 1], max_depth=40, trie_tokens=False)
+    assert w.T == tv.TV_MAX_TREE and w.Hq // w.Hkv == tv.TV_MAX_GROUP
+    d = upload(w)
+    mask = _mask_check(w, d)
+    got = run_attention(w, d, mask, chunk_keys=chunk)
+    tol = bf16_p_bound(w) if dtype == "bf16" else 2e-3
+    check_attention(w, got, oracle_attention(w), atol_out=tol)
+
+
+def test_greedy_largest_tree():
+    w = make_custom(611, 3, 2, 1, 64, 1000, "bf16", [4, 4, 4], 127, n_nodes=[128, 57, 1],
+                    max_depth=40, plant_depth=4)
+    d = upload(w)
+    check_greedy(run_greedy(d), oracle.accept_greedy(w.logits, w.tokens, w.parent, w.n_nodes))
+
+
+def test_sample_largest_tree():
+    w = make_custom(612, 3, 2, 1, 64, 300, "bf16", [4, 4, 4], 127, n_nodes=[128, 90, 1],
+                    max_depth=40, mode="sample", temperature=0.9)
+    d = upload(w)
+    got = run_sample(w, d)
+    want = oracle.accept_sample(w.logits, w.temperature, w.qdraft, w.u, w.tokens, w.parent,
+                                w.n_nodes)
+    check_sample(w, got, want)
