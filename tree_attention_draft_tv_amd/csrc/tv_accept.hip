@@ -601,13 +601,17 @@ __global__ __launch_bounds__(kWalkThreads) void sample_walk_one_kernel(
     return hi ? 64 + __ffsll(hi) - 1 : n;
   };
   int c = next_child(1, 0);
+  // rv holds this thread's entries of r (times inv when held >= 0); after a
+  // rejection with a positive sum they stay in registers (in_regs), so the
+  // next test reloads nothing but q_c's row.
+  double rv[kRegSlots];
+  bool in_regs = false;
   while (c < n) {
     const int x = sh.tok[c];
     // The whole pass's loads go out before the test, which the owner of x
     // runs on its own copies.
-    double rv[kRegSlots];
     float qv[kRegSlots];
-    load_r(rv);
+    if (!in_regs) load_r(rv);
     load_blocks(q + (rbase + __builtin_amdgcn_readfirstlane(c)) * qstride, V, qv);
     if (tid == (x & (kWalkThreads - 1))) {
       const int ks = x / kWalkThreads;
@@ -630,12 +634,14 @@ __global__ __launch_bounds__(kWalkThreads) void sample_walk_one_kernel(
       cur = c;
       held = -1;
       inv = 1.0;
+      in_regs = false;
       c = next_child(c + 1, cur);
       __syncthreads();
       continue;
     }
     // Rejected: r <- max(r inv - q_c, 0) into the free buffer, inv <- 1 /
-    // its sum; a zero sum keeps the old r.
+    // its sum; a zero sum keeps the old r (reloaded from where it was, as
+    // the registers now hold zeros).
     const int dst = held == 0 ? 1 : 0;
     double part_sum = 0.0;
 #pragma unroll
@@ -650,6 +656,7 @@ __global__ __launch_bounds__(kWalkThreads) void sample_walk_one_kernel(
       held = dst;
       inv = 1.0 / tot;
     }
+    in_regs = tot > 0.0;
     c = next_child(c + 1, cur);
   }
 
@@ -658,8 +665,7 @@ __global__ __launch_bounds__(kWalkThreads) void sample_walk_one_kernel(
   // per-(slot, wave) sums; (2) wave 0 scans the 512 sums in index order and
   // finds the first block whose running sum passes the threshold; (3) that
   // block's wave scans its 64 entries from the block's starting sum.
-  double rv[kRegSlots];
-  load_r(rv);
+  if (!in_regs) load_r(rv);
   {
     constexpr int H = kRegSlots / 2;
     double a[H];
