@@ -520,7 +520,8 @@ def test_linear_rows_batch_invariant():
                           full)
 
 
-@pytest.mark.parametrize("M,K,N", [(9, 64, 64), (100, 448, 320), (264, 3584, 1024)])
+@pytest.mark.parametrize("M,K,N", [(9, 64, 64), (100, 448, 320), (264, 3584, 1024),
+                                   (264, 3584, 18944)])
 def test_linear_swiglu_rows(M, K, N):
     rng = np.random.default_rng(7 * M + K)
     x, xb = _bf16_dev(rng.normal(size=(M, K)))
