@@ -297,7 +297,9 @@ def main():
     timed = lambda fn: time_calls(torch, fn, reps)
 
     t_mask = timed(do_mask)
-    t_attn = timed(do_attention)
+    # Attention: 10 timed replays of 20 calls (200 calls after the warm-up),
+    # reported as the mean and the spread of the replay averages.
+    t_attn, attn_rounds = time_calls(torch, do_attention, 20, rounds=10)
     t_acc = timed(do_accept)
 
     ms_per_step = wall / steps * 1e3
@@ -341,6 +343,8 @@ def main():
             "traffic": traffic,
             "alg_bytes_per_launch": a_bytes,
             "avg_launch_us": round(t_attn * 1e6, 3),
+            "launch_us_p10_p50_p90": [round(float(np.percentile(attn_rounds, q)) * 1e6, 3)
+                                      for q in (10, 50, 90)],
         },
         "kernels": {
             "mask_us": round(t_mask * 1e6, 3),
@@ -401,11 +405,13 @@ def projections_secondary(tv, torch, dev, w, args):
                                "torch_matmul_silu_mul_us": round(t_ffn_ref * 1e6, 3)}}
 
 
-def time_calls(torch, fn, reps):
+def time_calls(torch, fn, reps, rounds=1):
     """Average GPU time of fn(i) over `reps` back-to-back calls. The calls are
     captured once in a HIP graph and replayed between two events, so that
     the host's launch path (~10 us per call through the binding) does not
-    pace kernels shorter than it; eager launches if capture fails."""
+    pace kernels shorter than it; eager launches if capture fails. With
+    rounds > 1 the replay is timed that many times and (mean, [per-round
+    averages]) is returned."""
     for i in range(3):
         fn(i)
     torch.cuda.synchronize()
@@ -421,15 +427,20 @@ def time_calls(torch, fn, reps):
     except RuntimeError:
         graph = None
         torch.cuda.synchronize()
-    e0.record()
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(reps):
-            fn(i)
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e-3 / reps
+    per_round = []
+    for _ in range(rounds):
+        e0.record()
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(reps):
+                fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        per_round.append(e0.elapsed_time(e1) * 1e-3 / reps)
+    if rounds == 1:
+        return per_round[0]
+    return sum(per_round) / rounds, per_round
 
 
 def commit_secondary(tv, torch, dev, w, s, acc_out, args):
