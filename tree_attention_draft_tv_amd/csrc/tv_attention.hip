@@ -808,21 +808,45 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
       if (need_ref) take_reference(sa);
       need_ref = false;
       int t = 0;
+      if constexpr (PARTS == 1) {
+        // Two sub-blocks of P in flight: each step issues the S^T MFMAs of
+        // the next sub-block and the P.V MFMAs of the previous one beside
+        // the softmax of the current one, so the matrix cores have twice as
+        // much independent work to overlap with the VALU.
+        bf16x8_t pa[PARTS][kRT];
+        s_block(0, 1, sb);
+        softmax_block(sa, pb);  // P of sub-block 0
 #pragma unroll 1
-      for (; t + 1 < nfull; ++t) {
+        for (; t + 1 < nfull; ++t) {
+          // Here pb = P of (t, 0), sb = S of (t, 1).
+          enter_tile(t + 1);
+          s_block(t + 1, 0, sa);
+          pv_block(t, 0, pb);
+          softmax_block(sb, pa);
+          s_block(t + 1, 1, sb);
+          pv_block(t, 1, pa);
+          softmax_block(sa, pb);
+        }
+        pv_block(t, 0, pb);
+        softmax_block(sb, pa);
+        pv_block(t, 1, pa);
+      } else {
+#pragma unroll 1
+        for (; t + 1 < nfull; ++t) {
+          s_block(t, 1, sb);
+          softmax_block(sa, pb);
+          pv_block(t, 0, pb);
+          enter_tile(t + 1);
+          s_block(t + 1, 0, sa);
+          softmax_block(sb, pb);
+          pv_block(t, 1, pb);
+        }
         s_block(t, 1, sb);
         softmax_block(sa, pb);
         pv_block(t, 0, pb);
-        enter_tile(t + 1);
-        s_block(t + 1, 0, sa);
         softmax_block(sb, pb);
         pv_block(t, 1, pb);
       }
-      s_block(t, 1, sb);
-      softmax_block(sa, pb);
-      pv_block(t, 0, pb);
-      softmax_block(sb, pb);
-      pv_block(t, 1, pb);
     }
 #pragma unroll 1
     for (int t = nfull; t < ntile; ++t) {
