@@ -994,3 +994,18 @@ def test_sample_largest_tree():
     want = oracle.accept_sample(w.logits, w.temperature, w.qdraft, w.u, w.tokens, w.parent,
                                 w.n_nodes)
     check_sample(w, got, want)
+
+
+@pytest.mark.parametrize("D,parts", [(64, 1), (128, 1), (64, 2)])
+def test_attention_combine_many_rounds(D, parts):
+    # More than 16 units per pair (the combine's per-round batch): 64-key
+    # chunks over 1500- and 2100-key contexts give 24 and 33 units, so the
+    # merge runs two and three rounds; with D = 64 and one part a lane holds
+    # two unit records per round.
+    w = make_custom(701 + D + parts, 2, 8, 2, D, 50, "bf16", [1500, 2100], 20,
+                    n_nodes=[21, 13], trie_tokens=False)
+    d = upload(w)
+    mask = _mask_check(w, d)
+    got = run_attention(w, d, mask, chunk_keys=64, parts=parts)
+    tol = bf16_p_bound(w) if parts == 1 else 2e-3
+    check_attention(w, got, oracle_attention(w), atol_out=tol)
