@@ -31,6 +31,7 @@ import numpy as np  # noqa: E402
 
 METRIC = "verified draft nodes/sec + achieved HBM GB/s (B=8, 8k ctx, N=32 tree)"
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "tree_attention_draft_tv_amd", "csrc", "tv_attention.hip")
 
@@ -52,6 +53,8 @@ def parse():
                     help="skip the secondary sampling-acceptance measurement")
     ap.add_argument("--no-projections", action="store_true",
                     help="skip the few-row projection measurement")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the long-context (32768-key) attention measurement")
     ap.add_argument("--no-packed", action="store_true",
                     help="skip the packed-row attention and budget-controller measurement")
     ap.add_argument("--commit-layers", type=int, default=28,
@@ -367,6 +370,8 @@ def main():
     if not args.no_packed:
         res["packed_rows"] = packed_secondary(tv, torch, dev, w, sets, bufs, ws_attn, acc_out,
                                               t_attn, args)
+    if not args.no_long_context and args.config == "C3":
+        res["long_context"] = long_context_secondary(tv, torch, dev, args)
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
@@ -511,6 +516,38 @@ def packed_secondary(tv, torch, dev, w, sets, bufs, ws_attn, acc_out, t_padded, 
     return {"rows": rows, "padded_rows": w.B * w.T, "attention_us": round(t * 1e6, 3),
             "padded_attention_us": round(t_padded * 1e6, 3),
             "budget_controller_us": round(tc * 1e6, 3)}
+
+
+def long_context_secondary(tv, torch, dev, args):
+    """Tree attention at the long-context workload (one sequence, 32768
+    committed keys, 65-row tree): the compute-heavier shape, reported against
+    the bf16 MFMA peak beside its HBM fraction; warm (one input set)."""
+    from workloads import make_config
+
+    w = make_config("C4")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
+        torch.bfloat16).to(dev)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa: E731
+    q, k, v = bf(w.q), bf(w.k), bf(w.v)
+    ctx, n, par = i32(w.ctx_len), i32(w.n_nodes), i32(w.parent)
+    mask = tv.build_tree_mask(par, n)[0]
+    ws = torch.empty(max(1, tv.attention_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, w.max_ctx, 0)),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((w.B, w.T, w.Hq, w.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.T, w.Hq), dtype=torch.float32, device=dev)
+    st = torch.empty((w.B,), dtype=torch.int32, device=dev)
+
+    def call(i):
+        tv.tree_attention(q, k, v, ctx, n, mask, w.max_ctx, scale=float(w.scale), out=out,
+                          lse=lse, row_status=st, workspace=ws)
+
+    t = time_calls(torch, call, max(20, min(args.steps, 100)))
+    by, fl = attention_alg_bytes(w), attention_flops(w)
+    return {"workload": "C4: B=1, Hq/Hkv=28/4, D=128, ctx 32768, N=64 draft nodes (T=65)",
+            "attention_us": round(t * 1e6, 3), "alg_bytes": by, "flops": fl,
+            "GBps": round(by / t / 1e9, 1), "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4),
+            "TFLOPs": round(fl / t / 1e12, 1),
+            "mfma_frac": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def sampling_secondary(tv, torch, dev, args):
