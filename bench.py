@@ -161,7 +161,7 @@ def cpu_baseline(w, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
