@@ -191,15 +191,16 @@ __global__ __launch_bounds__(TV_MAX_TREE) void greedy_walk_kernel(
   ArgBest best{-INFINITY, 0x7fffffff};
   if (in_t) {
     // Rows past n were never written by the slice pass: read (in bounds) but
-    // unused. Clamped duplicates of the last slice never win a strict test.
+    // unused. Sixteen slices per round (one round up to V = 16 slices of
+    // 16384 entries, all requested together with the parent and token
+    // loads); clamped duplicates of the last slice never win a strict test.
     const ArgBest* pp = part + row * S;
-    best = pp[0];
-    for (int s0 = 1; s0 < S; s0 += 8) {
-      ArgBest o[8];
+    for (int s0 = 0; s0 < S; s0 += 16) {
+      ArgBest o[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) o[u] = pp[min(s0 + u, S - 1)];
+      for (int u = 0; u < 16; ++u) o[u] = pp[min(s0 + u, S - 1)];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 16; ++u)
         if (better(o[u].v, o[u].i, best.v, best.i)) best = o[u];
     }
   }
