@@ -291,24 +291,17 @@ __device__ int total_units(const P& p, int len0, int K) {
 template <class P>
 __device__ int choose_unit(const P& p, int len0) {
   if (p.kunit > 0) return p.kunit;
+  // Sequences in lanes (the first 64 from len0, later blocks from memory),
+  // reduced across the wave.
   int maxl = 0, keys = 0;
-  if (p.B <= 64) {
-    // Every length is in a lane of len0: read them as scalars.
-    for (int b = 0; b < p.B; ++b) {
-      const int L = __builtin_amdgcn_readlane(len0, b);
-      maxl = max(maxl, L);
-      keys += max(L, 0);
-    }
-  } else {
-    for (int b0 = 0; b0 < p.B; b0 += 64) {
-      const int L = block_len(p, b0, len0);
-      maxl = max(maxl, L);
-      keys += max(L, 0);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) maxl = max(maxl, __shfl_xor(maxl, o));
-    keys = wave_sum_i(keys);
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int L = block_len(p, b0, len0);
+    maxl = max(maxl, L);
+    keys += max(L, 0);
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) maxl = max(maxl, __shfl_xor(maxl, o));
+  keys = wave_sum_i(keys);
   // One unit per pair (L + kTreeExtra <= hi). Also the only choice when the
   // caller passed no workspace for partials.
   const int hi = max(kMinUnit, (maxl + kTreeExtra + 63) / 64 * 64);
@@ -320,24 +313,9 @@ __device__ int choose_unit(const P& p, int len0) {
   int lo = static_cast<int>((pair_keys + p.nw - 1) / p.nw);
   lo = max(kMinUnit, (lo + 63) / 64 * 64);
   if (lo >= hi) return hi;
-  if (p.B <= 64) {
-    // Lane j tries lo + 64 j: 64 candidate sizes per round, the smallest
-    // whose unit count fits is taken (the count only falls as K grows).
-    const int lane = threadIdx.x & 63;
-    const int64_t per = static_cast<int64_t>(p.Hkv) * p.RG;
-    for (int round = 0; round < 2; ++round) {
-      const int kc = lo + 64 * lane;
-      int64_t cnt = 0;
-      for (int b = 0; b < p.B; ++b) {
-        const int L = __builtin_amdgcn_readlane(len0, b);
-        if (L >= 0) cnt += L == 0 ? 1 : div_fast(L + kTreeExtra + kc - 1, kc);
-      }
-      const uint64_t fits = __ballot(kc <= hi && cnt * per <= p.nw);
-      if (fits) return lo + 64 * static_cast<int>(__builtin_ctzll(fits));
-      if (hi - lo <= 64 * 63) return hi;
-      lo += 64 * 64;
-    }
-  }
+  // Each candidate's unit count is one wave reduction over the sequences'
+  // lanes (no memory for the first 64): a few steps of 64 from the bound,
+  // then a bisection.
   for (int step = 0; step < 4 && lo < hi; ++step, lo += 64)
     if (total_units(p, len0, lo) <= p.nw) return lo;
   if (total_units(p, len0, hi) > p.nw) return hi;
