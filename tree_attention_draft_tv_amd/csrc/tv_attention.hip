@@ -332,32 +332,13 @@ __device__ int choose_unit(const P& p, int len0) {
 }
 
 // Unit u -> (b, kvh, rg, c) and the pair's unit count nch; false past the
-// last unit (wave-uniform; every lane must call).
+// last unit (wave-uniform; every lane must call). An inclusive scan of the
+// per-sequence unit counts over the lanes, 64 sequences per block, and a
+// ballot for the first sequence whose units reach past u.
 template <class P>
 __device__ bool decode_unit(const P& p, int len0, int K, int u, int& b, int& kvh, int& rg,
                             int& c, int& nch) {
   const int lane = threadIdx.x & 63;
-  if (p.B <= 64) {
-    // Lane b holds the unit count of sequence b; walk them as scalars.
-    const int cnt = units_of(p, len0, K);
-    int base = 0;
-    for (int bb = 0; bb < p.B; ++bb) {
-      const int cb = __builtin_amdgcn_readlane(cnt, bb);
-      if (u < base + cb) {
-        b = bb;
-        const int per_pair = cb / (p.Hkv * p.RG);
-        const int local = u - base;
-        nch = per_pair;
-        const int pair = local / per_pair;
-        c = local - pair * per_pair;
-        kvh = pair / p.RG;
-        rg = pair - kvh * p.RG;
-        return true;
-      }
-      base += cb;
-    }
-    return false;
-  }
   int base = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     const int cnt = units_of(p, block_len(p, b0, len0), K);
