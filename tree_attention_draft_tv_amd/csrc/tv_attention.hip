@@ -372,16 +372,6 @@ template <class P>
 __device__ void write_sched(const P& p, int len0, int K) {
   const int lane = threadIdx.x & 63;
   if (lane == 0) p.sched[0] = K;
-  if (p.B <= 64) {
-    const int cnt = units_of(p, len0, K);
-    int base = 0, first = 0;
-    for (int bb = 0; bb < p.B; ++bb) {
-      if (lane == bb) first = base;
-      base += __builtin_amdgcn_readlane(cnt, bb);
-    }
-    if (lane < p.B) p.sched[1 + lane] = first;
-    return;
-  }
   int base = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     const int cnt = units_of(p, block_len(p, b0, len0), K);
