@@ -17,6 +17,11 @@ Split-KV with a log-sum-exp combine reaches this same result up to rounding
 order, so the oracle is the definition itself: for each live (b, i, h) the
 scores s = scale * q . k over the visible keys, o = softmax(s) @ v and
 lse = ln sum exp(s) (natural log), evaluated as max + ln sum exp(s - max).
+
+A live row can see no key at all only through an explicit mask
+(:func:`masked_attention`) with an empty committed context; the pages never
+meet that case. Its sum over no keys is 0, so lse = ln 0 = -inf, and its
+output takes the padding value 0 (softmax over an empty set is undefined).
 """
 
 import numpy as np
@@ -170,10 +175,12 @@ def _attention(q, k, v, dtype, ctx_len, n_nodes, draft_keys, scale, max_ctx, kv_
                 qh = decode(q[b, :n, h, :], dtype)
                 s = sc * (qh @ K.T)
                 s = np.where(visible, s, -np.inf)
-                m = s.max(axis=1, keepdims=True)
-                w = np.exp(s - m)
+                seen = visible.any(axis=1)
+                m = np.where(seen, s.max(axis=1), 0.0)[:, None]
+                w = np.exp(s - m)  # exactly 0 on invisible keys
                 z = w.sum(axis=1)
-                out[b, :n, h, :] = (w @ Vv) / z[:, None]
-                lse[b, :n, h] = m[:, 0] + np.log(z)
+                zs = np.where(seen, z, 1.0)
+                out[b, :n, h, :] = np.where(seen[:, None], (w @ Vv) / zs[:, None], 0.0)
+                lse[b, :n, h] = np.where(seen, m[:, 0] + np.log(zs), -np.inf)
         status[b] = ROW_OK
     return out, lse, status

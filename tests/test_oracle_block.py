@@ -9,7 +9,9 @@ attention oracle, no GPU.
   in float64 over all ctx_len + n keys with no mask; causal block attention
   equals it with the causal offset mask (row i sees slots < ctx_len + i + 1)
   and equals tree attention of a chain tree;
-* status for n_nodes outside [0, T].
+* status for n_nodes outside [0, T];
+* a row that sees no key (explicit mask, empty context): out 0, lse -inf,
+  and the other rows equal SDPA over exactly their own visible keys.
 """
 
 import numpy as np
@@ -82,3 +84,28 @@ def test_status():
     m, pos, st = oracle.build_block_mask(np.array([5, -1, 2]), 4, oracle.BIDIRECTIONAL)
     assert st.tolist() == [oracle.ROW_NNODES, oracle.ROW_NNODES, 0]
     assert not m[:2].any() and (pos[:2] == -1).all()
+
+
+def test_row_without_visible_keys():
+    # Explicit masks over an empty committed context: row 0 sees nothing, row
+    # 35 sees only keys 33 and 35 (none of keys 0..31), row 36 sees every key.
+    w = make_custom(63, 1, 4, 2, 64, 50, "bf16", [0], 39, tree="chain", trie_tokens=False,
+                    padded_rows=[])
+    n = int(w.n_nodes[0])
+    assert n == 40 and int(w.ctx_len[0]) == 0
+    mask, _, _ = oracle.build_block_mask(w.n_nodes, w.T, oracle.CAUSAL)
+    mask[0, 0] = 0
+    mask[0, 35] = [0, (1 << 1) | (1 << 3)]
+    mask[0, 36] = [0xFFFFFFFF, 0xFF]
+    out, lse, st = oracle.masked_attention(w.q, w.k, w.v, w.dtype, w.ctx_len, w.n_nodes, mask,
+                                           w.scale)
+    assert not st.any()
+    assert np.all(out[0, 0] == 0.0) and np.all(lse[0, 0] == -np.inf)
+    qf, kf, vf = decode(w.q, w.dtype), decode(w.k, w.dtype), decode(w.v, w.dtype)
+    for i, keys in ((35, [33, 35]), (36, list(range(40))), (7, list(range(8)))):
+        for h in range(w.Hq):
+            g = h // w.G
+            ref = _sdpa(qf[0, i, h], kf[0, g, keys], vf[0, g, keys], float(w.scale))
+            assert np.abs(out[0, i, h] - ref).max() < 1e-12
+            s = float(w.scale) * (kf[0, g, keys] @ qf[0, i, h])
+            assert abs(lse[0, i, h] - (s.max() + np.log(np.exp(s - s.max()).sum()))) < 1e-12
