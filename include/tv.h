@@ -153,8 +153,10 @@ int tv_tree_attention_auto_chunk(int B, int T, int Hq, int Hkv, int max_ctx);
  *   out[b][i][h] = softmax(scale * q . k) @ v over the visible keys;
  *   lse[b][i][h] = natural log of sum over visible keys of exp(scale * q . k).
  * Padding rows (i >= n), padded sequences (n == 0) and sequences with a bad
- * status get out = 0 and lse = -inf. Cache slots >= L + n are never read, so
- * they may hold anything (NaN included). A padded sequence reads no KV.
+ * status get out = 0 and lse = -inf, and so does a live row that sees no key
+ * at all (possible only with a caller-built mask and L == 0: the sum over no
+ * keys is 0). Cache slots >= L + n are never read, so they may hold anything
+ * (NaN included). A padded sequence reads no KV.
  *
  *   q        [B][T][Hq][D] elements of in_dtype; element (b,i,h,d) at
  *            q + b*q_sb + i*q_st + h*q_sh + d (strides in elements)
@@ -166,18 +168,27 @@ int tv_tree_attention_auto_chunk(int B, int T, int Hq, int Hkv, int max_ctx);
  *   scale    softmax scale, finite and > 0 (1/sqrt(D) is the usual choice)
  *   in_dtype TV_F32 (fp32-faithful arithmetic) or TV_BF16 (bf16 matrix cores,
  *            fp32 accumulation)
+ *   out_dtype TV_F32 or TV_BF16: element type of out (bf16: the fp32 result
+ *            rounded to nearest even once); lse is always fp32
  *   probability_parts  1..3 (bf16 only): the probabilities enter the P.V
- *            product as a sum of that many bf16 terms (3 = fp32-faithful P).
- *            With 1, the per-unit partial outputs of split-KV are kept as
- *            16-bit fixed point against each row's largest magnitude, which
- *            adds at most max|v| / 65534 to each output entry; with 2 or 3
- *            they are kept in fp32
+ *            product as a sum of that many bf16 terms. 3 is the page's
+ *            setting: P is represented exactly (fp32-faithful) and the
+ *            split-KV partials stay fp32, so only fp32 rounding remains.
+ *            2 also keeps fp32 partials (P to 16 significant bits).
+ *            1 is a lossy fast mode: each P is rounded once to bf16
+ *            (relative error <= 2^-8) and the per-unit partial outputs are
+ *            kept as 16-bit fixed point against each row's largest
+ *            magnitude, so an output entry may be off by up to
+ *            (2^-8 + 2^-16) * max|v| over the row's visible values: within
+ *            2e-3 only while max|v| <= 0.5, and on long contexts, where
+ *            rounding errors of many probabilities cancel, typically far
+ *            better
  *   chunk_keys  keys per split-KV unit (multiple of 64, 64..65536), or 0 to
  *            let the device balance the units of the whole launch over its
  *            compute units from the actual lengths; results are bitwise
  *            independent of the other sequences of the batch for a fixed
  *            chunk_keys (with 0 they agree to rounding)
- *   out      float32 [B][T][Hq][D] contiguous; lse float32 [B][T][Hq]
+ *   out      [B][T][Hq][D] contiguous, out_dtype; lse float32 [B][T][Hq]
  *   workspace/ws_bytes  device scratch of at least
  *            tv_tree_attention_workspace_size(...) bytes, 256-byte aligned
  *            (may be NULL when that size is 0); contents need no initialisation
@@ -191,8 +202,8 @@ int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
                       const void* k, const void* v, int64_t kv_sb, int64_t kv_sh,
                       int64_t kv_ss, const int32_t* ctx_len, const int32_t* n_nodes,
                       const uint32_t* mask, int B, int T, int Hq, int Hkv, int D,
-                      int max_ctx, int kv_capacity, float scale, int in_dtype,
-                      int probability_parts, int chunk_keys, float* out, float* lse,
+                      int max_ctx, int kv_capacity, float scale, int in_dtype, int out_dtype,
+                      int probability_parts, int chunk_keys, void* out, float* lse,
                       void* workspace, size_t ws_bytes, int32_t* row_status,
                       hipStream_t stream);
 
@@ -207,7 +218,7 @@ int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
  *
  * Node i < n_nodes[b] of sequence b is packed row row_start[b] + i:
  *   q        [rows_total][Hq][D]; element (row,h,d) at q + row*q_st + h*q_sh + d
- *   out      float32 [rows_total][Hq][D] contiguous; lse float32 [rows_total][Hq]
+ *   out      [rows_total][Hq][D] contiguous, out_dtype; lse float32 [rows_total][Hq]
  *   row_start int32 [B]; the ranges [row_start[b], row_start[b] + n_nodes[b])
  *            must not overlap (not checked: overlapping rows race)
  * T is the query extent (the largest n_nodes the call accepts, as in the
@@ -225,9 +236,9 @@ int tv_tree_attention_packed(const void* q, int64_t q_st, int64_t q_sh, const vo
                              const int32_t* ctx_len, const int32_t* n_nodes,
                              const uint32_t* mask, const int32_t* row_start, int rows_total,
                              int B, int T, int Hq, int Hkv, int D, int max_ctx, int kv_capacity,
-                             float scale, int in_dtype, int probability_parts, int chunk_keys,
-                             float* out, float* lse, void* workspace, size_t ws_bytes,
-                             int32_t* row_status, hipStream_t stream);
+                             float scale, int in_dtype, int out_dtype, int probability_parts,
+                             int chunk_keys, void* out, float* lse, void* workspace,
+                             size_t ws_bytes, int32_t* row_status, hipStream_t stream);
 
 /*
  * Workspace (bytes) of tv_accept_greedy (mode 0) or tv_accept_sample
@@ -309,7 +320,12 @@ int tv_accept_sample(const float* logits, int64_t logits_row_stride, float tempe
  *   w  bf16 [N][K] (output features x input features, the layout of a
  *      PyTorch Linear weight), row stride w_stride (a multiple of 8, >= K)
  *   y  bf16 [M][N], row stride y_stride (a multiple of 4, >= N): each entry
- *      is the fp32 sum over k = 0..K-1 in that order, rounded to nearest even
+ *      is one fp32 accumulation over k, rounded to nearest even. K is walked
+ *      in increasing order, 32 products per matrix-core step
+ *      (v_mfma_f32_16x16x32_bf16, which sums its 32 products in the
+ *      hardware's own order before adding them to the running sum), so the
+ *      rounding order depends only on K, never on M, the row's place in the
+ *      batch or the tiling: a row's bits are batch-invariant
  * Constraints: K and N multiples of 64 (else TV_ERR_SHAPE),
  * 0 <= M <= 65536; pointers 16-byte aligned (else TV_ERR_ALIGN). Sized for a
  * few hundred rows; nothing is allocated.

@@ -70,13 +70,14 @@ def _attn(lib, **kw):
     a = dict(q=P, q_sb=8 * 33 * 28 * 128, q_st=28 * 128, q_sh=128, k=P, v=P2,
              kv_sb=4 * 4096 * 128, kv_sh=4096 * 128, kv_ss=128, ctx=P, n=P, mask=P,
              B=2, T=33, Hq=28, Hkv=4, D=128, max_ctx=4000, cap=4096, scale=0.088,
-             dtype=1, parts=1, chunk=0, out=P, lse=P, ws=P, ws_bytes=1 << 40, st=P)
+             dtype=1, out_dtype=0, parts=3, chunk=0, out=P, lse=P, ws=P, ws_bytes=1 << 40, st=P)
     a.update(kw)
     return lib.tv_tree_attention(a["q"], a["q_sb"], a["q_st"], a["q_sh"], a["k"], a["v"],
                                  a["kv_sb"], a["kv_sh"], a["kv_ss"], a["ctx"], a["n"], a["mask"],
                                  a["B"], a["T"], a["Hq"], a["Hkv"], a["D"], a["max_ctx"],
-                                 a["cap"], a["scale"], a["dtype"], a["parts"], a["chunk"],
-                                 a["out"], a["lse"], a["ws"], a["ws_bytes"], a["st"], STREAM)
+                                 a["cap"], a["scale"], a["dtype"], a["out_dtype"], a["parts"],
+                                 a["chunk"], a["out"], a["lse"], a["ws"], a["ws_bytes"], a["st"],
+                                 STREAM)
 
 
 def test_attention_validation(lib):
@@ -84,6 +85,7 @@ def test_attention_validation(lib):
     assert _attn(lib, mask=NULL) == -1
     assert _attn(lib, st=NULL) == -1
     assert _attn(lib, dtype=5) == -3
+    assert _attn(lib, out_dtype=2) == -3 and _attn(lib, out_dtype=-1) == -3
     assert _attn(lib, T=0) == -2
     assert _attn(lib, T=129) == -2
     assert _attn(lib, Hq=27) == -2                  # not a multiple of Hkv
@@ -104,14 +106,14 @@ def test_attention_validation(lib):
 def _attn_packed(lib, **kw):
     a = dict(q=P, q_st=28 * 128, q_sh=128, k=P, v=P2, kv_sb=4 * 4096 * 128, kv_sh=4096 * 128,
              kv_ss=128, ctx=P, n=P, mask=P, start=P, rows=100, B=2, T=33, Hq=28, Hkv=4, D=128,
-             max_ctx=4000, cap=4096, scale=0.088, dtype=1, parts=1, chunk=0, out=P, lse=P,
-             ws=P, ws_bytes=1 << 40, st=P)
+             max_ctx=4000, cap=4096, scale=0.088, dtype=1, out_dtype=1, parts=3, chunk=0, out=P,
+             lse=P, ws=P, ws_bytes=1 << 40, st=P)
     a.update(kw)
     return lib.tv_tree_attention_packed(
         a["q"], a["q_st"], a["q_sh"], a["k"], a["v"], a["kv_sb"], a["kv_sh"], a["kv_ss"],
         a["ctx"], a["n"], a["mask"], a["start"], a["rows"], a["B"], a["T"], a["Hq"], a["Hkv"],
-        a["D"], a["max_ctx"], a["cap"], a["scale"], a["dtype"], a["parts"], a["chunk"], a["out"],
-        a["lse"], a["ws"], a["ws_bytes"], a["st"], STREAM)
+        a["D"], a["max_ctx"], a["cap"], a["scale"], a["dtype"], a["out_dtype"], a["parts"],
+        a["chunk"], a["out"], a["lse"], a["ws"], a["ws_bytes"], a["st"], STREAM)
 
 
 def test_attention_packed_validation(lib):
@@ -120,6 +122,7 @@ def test_attention_packed_validation(lib):
     assert _attn_packed(lib, rows=-1) == -2
     assert _attn_packed(lib, T=129) == -2
     assert _attn_packed(lib, dtype=7) == -3
+    assert _attn_packed(lib, out_dtype=3) == -3
     assert _attn_packed(lib, q_st=28 * 128 + 4) == -4   # row stride not 16 bytes
     assert _attn_packed(lib, D=80) == -6
     assert _attn_packed(lib, ws=NULL, ws_bytes=0) == -5
@@ -210,8 +213,57 @@ def test_accept_workspace_size(lib):
 def test_python_binding_rejects_cpu_tensors():
     import torch
     parent = torch.zeros((1, 4), dtype=torch.int32)
-    with pytest.raises(tv.TVError):
+    with pytest.raises(tv.TVError, match="GPU"):
         tv.build_tree_mask(parent, torch.ones(1, dtype=torch.int32))
+
+
+def test_python_binding_rejects_wrong_shapes_before_launch():
+    # Shapes are checked before the device, so these raise on the host (the
+    # tensors are CPU tensors: a call that got as far as a launch would
+    # instead fail on the device check).
+    import torch
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)  # noqa: E731
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32)  # noqa: E731
+    B, T, Hq, Hkv, D, cap = 2, 9, 8, 2, 64, 128
+    q, k, v = f32(B, T, Hq, D), f32(B, Hkv, cap, D), f32(B, Hkv, cap, D)
+    mask = i32(B, T, 1)
+
+    def attn(**kw):
+        a = dict(ctx=i32(B), n=i32(B), mask=mask)
+        a.update(kw)
+        return tv.tree_attention(q, k, v, a.pop("ctx"), a.pop("n"), a.pop("mask"), 100, **a)
+
+    for kw, what in ((dict(ctx=i32(B + 1)), "ctx_len"), (dict(n=i32(1)), "n_nodes"),
+                     (dict(mask=i32(B, T, 2)), "mask"), (dict(out=f32(B, T, Hq, D + 1)), "out"),
+                     (dict(lse=f32(B, T)), "lse"), (dict(row_status=i32(B + 1)), "row_status")):
+        with pytest.raises(tv.TVError, match=what):
+            attn(**kw)
+    with pytest.raises(TypeError):
+        attn(out=torch.zeros((B, T, Hq, D), dtype=torch.float64))
+    with pytest.raises(TypeError):
+        attn(out_dtype=torch.float16)
+    with pytest.raises(tv.TVError, match="row_start"):
+        tv.tree_attention_packed(f32(20, Hq, D), k, v, i32(B), i32(B), mask, i32(B + 2), 100)
+    logits = f32(B, T, 50)
+    outs = (i32(B), i32(B, T), i32(B), torch.zeros((B, T), dtype=torch.uint8), i32(B))
+    with pytest.raises(tv.TVError, match="n_nodes"):
+        tv.accept_greedy(logits, i32(B, T), i32(B, T), i32(B + 1))
+    bad = (i32(B + 1),) + outs[1:]
+    with pytest.raises(tv.TVError, match="accept_len"):
+        tv.accept_greedy(logits, i32(B, T), i32(B, T), i32(B), outputs=bad)
+    bad = outs[:3] + (torch.zeros((B, T + 1), dtype=torch.uint8), outs[4])
+    with pytest.raises(tv.TVError, match="accept_mask"):
+        tv.accept_greedy(logits, i32(B, T), i32(B, T), i32(B), outputs=bad)
+    dec = torch.zeros((B, T), dtype=torch.int8)
+    with pytest.raises(tv.TVError, match="decision"):
+        tv.accept_sample(logits, 0.7, f32(B, T, 50), f32(B, T), i32(B, T), i32(B, T), i32(B),
+                         outputs=outs[:4] + (dec[:1], outs[4]))
+    with pytest.raises(tv.TVError, match="u"):
+        tv.accept_sample(logits, 0.7, f32(B, T, 50), f32(B, T + 1), i32(B, T), i32(B, T), i32(B))
+    with pytest.raises(tv.TVError, match="mask"):
+        tv.build_tree_mask(i32(B, T), i32(B), out=(i32(B, T, 2), i32(B, T), i32(B)))
+    with pytest.raises(tv.TVError, match="accept_len"):
+        tv.commit_accepted_kv(k, v, i32(B), i32(B), i32(B + 1), i32(B, T))
 
 
 def _commit(lib, **kw):

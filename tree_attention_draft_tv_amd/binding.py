@@ -45,10 +45,10 @@ SIGNATURES = {
     "tv_tree_attention_workspace_size": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "tv_tree_attention_auto_chunk": (_I, [_I, _I, _I, _I, _I]),
     "tv_tree_attention": (_I, [_P, _L, _L, _L, _P, _P, _L, _L, _L, _P, _P, _P,
-                               _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
+                               _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I,
                                _P, _P, _P, _S, _P, _P]),
     "tv_tree_attention_packed": (_I, [_P, _L, _L, _P, _P, _L, _L, _L, _P, _P, _P, _P, _I,
-                                      _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
+                                      _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I,
                                       _P, _P, _P, _S, _P, _P]),
     "tv_adapt_tree_budget": (_I, [_P, _P, _P, _I, _F, _F, _I, _I, _P, _P, _P, _P, _P]),
     "tv_accept_workspace_size": (_S, [_I, _I, _I, _I]),
@@ -101,21 +101,43 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t: torch.Tensor, name: str, dtype, device=None):
+def _shape(t: torch.Tensor, name: str, dtype, shape=None, contiguous=False):
+    """Type, element type, shape and layout of an argument (no device check)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch tensor" % name)
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise TVError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if contiguous and not t.is_contiguous():
+        raise TVError("%s must be contiguous" % name)
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None, shape=None, contiguous=False):
+    """:func:`_shape`, then the device."""
+    _shape(t, name, dtype, shape, contiguous)
     if t.device.type != "cuda":
         raise TVError("%s must live on the GPU (got %s)" % (name, t.device))
     if device is not None and t.device != device:
         raise TVError("%s is on %s, expected %s" % (name, t.device, device))
 
 
+def _out_dtype(dtype):
+    if dtype == torch.float32:
+        return TV_F32
+    if dtype == torch.bfloat16:
+        return TV_BF16
+    raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+
+
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
     if nbytes == 0:
         return None, 0
     if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous():
+            raise TVError("workspace must be a contiguous tensor")
+        if workspace.device != device:
+            raise TVError("workspace is on %s, expected %s" % (workspace.device, device))
         if workspace.numel() * workspace.element_size() < nbytes:
             raise TVError("workspace too small: %d < %d bytes" %
                           (workspace.numel() * workspace.element_size(), nbytes))
@@ -131,12 +153,17 @@ def build_tree_mask(parent: torch.Tensor, n_nodes: torch.Tensor,
     """Ancestor bitmasks (int32 storage of uint32 words), depths, row status."""
     lib = load()
     dev = parent.device
-    _need(parent, "parent", torch.int32)
-    _need(n_nodes, "n_nodes", torch.int32, dev)
-    if parent.dim() != 2 or not parent.is_contiguous():
+    if not isinstance(parent, torch.Tensor) or parent.dim() != 2:
         raise TVError("parent must be a contiguous [B, T] tensor")
     B, T = parent.shape
     W = (T + 31) // 32
+    checks = [(parent, "parent", (B, T)), (n_nodes, "n_nodes", (B,))]
+    if out is not None:
+        checks += list(zip(out, ("mask", "depth", "row_status"), ((B, T, W), (B, T), (B,))))
+    for t, name, shape in checks:
+        _shape(t, name, torch.int32, shape, contiguous=True)
+    for t, name, _ in checks:
+        _need(t, name, torch.int32, dev)
     if out is None:
         mask = torch.empty((B, T, W), dtype=torch.int32, device=dev)
         depth = torch.empty((B, T), dtype=torch.int32, device=dev)
@@ -154,11 +181,18 @@ def build_block_mask(n_nodes: torch.Tensor, T: int, mode: int = TV_BLOCK_CAUSAL,
     the layout of :func:`build_tree_mask`: (mask, position, row_status)."""
     lib = load()
     dev = n_nodes.device
-    _need(n_nodes, "n_nodes", torch.int32)
-    if n_nodes.dim() != 1 or not n_nodes.is_contiguous():
+    if not isinstance(n_nodes, torch.Tensor) or n_nodes.dim() != 1:
         raise TVError("n_nodes must be a contiguous [B] tensor")
     B = n_nodes.shape[0]
+    T = int(T)
     W = (T + 31) // 32
+    checks = [(n_nodes, "n_nodes", (B,))]
+    if out is not None:
+        checks += list(zip(out, ("mask", "position", "row_status"), ((B, T, W), (B, T), (B,))))
+    for t, name, shape in checks:
+        _shape(t, name, torch.int32, shape, contiguous=True)
+    for t, name, _ in checks:
+        _need(t, name, torch.int32, dev)
     if out is None:
         mask = torch.empty((B, T, W), dtype=torch.int32, device=dev)
         pos = torch.empty((B, T), dtype=torch.int32, device=dev)
@@ -183,62 +217,87 @@ def auto_chunk(B, T, Hq, Hkv, max_ctx) -> int:
     return int(load().tv_tree_attention_auto_chunk(B, T, Hq, Hkv, max_ctx))
 
 
-def tree_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ctx_len: torch.Tensor,
-                   n_nodes: torch.Tensor, mask: torch.Tensor, max_ctx: int,
-                   scale: Optional[float] = None, probability_parts: int = 1,
-                   chunk_keys: int = 0, out: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None, row_status: Optional[torch.Tensor] = None,
-                   workspace: Optional[torch.Tensor] = None):
-    """Tree-masked split-KV GQA attention.
-
-    q: [B, T, Hq, D]; k, v: [B, Hkv, kv_capacity, D] (float32 or bfloat16,
-    D contiguous, any other strides); ctx_len, n_nodes: int32 [B];
-    mask: from :func:`build_tree_mask`. Returns (out float32 [B, T, Hq, D],
-    lse float32 [B, T, Hq], row_status int32 [B]).
-    """
-    lib = load()
-    dev = q.device
+def _attention_args(q, k, v, ctx_len, n_nodes, mask, B, T, lead, Hq, D, out_dtype, out, lse,
+                    row_status):
+    """Checks every attention argument (all shapes before any device) and
+    allocates the outputs not given: out [*lead, Hq, D] of out_dtype, lse
+    float32 [*lead, Hq], row_status int32 [B]. Returns (element type code,
+    out, lse, row_status)."""
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a torch tensor")
     if q.dtype == torch.bfloat16:
         dt = TV_BF16
     elif q.dtype == torch.float32:
         dt = TV_F32
     else:
         raise TypeError("q must be float32 or bfloat16")
-    _need(q, "q", q.dtype)
-    _need(k, "k", q.dtype, dev)
-    _need(v, "v", q.dtype, dev)
-    _need(ctx_len, "ctx_len", torch.int32, dev)
-    _need(n_nodes, "n_nodes", torch.int32, dev)
-    _need(mask, "mask", torch.int32, dev)
-    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+    _out_dtype(out_dtype)
+    o_shape, l_shape = tuple(lead) + (Hq, D), tuple(lead) + (Hq,)
+    checks = [(ctx_len, "ctx_len", torch.int32, (B,)), (n_nodes, "n_nodes", torch.int32, (B,)),
+              (mask, "mask", torch.int32, (B, T, (T + 31) // 32)),
+              (out, "out", out_dtype, o_shape), (lse, "lse", torch.float32, l_shape),
+              (row_status, "row_status", torch.int32, (B,))]
+    _shape(k, "k", q.dtype)
+    _shape(v, "v", q.dtype)
+    for t, name, dtype, shape in checks:
+        if t is not None:
+            _shape(t, name, dtype, shape, contiguous=True)
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, q.dtype, dev)
+    for t, name, dtype, _ in checks:
+        if t is not None:
+            _need(t, name, dtype, dev)
+    if out is None:
+        out = torch.empty(o_shape, dtype=out_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty(l_shape, dtype=torch.float32, device=dev)
+    if row_status is None:
+        row_status = torch.empty((B,), dtype=torch.int32, device=dev)
+    return dt, out, lse, row_status
+
+
+def tree_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ctx_len: torch.Tensor,
+                   n_nodes: torch.Tensor, mask: torch.Tensor, max_ctx: int,
+                   scale: Optional[float] = None, probability_parts: int = 3,
+                   chunk_keys: int = 0, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, row_status: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None,
+                   out_dtype: torch.dtype = torch.float32):
+    """Tree-masked split-KV GQA attention.
+
+    q: [B, T, Hq, D]; k, v: [B, Hkv, kv_capacity, D] (float32 or bfloat16,
+    D contiguous, any other strides); ctx_len, n_nodes: int32 [B];
+    mask: from :func:`build_tree_mask`. ``probability_parts`` 3 (default)
+    keeps the probabilities fp32-faithful; 1 is the lossy fast mode described
+    in include/tv.h. Returns (out [B, T, Hq, D] of ``out_dtype`` (float32 or
+    bfloat16), lse float32 [B, T, Hq], row_status int32 [B]).
+    """
+    lib = load()
+    if not isinstance(q, torch.Tensor) or q.dim() != 4 or not isinstance(k, torch.Tensor) or \
+            k.dim() != 4 or not isinstance(v, torch.Tensor) or v.shape != k.shape:
         raise TVError("q must be [B, T, Hq, D] and k, v [B, Hkv, capacity, D]")
     B, T, Hq, D = q.shape
     _, Hkv, cap, Dk = k.shape
     if Dk != D or k.shape[0] != B:
         raise TVError("q and k disagree on B or D")
+    dt, out, lse, row_status = _attention_args(q, k, v, ctx_len, n_nodes, mask, B, T, (B, T),
+                                               Hq, D, out_dtype, out, lse, row_status)
+    dev = q.device
     if q.stride(3) != 1 or k.stride(3) != 1 or v.stride(3) != 1:
         raise TVError("the head dimension must be contiguous")
     if k.stride() != v.stride():
         raise TVError("k and v must share strides")
-    if not mask.is_contiguous() or tuple(mask.shape) != (B, T, (T + 31) // 32):
-        raise TVError("mask must be a contiguous [B, T, ceil(T/32)] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
-    if lse is None:
-        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
-    if row_status is None:
-        row_status = torch.empty((B,), dtype=torch.int32, device=dev)
-    if not out.is_contiguous() or not lse.is_contiguous():
-        raise TVError("out and lse must be contiguous")
+    odt = _out_dtype(out_dtype)
     nbytes = attention_workspace_size(B, T, Hq, Hkv, D, max_ctx, chunk_keys)
     ws, ws_bytes = _workspace(nbytes, dev, workspace)
     _check(lib.tv_tree_attention(
         _ptr(q), q.stride(0), q.stride(1), q.stride(2),
         _ptr(k), _ptr(v), k.stride(0), k.stride(1), k.stride(2),
         _ptr(ctx_len), _ptr(n_nodes), _ptr(mask),
-        B, T, Hq, Hkv, D, int(max_ctx), cap, float(scale), dt, int(probability_parts),
+        B, T, Hq, Hkv, D, int(max_ctx), cap, float(scale), dt, odt, int(probability_parts),
         int(chunk_keys), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _ptr(row_status),
         _stream(dev)), "tv_tree_attention")
     return out, lse, row_status
@@ -247,10 +306,11 @@ def tree_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ctx_len: t
 def tree_attention_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                           ctx_len: torch.Tensor, n_nodes: torch.Tensor, mask: torch.Tensor,
                           row_start: torch.Tensor, max_ctx: int, scale: Optional[float] = None,
-                          probability_parts: int = 1, chunk_keys: int = 0,
+                          probability_parts: int = 3, chunk_keys: int = 0,
                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                           row_status: Optional[torch.Tensor] = None,
-                          workspace: Optional[torch.Tensor] = None):
+                          workspace: Optional[torch.Tensor] = None,
+                          out_dtype: torch.dtype = torch.float32):
     """:func:`tree_attention` over packed query rows: node i of sequence b is
     row row_start[b] + i of q [rows, Hq, D], out [rows, Hq, D] and lse
     [rows, Hq]; the query extent T (largest n_nodes accepted) is the mask's
@@ -258,55 +318,34 @@ def tree_attention_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     Rows of no live sequence are left as they are (``out``/``lse`` given) or
     uninitialised. Returns (out, lse, row_status)."""
     lib = load()
-    dev = q.device
-    if q.dtype == torch.bfloat16:
-        dt = TV_BF16
-    elif q.dtype == torch.float32:
-        dt = TV_F32
-    else:
-        raise TypeError("q must be float32 or bfloat16")
-    _need(q, "q", q.dtype)
-    _need(k, "k", q.dtype, dev)
-    _need(v, "v", q.dtype, dev)
-    _need(ctx_len, "ctx_len", torch.int32, dev)
-    _need(n_nodes, "n_nodes", torch.int32, dev)
-    _need(mask, "mask", torch.int32, dev)
-    _need(row_start, "row_start", torch.int32, dev)
-    if q.dim() != 3 or k.dim() != 4 or v.shape != k.shape:
+    if not isinstance(q, torch.Tensor) or q.dim() != 3 or not isinstance(k, torch.Tensor) or \
+            k.dim() != 4 or not isinstance(v, torch.Tensor) or v.shape != k.shape:
         raise TVError("q must be [rows, Hq, D] and k, v [B, Hkv, capacity, D]")
     rows, Hq, D = q.shape
     B, Hkv, cap, Dk = k.shape
     if Dk != D:
         raise TVError("q and k disagree on D")
+    if not isinstance(mask, torch.Tensor) or mask.dim() != 3:
+        raise TVError("mask must be a contiguous [B, T, ceil(T/32)] tensor")
+    T = mask.shape[1]
+    _shape(row_start, "row_start", torch.int32, shape=(B,), contiguous=True)
+    dt, out, lse, row_status = _attention_args(q, k, v, ctx_len, n_nodes, mask, B, T, (rows,),
+                                               Hq, D, out_dtype, out, lse, row_status)
+    dev = q.device
+    _need(row_start, "row_start", torch.int32, dev)
     if q.stride(2) != 1 or k.stride(3) != 1 or v.stride(3) != 1:
         raise TVError("the head dimension must be contiguous")
     if k.stride() != v.stride():
         raise TVError("k and v must share strides")
-    if mask.dim() != 3 or mask.shape[0] != B or not mask.is_contiguous():
-        raise TVError("mask must be a contiguous [B, T, ceil(T/32)] tensor")
-    T = mask.shape[1]
-    if mask.shape[2] != (T + 31) // 32:
-        raise TVError("mask must be a contiguous [B, T, ceil(T/32)] tensor")
-    if tuple(row_start.shape) != (B,) or tuple(ctx_len.shape) != (B,) or \
-            tuple(n_nodes.shape) != (B,):
-        raise TVError("ctx_len, n_nodes and row_start must be [B]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((rows, Hq, D), dtype=torch.float32, device=dev)
-    if lse is None:
-        lse = torch.empty((rows, Hq), dtype=torch.float32, device=dev)
-    if row_status is None:
-        row_status = torch.empty((B,), dtype=torch.int32, device=dev)
-    if not out.is_contiguous() or not lse.is_contiguous() or \
-            tuple(out.shape) != (rows, Hq, D) or tuple(lse.shape) != (rows, Hq):
-        raise TVError("out and lse must be contiguous [rows, Hq, D] and [rows, Hq]")
+    odt = _out_dtype(out_dtype)
     nbytes = attention_workspace_size(B, T, Hq, Hkv, D, max_ctx, chunk_keys)
     ws, ws_bytes = _workspace(nbytes, dev, workspace)
     _check(lib.tv_tree_attention_packed(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k), _ptr(v), k.stride(0), k.stride(1),
         k.stride(2), _ptr(ctx_len), _ptr(n_nodes), _ptr(mask), _ptr(row_start), rows,
-        B, T, Hq, Hkv, D, int(max_ctx), cap, float(scale), dt, int(probability_parts),
+        B, T, Hq, Hkv, D, int(max_ctx), cap, float(scale), dt, odt, int(probability_parts),
         int(chunk_keys), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _ptr(row_status),
         _stream(dev)), "tv_tree_attention_packed")
     return out, lse, row_status
@@ -341,6 +380,8 @@ def adapt_tree_budget(accept_len: torch.Tensor, n_nodes: torch.Tensor,
         row_start = torch.empty((B,), dtype=torch.int32, device=dev)
     if rows_total is None:
         rows_total = torch.empty((1,), dtype=torch.int32, device=dev)
+    _need(row_start, "row_start", torch.int32, dev, shape=(B,), contiguous=True)
+    _need(rows_total, "rows_total", torch.int32, dev, shape=(1,), contiguous=True)
     _check(lib.tv_adapt_tree_budget(
         _ptr(accept_len), _ptr(n_nodes), _ptr(row_status), B, float(target), float(alpha),
         int(n_min), int(n_max), _ptr(ratio_ema), _ptr(budget), _ptr(row_start),
@@ -365,6 +406,25 @@ def _accept_outputs(B, T, dev):
             torch.empty((B,), dtype=torch.int32, device=dev))
 
 
+_ACCEPT_OUT = (("accept_len", torch.int32, 1), ("path", torch.int32, 2),
+               ("bonus", torch.int32, 1), ("accept_mask", torch.uint8, 2),
+               ("row_status", torch.int32, 1))
+
+
+def _check_accept_outputs(outs, B, T, dev, with_decision=False):
+    """Shapes and types of caller-given acceptance outputs; with dev, also
+    their device."""
+    spec = list(_ACCEPT_OUT)
+    if with_decision:
+        spec.insert(4, ("decision", torch.int8, 2))
+    if len(outs) != len(spec):
+        raise TVError("outputs must hold %d tensors" % len(spec))
+    for t, (name, dtype, nd) in zip(outs, spec):
+        _shape(t, name, dtype, shape=(B,) if nd == 1 else (B, T), contiguous=True)
+        if dev is not None:
+            _need(t, name, dtype, dev)
+
+
 def _check_logits(logits, name, dev):
     _need(logits, name, torch.float32, dev)
     if logits.dim() != 3 or logits.stride(2) != 1 or logits.stride(0) != logits.shape[1] * logits.stride(1):
@@ -377,14 +437,19 @@ def accept_greedy(logits: torch.Tensor, tokens: torch.Tensor, parent: torch.Tens
     """Greedy acceptance. Returns (accept_len, path, bonus, accept_mask, row_status)."""
     lib = load()
     dev = logits.device
-    stride = _check_logits(logits, "logits", dev)
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 3:
+        raise TVError("logits must be [B, T, V]")
     B, T, V = logits.shape
     for t, nm in ((tokens, "tokens"), (parent, "parent")):
+        _shape(t, nm, torch.int32, shape=(B, T), contiguous=True)
+    _shape(n_nodes, "n_nodes", torch.int32, shape=(B,), contiguous=True)
+    if outputs is not None:
+        _check_accept_outputs(outputs, B, T, None)
+    stride = _check_logits(logits, "logits", dev)
+    for t, nm in ((tokens, "tokens"), (parent, "parent"), (n_nodes, "n_nodes")):
         _need(t, nm, torch.int32, dev)
-        if tuple(t.shape) != (B, T) or not t.is_contiguous():
-            raise TVError("%s must be a contiguous [B, T] tensor" % nm)
-    _need(n_nodes, "n_nodes", torch.int32, dev)
     outs = outputs if outputs is not None else _accept_outputs(B, T, dev)
+    _check_accept_outputs(outs, B, T, dev)
     acc_len, path, bonus, amask, status = outs
     nbytes = accept_workspace_size(B, T, V, 0)
     ws, ws_bytes = _workspace(nbytes, dev, workspace)
@@ -404,23 +469,26 @@ def accept_sample(logits: torch.Tensor, temperature: float, q: torch.Tensor, u: 
     """
     lib = load()
     dev = logits.device
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 3:
+        raise TVError("logits must be [B, T, V]")
+    B, T, V = logits.shape
+    if not isinstance(q, torch.Tensor) or tuple(q.shape) != (B, T, V):
+        raise TVError("q must match logits' shape")
+    _shape(u, "u", torch.float32, shape=(B, T), contiguous=True)
+    for t, nm in ((tokens, "tokens"), (parent, "parent")):
+        _shape(t, nm, torch.int32, shape=(B, T), contiguous=True)
+    _shape(n_nodes, "n_nodes", torch.int32, shape=(B,), contiguous=True)
+    if outputs is not None:
+        _check_accept_outputs(outputs, B, T, None, with_decision=True)
     stride = _check_logits(logits, "logits", dev)
     qstride = _check_logits(q, "q", dev)
-    B, T, V = logits.shape
-    if tuple(q.shape) != (B, T, V):
-        raise TVError("q must match logits' shape")
-    _need(u, "u", torch.float32, dev)
-    if tuple(u.shape) != (B, T) or not u.is_contiguous():
-        raise TVError("u must be a contiguous [B, T] tensor")
-    for t, nm in ((tokens, "tokens"), (parent, "parent")):
-        _need(t, nm, torch.int32, dev)
-        if tuple(t.shape) != (B, T) or not t.is_contiguous():
-            raise TVError("%s must be a contiguous [B, T] tensor" % nm)
-    _need(n_nodes, "n_nodes", torch.int32, dev)
+    for t, nm in ((u, "u"), (tokens, "tokens"), (parent, "parent"), (n_nodes, "n_nodes")):
+        _need(t, nm, t.dtype, dev)
     if outputs is None:
         acc_len, path, bonus, amask, status = _accept_outputs(B, T, dev)
         decision = torch.empty((B, T), dtype=torch.int8, device=dev)
     else:
+        _check_accept_outputs(outputs, B, T, dev, with_decision=True)
         acc_len, path, bonus, amask, decision, status = outputs
     nbytes = accept_workspace_size(B, T, V, 1)
     ws, ws_bytes = _workspace(nbytes, dev, workspace)
@@ -448,13 +516,9 @@ def commit_accepted_kv(k: torch.Tensor, v: torch.Tensor, ctx_len: torch.Tensor,
     lib = load()
     dev = k.device
     sizes = {torch.bfloat16: 2, torch.float16: 2, torch.float32: 4}
-    if k.dtype not in sizes:
+    if not isinstance(k, torch.Tensor) or k.dtype not in sizes:
         raise TypeError("k must be bfloat16, float16 or float32")
-    _need(k, "k", k.dtype)
-    _need(v, "v", k.dtype, dev)
-    for t, name in ((ctx_len, "ctx_len"), (n_nodes, "n_nodes"), (accept_len, "accept_len"),
-                    (path, "path")):
-        _need(t, name, torch.int32, dev)
+    _shape(v, "v", k.dtype)
     if k.dim() == 4:
         layers, kk, vv = 1, k.unsqueeze(0), v.unsqueeze(0)
     elif k.dim() == 5:
@@ -466,13 +530,28 @@ def commit_accepted_kv(k: torch.Tensor, v: torch.Tensor, ctx_len: torch.Tensor,
     if kk.stride(4) != 1:
         raise TVError("the head dimension must be contiguous")
     _, B, Hkv, cap, D = kk.shape
-    if path.dim() != 2 or path.shape[0] != B or not path.is_contiguous():
+    if not isinstance(path, torch.Tensor) or path.dim() != 2 or path.shape[0] != B:
         raise TVError("path must be a contiguous [B, T] tensor")
     T = path.shape[1]
+    checks = [(ctx_len, "ctx_len", (B,)), (n_nodes, "n_nodes", (B,)),
+              (accept_len, "accept_len", (B,)), (path, "path", (B, T)),
+              (new_ctx_len, "new_ctx_len", (B,)), (row_status, "row_status", (B,))]
+    for t, name, shape in checks:
+        if t is not None:
+            _shape(t, name, torch.int32, shape, contiguous=True)
+    _need(k, "k", k.dtype)
+    _need(v, "v", k.dtype, dev)
+    for t, name, _ in checks:
+        if t is not None:
+            _need(t, name, torch.int32, dev)
     if new_ctx_len is None:
         new_ctx_len = torch.empty((B,), dtype=torch.int32, device=dev)
     if row_status is None:
         row_status = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(new_ctx_len, "new_ctx_len", torch.int32, dev, shape=(B,), contiguous=True)
+    _need(row_status, "row_status", torch.int32, dev, shape=(B,), contiguous=True)
+    if new_ctx_len.data_ptr() == ctx_len.data_ptr():
+        raise TVError("new_ctx_len must not be ctx_len itself")
     _check(lib.tv_commit_accepted_kv(
         _ptr(kk), _ptr(vv), kk.stride(0) if layers > 1 else 0, kk.stride(1), kk.stride(2),
         kk.stride(3), _ptr(ctx_len), _ptr(n_nodes), _ptr(accept_len), _ptr(path), B, T, Hkv, D,

@@ -66,6 +66,10 @@ constexpr int kKBf32 = 32;         // keys per fp32 LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRowSumLimit = 4294967296.0f;  // 2^32: a row sum above it means P ran away
+constexpr float kRowSumFloor = 2.3283064365386963e-10f;  // 2^-32
+
+// Reference max of a row: 0 when the row saw no key (-inf).
+__device__ __forceinline__ float finite_ref(float m) { return m == -INFINITY ? 0.f : m; }
 
 struct AttnParams {
   const void* q;
@@ -85,7 +89,8 @@ struct AttnParams {
   int RG;       // row groups per (sequence, KV head)
   int nw;       // workgroups launched (a multiple of 8)
   float scale_log2;
-  float* out;
+  void* out;        // [rows][Hq][D] fp32, or bf16 when out_bf16
+  int out_bf16;
   float* lse;
   int32_t* sched;   // [0] keys per unit, [1 + b] first unit of sequence b
   float* part_o;    // [unit][rows_wg][D], un-normalised: fp32 in d order, or int16 fixed
@@ -118,6 +123,23 @@ __device__ __forceinline__ int seq_status(const P& p, int n, int L, int start) {
 template <class P>
 __device__ __forceinline__ int64_t seq_row0(const P& p, int b, int start) {
   return P::kPacked ? static_cast<int64_t>(start) : static_cast<int64_t>(b) * p.T;
+}
+
+// Four consecutive output entries starting at entry `off` of out: fp32, or
+// bf16 rounded to nearest even.
+__device__ __forceinline__ void store_out4(const AttnParams& p, int64_t off, float a, float b,
+                                           float c, float d) {
+  if (p.out_bf16) {
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    bf16x4_t h;
+    h[0] = static_cast<__bf16>(a);
+    h[1] = static_cast<__bf16>(b);
+    h[2] = static_cast<__bf16>(c);
+    h[3] = static_cast<__bf16>(d);
+    *reinterpret_cast<bf16x4_t*>(static_cast<uint16_t*>(p.out) + off) = h;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off) = make_float4(a, b, c, d);
+  }
 }
 
 // a / b for 0 <= a, 1 <= b (exact). Below 2^22 the float quotient through
@@ -176,11 +198,11 @@ __device__ void finish_non_live(const P& p, int st0, int n0, int s0) {
       const int b = b0 + bl;
       const int rows = __shfl(nclr, bl);
       const int64_t r0 = seq_row0(p, b, __shfl(start, bl));
-      float4* o = reinterpret_cast<float4*>(p.out + r0 * p.Hq * D);
+      const int64_t o0 = r0 * p.Hq * D;
       float* l = p.lse + r0 * p.Hq;
       const int per_seq = rows * p.Hq * D4;
       for (int idx = gtid; idx < per_seq; idx += nthreads) {
-        o[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
+        store_out4(p, o0 + 4 * static_cast<int64_t>(idx), 0.f, 0.f, 0.f, 0.f);
         if (idx % D4 == 0) l[idx / D4] = -INFINITY;
       }
     }
@@ -659,8 +681,11 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
                                   fmaxf(sacc[0][rt][2], sacc[0][rt][3])),
                             fmaxf(fmaxf(sacc[1][rt][0], sacc[1][rt][1]),
                                   fmaxf(sacc[1][rt][2], sacc[1][rt][3])));
-      mref[rt] = row_max4(m) * cs;
-      neg_m[rt] = (mref[rt] == -INFINITY) ? 0.f : -mref[rt];
+      // A row that sees none of these keys (a caller-built mask without
+      // them) takes 0 as its reference: the reference stored with the
+      // partial is always the one P was computed against.
+      mref[rt] = finite_ref(row_max4(m) * cs);
+      neg_m[rt] = -mref[rt];
     }
   };
   // P = 2^(s cs - mref) as bf16 parts (the MFMA B operand P^T). No running
@@ -735,7 +760,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
       l_run[rt] = 0.f;
-      neg_m[rt] = (mref[rt] == -INFINITY) ? 0.f : -mref[rt];
+      neg_m[rt] = -mref[rt];
     }
     if (tid == 0) sOvf = 0;
     bool need_ref = (attempt == 0);
@@ -817,12 +842,14 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
         }
       }
     }
-    // ---- end of pass: row sums and the runaway test ----
+    // ---- end of pass: row sums and the runaway test (live rows only; a
+    // sum below 2^-32 can only come from the zero reference of a row that
+    // saw none of the unit's first keys) ----
     bool ovf = false;
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
       l_tot[rt] = row_sum4(l_run[rt]);
-      ovf |= !(l_tot[rt] <= kRowSumLimit);
+      ovf |= node_rt[rt] >= 0 && !(l_tot[rt] <= kRowSumLimit && l_tot[rt] >= kRowSumFloor);
     }
     if (wave_active && __any(ovf) && lane == 0) sOvf = 1;
     TV_WAIT_VMCNT(0);
@@ -863,7 +890,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
     TV_WAIT_VMCNT(0);
     lds_barrier();
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) mref[rt] = row_max4(lm[rt]) * cs;
+    for (int rt = 0; rt < kRT; ++rt) mref[rt] = finite_ref(row_max4(lm[rt]) * cs);
   };
   if (run_pass(0)) {
     max_pass();
@@ -897,14 +924,16 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
       const int i = row_node(p, r);
       const int h = kvh * p.G + (r - i * p.G);
       const int64_t orow = (srow0 + i) * p.Hq + h;
-      float* dst = p.out + orow * D;
-      const float inv = live ? 1.f / l_tot[rt] : 0.f;
+      // A live row that saw no key at all (only possible with a caller-built
+      // mask and no committed context) gets the padding values.
+      const bool seen = live && l_tot[rt] > 0.f;
+      const float inv = seen ? 1.f / l_tot[rt] : 0.f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const f32x4_t v = o[dt][rt] * inv;
-        *reinterpret_cast<float4*>(dst + 16 * dt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+        store_out4(p, orow * D + 16 * dt + 4 * g, v[0], v[1], v[2], v[3]);
       }
-      if (g == 0) p.lse[orow] = live ? (mref[rt] + __log2f(l_tot[rt])) * kLn2 : -INFINITY;
+      if (g == 0) p.lse[orow] = seen ? (mref[rt] + __log2f(l_tot[rt])) * kLn2 : -INFINITY;
     } else {
       const int64_t prow = static_cast<int64_t>(u) * p.rows_wg + (r - rg * kRowsWG);
       if constexpr (kQ16) {
@@ -1055,10 +1084,13 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParamsT
     const bool live = node >= 0;
     if (PACKED && !live) return;  // packed: rows past n do not exist
     const int64_t orow = (srow0 + i) * p.Hq + h;
-    const float inv = live ? 1.f / l_run : 0.f;
+    const bool seen = live && l_run > 0.f;  // a live row that saw no key: padding values
+    const float inv = seen ? 1.f / l_run : 0.f;
 #pragma unroll
-    for (int d = 0; d < DQ; ++d) p.out[orow * D + quarter * DQ + d] = live ? ov[d] * inv : 0.f;
-    if (quarter == 0) p.lse[orow] = live ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+    for (int d = 0; d < DQ; d += 4)
+      store_out4(p, orow * D + quarter * DQ + d, ov[d] * inv, ov[d + 1] * inv, ov[d + 2] * inv,
+                 ov[d + 3] * inv);
+    if (quarter == 0) p.lse[orow] = seen ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
   } else {
     const int64_t prow = static_cast<int64_t>(u) * p.rows_wg + (r - rg * kRowsWGf32);
 #pragma unroll
@@ -1137,19 +1169,19 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   // lane's eight entries are (g, dt = 2 dp and 2 dp + 1, e) of the split's
   // row layout [g][dt][e], i.e. d = 16 dt + 4 g + e; fp32 partials are in
   // plain d order.
-  float4* dst[EPL / 4];
+  int64_t dst[EPL / 4];  // entry offsets in out
   if constexpr (Q16) {
     constexpr int HALF = D / 32;  // dt pairs per g
     const int g = sub / HALF;
     const int dp = sub - g * HALF;
-    dst[0] = reinterpret_cast<float4*>(p.out + orow * D + 32 * dp + 4 * g);
-    dst[1] = reinterpret_cast<float4*>(p.out + orow * D + 32 * dp + 16 + 4 * g);
+    dst[0] = orow * D + 32 * dp + 4 * g;
+    dst[1] = orow * D + 32 * dp + 16 + 4 * g;
   } else {
-    dst[0] = reinterpret_cast<float4*>(p.out + orow * D + EPL * sub);
+    dst[0] = orow * D + EPL * sub;
   }
   if (i >= n) {
 #pragma unroll
-    for (int e = 0; e < EPL / 4; ++e) *dst[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int e = 0; e < EPL / 4; ++e) store_out4(p, dst[e], 0.f, 0.f, 0.f, 0.f);
     if (sub == 0) p.lse[orow] = -INFINITY;
     return;
   }
@@ -1231,12 +1263,12 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
     }
     mstar = m;
   }
-  const float inv = 1.f / lstar;
+  const float inv = lstar > 0.f ? 1.f / lstar : 0.f;
 #pragma unroll
   for (int e = 0; e < EPL / 4; ++e)
-    *dst[e] = make_float4(acc[4 * e] * inv, acc[4 * e + 1] * inv, acc[4 * e + 2] * inv,
-                          acc[4 * e + 3] * inv);
-  if (sub == 0) p.lse[orow] = (mstar + __log2f(lstar)) * kLn2;
+    store_out4(p, dst[e], acc[4 * e] * inv, acc[4 * e + 1] * inv, acc[4 * e + 2] * inv,
+               acc[4 * e + 3] * inv);
+  if (sub == 0) p.lse[orow] = lstar > 0.f ? (mstar + __log2f(lstar)) * kLn2 : -INFINITY;
 }
 
 // Workgroups per launch: one per compute unit (a multiple of 8), cached per
@@ -1371,12 +1403,13 @@ int attention_call(const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh, cons
                    const void* v, int64_t kv_sb, int64_t kv_sh, int64_t kv_ss,
                    const int32_t* ctx_len, const int32_t* n_nodes, const uint32_t* mask,
                    const int32_t* row_start, int rows_total, int B, int T, int Hq, int Hkv, int D,
-                   int max_ctx, int kv_capacity, float scale, int in_dtype, int probability_parts,
-                   int chunk_keys, float* out, float* lse, void* workspace, size_t ws_bytes,
-                   int32_t* row_status, hipStream_t stream) {
+                   int max_ctx, int kv_capacity, float scale, int in_dtype, int out_dtype,
+                   int probability_parts, int chunk_keys, void* out, float* lse, void* workspace,
+                   size_t ws_bytes, int32_t* row_status, hipStream_t stream) {
   if (!q || !k || !v || !ctx_len || !n_nodes || !mask || !out || !lse || !row_status)
     return TV_ERR_NULL;
   if (in_dtype != TV_F32 && in_dtype != TV_BF16) return TV_ERR_DTYPE;
+  if (out_dtype != TV_F32 && out_dtype != TV_BF16) return TV_ERR_DTYPE;
   if (!valid_sizes(B, T, Hq, Hkv, D, max_ctx, chunk_keys) || kv_capacity < 1)
     return TV_ERR_SHAPE;
   if (probability_parts < 1 || probability_parts > 3) return TV_ERR_SHAPE;
@@ -1428,6 +1461,7 @@ int attention_call(const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh, cons
   p.nw = grid_workgroups();
   p.scale_log2 = scale * kLog2e;
   p.out = out;
+  p.out_bf16 = out_dtype == TV_BF16;
   p.lse = lse;
   p.sched = nullptr;
   p.part_o = nullptr;
@@ -1456,13 +1490,13 @@ extern "C" int tv_tree_attention(const void* q, int64_t q_sb, int64_t q_st, int6
                                  int64_t kv_ss, const int32_t* ctx_len, const int32_t* n_nodes,
                                  const uint32_t* mask, int B, int T, int Hq, int Hkv, int D,
                                  int max_ctx, int kv_capacity, float scale, int in_dtype,
-                                 int probability_parts, int chunk_keys, float* out, float* lse,
-                                 void* workspace, size_t ws_bytes, int32_t* row_status,
-                                 hipStream_t stream) {
+                                 int out_dtype, int probability_parts, int chunk_keys, void* out,
+                                 float* lse, void* workspace, size_t ws_bytes,
+                                 int32_t* row_status, hipStream_t stream) {
   return attention_call(q, q_sb, q_st, q_sh, k, v, kv_sb, kv_sh, kv_ss, ctx_len, n_nodes, mask,
                         nullptr, 0, B, T, Hq, Hkv, D, max_ctx, kv_capacity, scale, in_dtype,
-                        probability_parts, chunk_keys, out, lse, workspace, ws_bytes, row_status,
-                        stream);
+                        out_dtype, probability_parts, chunk_keys, out, lse, workspace, ws_bytes,
+                        row_status, stream);
 }
 
 extern "C" int tv_tree_attention_packed(const void* q, int64_t q_st, int64_t q_sh, const void* k,
@@ -1471,14 +1505,14 @@ extern "C" int tv_tree_attention_packed(const void* q, int64_t q_st, int64_t q_s
                                         const int32_t* n_nodes, const uint32_t* mask,
                                         const int32_t* row_start, int rows_total, int B, int T,
                                         int Hq, int Hkv, int D, int max_ctx, int kv_capacity,
-                                        float scale, int in_dtype, int probability_parts,
-                                        int chunk_keys, float* out, float* lse, void* workspace,
-                                        size_t ws_bytes, int32_t* row_status,
-                                        hipStream_t stream) {
+                                        float scale, int in_dtype, int out_dtype,
+                                        int probability_parts, int chunk_keys, void* out,
+                                        float* lse, void* workspace, size_t ws_bytes,
+                                        int32_t* row_status, hipStream_t stream) {
   if (!row_start) return TV_ERR_NULL;
   if (rows_total < 0) return TV_ERR_SHAPE;
   return attention_call(q, 0, q_st, q_sh, k, v, kv_sb, kv_sh, kv_ss, ctx_len, n_nodes, mask,
                         row_start, rows_total, B, T, Hq, Hkv, D, max_ctx, kv_capacity, scale,
-                        in_dtype, probability_parts, chunk_keys, out, lse, workspace, ws_bytes,
-                        row_status, stream);
+                        in_dtype, out_dtype, probability_parts, chunk_keys, out, lse, workspace,
+                        ws_bytes, row_status, stream);
 }
