@@ -5,6 +5,7 @@ import numpy as np
 import torch
 
 import oracle
+from oracle.decode import decode
 import tree_attention_draft_tv_amd as tv
 
 # Attention tolerances (max abs error over live entries).
@@ -54,13 +55,13 @@ def run_mask(d, T):
     return mask, depth, status
 
 
-def run_attention(w, d, mask, chunk_keys=0, parts=1, max_ctx=None):
+def run_attention(w, d, mask, chunk_keys=0, parts=3, max_ctx=None, out_dtype=torch.float32):
     out, lse, st = tv.tree_attention(d["q"], d["k"], d["v"], d["ctx_len"], d["n_nodes"], mask,
                                      w.max_ctx if max_ctx is None else max_ctx,
                                      scale=float(w.scale), probability_parts=parts,
-                                     chunk_keys=chunk_keys)
+                                     chunk_keys=chunk_keys, out_dtype=out_dtype)
     torch.cuda.synchronize()
-    return out.cpu().numpy(), lse.cpu().numpy(), st.cpu().numpy()
+    return out.float().cpu().numpy(), lse.cpu().numpy(), st.cpu().numpy()
 
 
 def oracle_attention(w):
@@ -68,24 +69,26 @@ def oracle_attention(w):
                                  w.scale, max_ctx=w.max_ctx, kv_capacity=w.kv_capacity)
 
 
-def bf16_p_bound(w):
-    """Worst-case output error of one-part bf16 probabilities: each P is
-    rounded to nearest with relative error <= 2^-8 (the unit roundoff of an
-    8-bit significand), so |out - exact| <= 2^-8 max|v| over the visible
-    values (plus fp32 accumulation slack). Used for the
-    tiny-context edge cases, where few keys carry all the weight; the
-    measured workloads meet 2e-3 directly."""
-    from oracle import decode
+def fast_mode_bound(w):
+    """Error bound of the lossy fast mode (probability_parts = 1), as
+    include/tv.h states it: each probability rounded once to bf16 (relative
+    error <= 2^-8, the unit roundoff of an 8-bit significand) and the split
+    partials kept as 16-bit fixed point (<= max|v| / 65534), so an output
+    entry is within (2^-8 + 2^-16) max|v| over the visible values, plus fp32
+    accumulation slack. Only tests of that mode use it; every other
+    attention test holds the 2e-3 / 1e-4 bound."""
     vmax = 0.0
     for b in range(w.B):
         n = int(w.n_nodes[b])
         if n:
             live = decode(w.v[b, :, : int(w.ctx_len[b]) + n], w.dtype)
             vmax = max(vmax, float(np.abs(live).max()))
-    return max(ATOL_OUT, 2.0 ** -8 * vmax + 1e-5)
+    return max(ATOL_OUT, (2.0 ** -8 + 2.0 ** -16) * vmax + 1e-5)
 
 
-def check_attention(w, got, want, atol_out=ATOL_OUT, atol_lse=ATOL_LSE):
+def check_attention(w, got, want, atol_out=ATOL_OUT, atol_lse=ATOL_LSE, label=""):
+    """Statuses equal, no NaN, live entries within the bounds (max abs error),
+    padding exactly 0 / -inf. Prints and returns (err_out, err_lse)."""
     out, lse, st = got
     o_ref, l_ref, st_ref = want
     assert np.array_equal(st, st_ref), (st, st_ref)
@@ -94,8 +97,12 @@ def check_attention(w, got, want, atol_out=ATOL_OUT, atol_lse=ATOL_LSE):
     for b in range(w.B):
         if st_ref[b] == 0:
             live[b, : int(w.n_nodes[b])] = True
-    err_o = np.abs(out[live] - o_ref[live]).max(initial=0.0)
-    err_l = np.abs(lse[live] - l_ref[live]).max(initial=0.0)
+    err_o = float(np.abs(out[live] - o_ref[live]).max(initial=0.0))
+    fin = live & np.isfinite(l_ref)
+    assert np.array_equal(lse[live & ~fin], l_ref[live & ~fin])  # rows that see no key
+    err_l = float(np.abs(lse[fin] - l_ref[fin]).max(initial=0.0))
+    print("attention %s: max|out - oracle| = %.3g (bound %.3g), max|lse - oracle| = %.3g "
+          "(bound %.3g)" % (label, err_o, atol_out, err_l, atol_lse))
     assert err_o <= atol_out, "max |out - oracle| = %g" % err_o
     assert err_l <= atol_lse, "max |lse - oracle| = %g" % err_l
     assert np.all(out[~live] == 0.0)
