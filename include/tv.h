@@ -265,15 +265,36 @@ size_t tv_accept_workspace_size(int B, int T, int V, int mode);
  *   accept_mask uint8 [B][T] 1 on the nodes of path, else 0
  *   row_status int32 [B]: OK, BAD_PARENT, NNODES or BAD_TOKEN
  *
- * Constraints: 1 <= T <= TV_MAX_TREE; V >= 1; logits_row_stride >= V (any
- * value: rows need not be 16-byte aligned). Workspace as sized above,
- * 256-byte aligned, no initialisation needed.
+ * Constraints: 1 <= T <= TV_MAX_TREE; 0 <= B <= 65535; V >= 1;
+ * logits_row_stride >= V (any value: rows need not be 16-byte aligned).
+ * Workspace as sized above, 256-byte aligned, no initialisation needed.
  */
 int tv_accept_greedy(const float* logits, int64_t logits_row_stride, const int32_t* tokens,
                      const int32_t* parent, const int32_t* n_nodes, int B, int T, int V,
                      int32_t* accept_len, int32_t* path, int32_t* bonus, uint8_t* accept_mask,
                      void* workspace, size_t ws_bytes, int32_t* row_status,
                      hipStream_t stream);
+
+/*
+ * tv_accept_greedy_noalloc — tv_accept_greedy for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and results, with the
+ * per-slice argmax partials kept in a static scratch array of the library
+ * (2 MiB per device, held until the process ends) instead of a workspace.
+ * Arguments, outputs and errors as tv_accept_greedy, without workspace and
+ * ws_bytes. Sizes whose workspace (tv_accept_workspace_size(B, T, V, 0):
+ * B * T * min(64, ceil(V / 16384)) * 8 bytes, rounded up to 256) exceeds
+ * 2 MiB return TV_ERR_WORKSPACE before anything is enqueued. Every call on a
+ * device shares that device's array: calls that overlap on one device (two
+ * streams, two threads) race and must be ordered by the caller. Calls on
+ * different devices do not interact. The first call on a device looks the
+ * array's address up once (TV_ERR_HIP if that fails); nothing is allocated.
+ */
+int tv_accept_greedy_noalloc(const float* logits, int64_t logits_row_stride,
+                             const int32_t* tokens, const int32_t* parent,
+                             const int32_t* n_nodes, int B, int T, int V, int32_t* accept_len,
+                             int32_t* path, int32_t* bonus, uint8_t* accept_mask,
+                             int32_t* row_status, hipStream_t stream);
 
 /*
  * tv_accept_sample — SpecInfer-style rejection sampling on the tree.

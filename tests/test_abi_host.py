@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.SIGNATURES) == names
@@ -306,3 +306,26 @@ def test_linear_validation(lib):
     g = lib.tv_linear_swiglu_rows
     assert g(P, 3584, P, NULL, 3584, 264, 3584, 18944, P2, 18944, STREAM) == -1
     assert g(P, 3584, P, P, 3584, 0, 3584, 18944, P2, 18944, STREAM) == 0
+
+
+def test_accept_greedy_noalloc_validation(lib):
+    f = lib.tv_accept_greedy_noalloc
+
+    def call(**kw):
+        a = dict(lg=P, stride=152064, tok=P, par=P, n=P, B=8, T=33, V=152064, al=P, path=P,
+                 bonus=P, am=P, st=P)
+        a.update(kw)
+        return f(a["lg"], a["stride"], a["tok"], a["par"], a["n"], a["B"], a["T"], a["V"],
+                 a["al"], a["path"], a["bonus"], a["am"], a["st"], STREAM)
+
+    assert call(lg=NULL) == -1 and call(st=NULL) == -1
+    assert call(T=0) == -2 and call(V=0) == -2 and call(stride=10) == -2
+    assert call(B=65536) == -2
+    assert call(lg=ctypes.c_void_p(0x100002)) == -4
+    assert call(B=0) == 0
+    # Beyond the 2 MiB static scratch: B * T * slices * 8 bytes. Rejected on
+    # the host before the device is touched.
+    big = lib.tv_accept_workspace_size(1024, 33, 152064, 0)
+    assert big > (2 << 20)
+    assert call(B=1024) == -5
+    assert lib.tv_accept_workspace_size(512, 33, 152064, 0) <= (2 << 20)

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     TV_MAX_TREE,
     TVError,
     accept_greedy,
+    accept_greedy_noalloc,
     accept_sample,
     accept_workspace_size,
     adapt_tree_budget,

@@ -53,6 +53,7 @@ SIGNATURES = {
     "tv_adapt_tree_budget": (_I, [_P, _P, _P, _I, _F, _F, _I, _I, _P, _P, _P, _P, _P]),
     "tv_accept_workspace_size": (_S, [_I, _I, _I, _I]),
     "tv_accept_greedy": (_I, [_P, _L, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _S, _P, _P]),
+    "tv_accept_greedy_noalloc": (_I, [_P, _L, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "tv_accept_sample": (_I, [_P, _L, _F, _P, _L, _P, _P, _P, _P, _I, _I, _I,
                               _P, _P, _P, _P, _P, _P, _S, _P, _P]),
     "tv_commit_accepted_kv": (_I, [_P, _P, _L, _L, _L, _L, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
@@ -458,6 +459,35 @@ def accept_greedy(logits: torch.Tensor, tokens: torch.Tensor, parent: torch.Tens
                                 _ptr(ws), ws_bytes, _ptr(status), _stream(dev)),
            "tv_accept_greedy")
     return outs
+
+
+def accept_greedy_noalloc(logits: torch.Tensor, tokens: torch.Tensor, parent: torch.Tensor,
+                          n_nodes: torch.Tensor, outputs):
+    """:func:`accept_greedy` through ``tv_accept_greedy_noalloc``: the library's
+    static per-device scratch replaces the workspace, so the call allocates
+    nothing. ``outputs`` (accept_len, path, bonus, accept_mask, row_status)
+    must be given. Calls that overlap on one device race."""
+    lib = load()
+    dev = logits.device
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 3:
+        raise TVError("logits must be [B, T, V]")
+    B, T, V = logits.shape
+    for t, nm in ((tokens, "tokens"), (parent, "parent")):
+        _shape(t, nm, torch.int32, shape=(B, T), contiguous=True)
+    _shape(n_nodes, "n_nodes", torch.int32, shape=(B,), contiguous=True)
+    if outputs is None:
+        raise TVError("outputs must be given: this call allocates nothing")
+    _check_accept_outputs(outputs, B, T, None)
+    stride = _check_logits(logits, "logits", dev)
+    for t, nm in ((tokens, "tokens"), (parent, "parent"), (n_nodes, "n_nodes")):
+        _need(t, nm, torch.int32, dev)
+    _check_accept_outputs(outputs, B, T, dev)
+    acc_len, path, bonus, amask, status = outputs
+    _check(lib.tv_accept_greedy_noalloc(_ptr(logits), stride, _ptr(tokens), _ptr(parent),
+                                        _ptr(n_nodes), B, T, V, _ptr(acc_len), _ptr(path),
+                                        _ptr(bonus), _ptr(amask), _ptr(status), _stream(dev)),
+           "tv_accept_greedy_noalloc")
+    return outputs
 
 
 def accept_sample(logits: torch.Tensor, temperature: float, q: torch.Tensor, u: torch.Tensor,

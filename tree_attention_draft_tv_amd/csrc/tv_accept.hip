@@ -19,6 +19,8 @@
 // Sequences with n_nodes == 0 read nothing.
 #include <limits.h>
 
+#include <mutex>
+
 #include "tv_common.h"
 
 namespace {
@@ -956,27 +958,99 @@ extern "C" size_t tv_accept_workspace_size(int B, int T, int V, int mode) {
   return mode == 0 ? greedy_ws(B, T, V) : sample_ws(B, T, V);
 }
 
+namespace {
+
+// ---------------------------------------------- greedy without allocation ---
+// tv_accept_greedy_noalloc keeps the per-slice argmax partials in this
+// file-scope array instead of a caller workspace: one copy per device, held
+// until the process ends. Every call on a device shares it (calls that
+// overlap on one device race). The argmax kernel writes every partial the
+// walk reads, so nothing in it needs clearing between calls.
+constexpr size_t kStaticScratchBytes = size_t(2) << 20;  // 2 MiB
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// Device address of this device's `scratch`, looked up once per device (the
+// array's name is only a host-side handle: kernels must get the address).
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();  // do not leave the failure for the next call to report
+      return TV_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TV_OK;
+}
+
+int greedy_launch(const float* logits, int64_t logits_row_stride, const int32_t* tokens,
+                  const int32_t* parent, const int32_t* n_nodes, int B, int T, int V,
+                  int32_t* accept_len, int32_t* path, int32_t* bonus, uint8_t* accept_mask,
+                  ArgBest* part, int32_t* row_status, hipStream_t stream) {
+  const int S = num_splits(V);
+  hipLaunchKernelGGL(argmax_slices_kernel, dim3(S, T, B), dim3(kThreads), 0, stream, logits,
+                     logits_row_stride, n_nodes, T, V, S, part);
+  hipLaunchKernelGGL(greedy_walk_kernel, dim3(B), dim3(TV_MAX_TREE), 0, stream, part, S, tokens,
+                     parent, n_nodes, T, V, accept_len, path, bonus, accept_mask, row_status);
+  return tvh::launch_status();
+}
+
+int greedy_args(const float* logits, int64_t logits_row_stride, const int32_t* tokens,
+                const int32_t* parent, const int32_t* n_nodes, int B, int T, int V,
+                int32_t* accept_len, int32_t* path, int32_t* bonus, uint8_t* accept_mask,
+                int32_t* row_status) {
+  if (!logits || !tokens || !parent || !n_nodes || !accept_len || !path || !bonus ||
+      !accept_mask || !row_status)
+    return TV_ERR_NULL;
+  // B is a grid dimension of the argmax launch (at most 65535).
+  if (!accept_sizes_ok(B, T, V) || B > 65535 || logits_row_stride < V) return TV_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(logits) & 3u) return TV_ERR_ALIGN;
+  return TV_OK;
+}
+
+}  // namespace
+
+extern "C" int tv_accept_greedy_noalloc(const float* logits, int64_t logits_row_stride,
+                                        const int32_t* tokens, const int32_t* parent,
+                                        const int32_t* n_nodes, int B, int T, int V,
+                                        int32_t* accept_len, int32_t* path, int32_t* bonus,
+                                        uint8_t* accept_mask, int32_t* row_status,
+                                        hipStream_t stream) {
+  const int st = greedy_args(logits, logits_row_stride, tokens, parent, n_nodes, B, T, V,
+                             accept_len, path, bonus, accept_mask, row_status);
+  if (st != TV_OK) return st;
+  if (B == 0) return TV_OK;
+  if (greedy_ws(B, T, V) > kStaticScratchBytes) return TV_ERR_WORKSPACE;
+  void* ptr = nullptr;
+  const int sp = scratch_ptr(&ptr);
+  if (sp != TV_OK) return sp;
+  return greedy_launch(logits, logits_row_stride, tokens, parent, n_nodes, B, T, V, accept_len,
+                       path, bonus, accept_mask, static_cast<ArgBest*>(ptr), row_status, stream);
+}
+
 extern "C" int tv_accept_greedy(const float* logits, int64_t logits_row_stride,
                                 const int32_t* tokens, const int32_t* parent,
                                 const int32_t* n_nodes, int B, int T, int V, int32_t* accept_len,
                                 int32_t* path, int32_t* bonus, uint8_t* accept_mask,
                                 void* workspace, size_t ws_bytes, int32_t* row_status,
                                 hipStream_t stream) {
-  if (!logits || !tokens || !parent || !n_nodes || !accept_len || !path || !bonus ||
-      !accept_mask || !row_status)
-    return TV_ERR_NULL;
-  if (!accept_sizes_ok(B, T, V) || logits_row_stride < V) return TV_ERR_SHAPE;
-  if (reinterpret_cast<uintptr_t>(logits) & 3u) return TV_ERR_ALIGN;
+  const int st = greedy_args(logits, logits_row_stride, tokens, parent, n_nodes, B, T, V,
+                             accept_len, path, bonus, accept_mask, row_status);
+  if (st != TV_OK) return st;
   if (B == 0) return TV_OK;
   if (!workspace || ws_bytes < greedy_ws(B, T, V) || !tvh::aligned256(workspace))
     return TV_ERR_WORKSPACE;
-  const int S = num_splits(V);
-  ArgBest* part = static_cast<ArgBest*>(workspace);
-  hipLaunchKernelGGL(argmax_slices_kernel, dim3(S, T, B), dim3(kThreads), 0, stream, logits,
-                     logits_row_stride, n_nodes, T, V, S, part);
-  hipLaunchKernelGGL(greedy_walk_kernel, dim3(B), dim3(TV_MAX_TREE), 0, stream, part, S, tokens,
-                     parent, n_nodes, T, V, accept_len, path, bonus, accept_mask, row_status);
-  return tvh::launch_status();
+  return greedy_launch(logits, logits_row_stride, tokens, parent, n_nodes, B, T, V, accept_len,
+                       path, bonus, accept_mask, static_cast<ArgBest*>(workspace), row_status,
+                       stream);
 }
 
 extern "C" int tv_accept_sample(const float* logits, int64_t logits_row_stride,
