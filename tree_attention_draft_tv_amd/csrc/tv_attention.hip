@@ -486,6 +486,21 @@ __device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
 template <int V>
 using IC = std::integral_constant<int, V>;
 
+// a (low half) and b (high half) rounded to bf16, nearest even.
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t t;
+  t[0] = static_cast<__bf16>(a);
+  t[1] = static_cast<__bf16>(b);
+  return __builtin_bit_cast(uint32_t, t);
+}
+
+// The high 16 bits of b and of a side by side: (b >> 16) << 16 | a >> 16,
+// i.e. the bf16 truncations of a (low half) and b (high half).
+__device__ __forceinline__ uint32_t high_halves(float b, float a) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
 // Max over the four lanes l, l^16, l^32, l^48 (the four lane groups that
 // hold the same packed row), with the gfx950 row-swap permutes (no LDS).
 __device__ __forceinline__ float row_max4(float x) {
@@ -690,6 +705,13 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
   };
   // P = 2^(s cs - mref) as bf16 parts (the MFMA B operand P^T). No running
   // max is kept: a score far above the reference shows up in the row sum.
+  // One part: P rounded to nearest even. Two parts: hi = P rounded to
+  // nearest, mid = P - hi (exact in fp32) rounded to nearest. Three parts
+  // are cut by truncation, which is exact: hi = the top 16 bits of P (a
+  // bf16 value), r1 = P - hi (exact in fp32, at most 16 significant bits),
+  // mid = the top 16 bits of r1, lo = r1 - mid (exact, at most 8
+  // significant bits, so a bf16 value); P = hi + mid + lo exactly, and two
+  // entries go into one register with one byte permute.
   auto softmax_block = [&](const f32x4_t (&sacc)[2][kRT], bf16x8_t (&pb)[PARTS][kRT])
                            __attribute__((always_inline)) {
 #pragma unroll
@@ -702,20 +724,36 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
 #pragma unroll
       for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(y[e]);
       l_run[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-      bf16x8_t h1;
+      if constexpr (PARTS == 1) {
+        bf16x8_t h1;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) h1[e] = static_cast<__bf16>(pr[e]);
-      pb[0][rt] = h1;
-      if constexpr (PARTS > 1) {
-        bf16x8_t h2, h3;
+        for (int e = 0; e < 8; ++e) h1[e] = static_cast<__bf16>(pr[e]);
+        pb[0][rt] = h1;
+      } else {
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        u32x4_t w0, w1, w2;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float r1 = pr[e] - static_cast<float>(h1[e]);
-          h2[e] = static_cast<__bf16>(r1);
-          h3[e] = static_cast<__bf16>(r1 - static_cast<float>(h2[e]));
+        for (int k = 0; k < 4; ++k) {
+          const float a = pr[2 * k], b = pr[2 * k + 1];
+          if constexpr (PARTS == 2) {
+            // Both parts rounded to nearest: P - hi - mid <= 2^-16 P.
+            w0[k] = bf16_pair(a, b);
+            const float ra = a - __uint_as_float(w0[k] << 16);
+            const float rb = b - __uint_as_float(w0[k] & 0xFFFF0000u);
+            w1[k] = bf16_pair(ra, rb);
+          } else {
+            w0[k] = high_halves(b, a);
+            const float ra = a - __uint_as_float(__float_as_uint(a) & 0xFFFF0000u);
+            const float rb = b - __uint_as_float(__float_as_uint(b) & 0xFFFF0000u);
+            w1[k] = high_halves(rb, ra);
+            const float sa = ra - __uint_as_float(__float_as_uint(ra) & 0xFFFF0000u);
+            const float sb = rb - __uint_as_float(__float_as_uint(rb) & 0xFFFF0000u);
+            w2[k] = high_halves(sb, sa);
+          }
         }
-        pb[1][rt] = h2;
-        if constexpr (PARTS > 2) pb[2][rt] = h3;
+        pb[0][rt] = __builtin_bit_cast(bf16x8_t, w0);
+        pb[1][rt] = __builtin_bit_cast(bf16x8_t, w1);
+        if constexpr (PARTS > 2) pb[2][rt] = __builtin_bit_cast(bf16x8_t, w2);
       }
     }
   };
@@ -727,18 +765,33 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
   auto pv_block = [&](int t, int sb, const bf16x8_t (&pb)[PARTS][kRT])
                       __attribute__((always_inline)) {
     const uint16_t* tV = sV + (t & (kRing - 1)) * TILE + 32 * sb * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    auto read_v = [&](int dt) __attribute__((always_inline)) {
       const s16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tV + v_off[dt]));
       const s16x4_t h1 =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tV + 16 * D + v_off[dt]));
-      const bf16x8_t a =
-          __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+      return __builtin_bit_cast(bf16x8_t,
+                                __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // The operands of d-tile dt + 1 are requested before the MFMAs of dt
+    // (pinned below), so each slice's LDS latency hides behind the previous
+    // slice's MFMAs; consecutive MFMAs go to different accumulators.
+    bf16x8_t a = read_v(0);
 #pragma unroll
-      for (int rt = 0; rt < kRT; ++rt)
+    for (int dt = 0; dt < DT; ++dt) {
+      bf16x8_t an = a;
+      if (dt + 1 < DT) an = read_v(dt + 1);
 #pragma unroll
-        for (int q = 0; q < PARTS; ++q)
+      for (int q = 0; q < PARTS; ++q)
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt)
           o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[q][rt], o[dt][rt], 0, 0, 0);
+      a = an;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      if (dt == 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // reads of d-tiles 0, 1
+      else if (dt + 1 < DT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // d-tile dt + 1
+      __builtin_amdgcn_sched_group_barrier(0x008, PARTS * kRT, 0);  // MFMAs of d-tile dt
     }
   };
 
@@ -747,11 +800,44 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
   // finite), a score rose far above that reference (P <= l): then a
   // max-only pass finds the exact chunk max per row and a second pass runs
   // with it as reference, where every P <= 1.
-  // Leading tiles whose keys every row sees run software-pipelined: the
-  // S^T MFMAs of the next 32 keys are issued together with the softmax of
-  // the current ones, so the matrix cores and the VALU work side by side.
-  // The remaining tail tiles (tree block, chunk end) run masked, unpipelined.
-  const int nfull = max(0, (vis_all_end - kbeg) / kKB);
+  //
+  // A pass walks the chunk in 32-key sub-blocks j. Each step issues the
+  // S^T MFMAs of sub-block j and the P.V MFMAs of sub-block j - 1 (whose
+  // probabilities the previous step produced), then computes the
+  // probabilities of sub-block j on the VALU. A workgroup barrier after
+  // every second step publishes the next 64-key tile: tile t (sub-blocks
+  // 2t, 2t + 1) is published before the step that reads its first keys, and
+  // right after that barrier tile t + 2 is requested into the ring stage of
+  // tile t - 2, which every wave has finished. Two tiles are in flight
+  // while one is computed: the wait before the barrier leaves tile t + 1's
+  // copies outstanding (vector-memory operations complete in issue order
+  // for the counter, and these copies are the only ones issued inside the
+  // loop). One barrier per tile: finer-grained phase barriers (one wave
+  // group feeding the matrix cores while the other runs the softmax) were
+  // measured slower once the HBM->LDS copies stream underneath.
+  auto lds_barrier_pinned = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Waits until tile t has landed, leaving tile t + 1's copies in flight.
+  constexpr int kTileOps = 2 * LOADS;  // copies per thread per tile (K and V)
+  auto wait_tile = [&](int t) __attribute__((always_inline)) {
+    if (t + 1 < ntile)
+      TV_WAIT_VMCNT(kTileOps);
+    else
+      TV_WAIT_VMCNT(0);
+  };
+  const int nsub = (kend - kbeg + 31) / 32;  // 32-key sub-blocks of the chunk
+  // Mask (tail sub-blocks only), reference (first sub-block of the first
+  // pass), probabilities.
+  auto s_phase = [&](int j, f32x4_t (&sacc)[2][kRT], bf16x8_t (&pb)[PARTS][kRT], bool need_ref)
+                     __attribute__((always_inline)) {
+    const int skey0 = kbeg + 32 * j;
+    if (skey0 + 32 > vis_all_end) mask_block(skey0, sacc);
+    if (need_ref) take_reference(sacc);
+    softmax_block(sacc, pb);
+  };
   auto run_pass = [&](const int attempt) __attribute__((always_inline)) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -763,82 +849,28 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
       neg_m[rt] = -mref[rt];
     }
     if (tid == 0) sOvf = 0;
-    bool need_ref = (attempt == 0);
     issue_tile(0);
     if (ntile > 1) issue_tile(1);
-    if (nfull > 0 && !wave_active) {
-      // A wave without live rows (small trees and blocks leave whole waves
-      // of a row group empty) only takes part in the copies and barriers.
-      need_ref = false;
+    wait_tile(0);
+    lds_barrier_pinned();  // tile 0 published
+    if (ntile > 2) issue_tile(2);
+    f32x4_t sacc[2][kRT];
+    bf16x8_t pb[PARTS][kRT];
+    bool need_ref = (attempt == 0);
 #pragma unroll 1
-      for (int t = 0; t < nfull; ++t) enter_tile(t);
-    } else if (nfull > 0) {
-      // Waves with some live rows compute every row of their tiles: the
-      // loop body stays one straight-line block.
-      enter_tile(0);
-      f32x4_t sa[2][kRT], sb[2][kRT];
-      bf16x8_t pb[PARTS][kRT];
-      s_block(0, 0, sa);
-      if (need_ref) take_reference(sa);
-      need_ref = false;
-      int t = 0;
-      if constexpr (PARTS == 1) {
-        // Two sub-blocks of P in flight: each step issues the S^T MFMAs of
-        // the next sub-block and the P.V MFMAs of the previous one beside
-        // the softmax of the current one, so the matrix cores have twice as
-        // much independent work to overlap with the VALU.
-        bf16x8_t pa[PARTS][kRT];
-        s_block(0, 1, sb);
-        softmax_block(sa, pb);  // P of sub-block 0
-#pragma unroll 1
-        for (; t + 1 < nfull; ++t) {
-          // Here pb = P of (t, 0), sb = S of (t, 1).
-          enter_tile(t + 1);
-          s_block(t + 1, 0, sa);
-          pv_block(t, 0, pb);
-          softmax_block(sb, pa);
-          s_block(t + 1, 1, sb);
-          pv_block(t, 1, pa);
-          softmax_block(sa, pb);
-        }
-        pv_block(t, 0, pb);
-        softmax_block(sb, pa);
-        pv_block(t, 1, pa);
-      } else {
-#pragma unroll 1
-        for (; t + 1 < nfull; ++t) {
-          s_block(t, 1, sb);
-          softmax_block(sa, pb);
-          pv_block(t, 0, pb);
-          enter_tile(t + 1);
-          s_block(t + 1, 0, sa);
-          softmax_block(sb, pb);
-          pv_block(t, 1, pb);
-        }
-        s_block(t, 1, sb);
-        softmax_block(sa, pb);
-        pv_block(t, 0, pb);
-        softmax_block(sb, pb);
-        pv_block(t, 1, pb);
-      }
-    }
-#pragma unroll 1
-    for (int t = nfull; t < ntile; ++t) {
-      enter_tile(t);
+    for (int j = 0; j <= nsub; ++j) {
       if (wave_active) {
-#pragma unroll
-        for (int sbk = 0; sbk < 2; ++sbk) {
-          const int skey0 = kbeg + t * kKB + 32 * sbk;
-          if (skey0 < kend) {
-            f32x4_t sacc[2][kRT];
-            bf16x8_t pb[PARTS][kRT];
-            s_block(t, sbk, sacc);
-            if (skey0 + 32 > vis_all_end) mask_block(skey0, sacc);
-            if (need_ref) take_reference(sacc);
-            need_ref = false;
-            softmax_block(sacc, pb);
-            pv_block(t, sbk, pb);
-          }
+        if (j < nsub) s_block(j >> 1, j & 1, sacc);
+        if (j >= 1) pv_block((j - 1) >> 1, (j - 1) & 1, pb);
+        if (j < nsub) s_phase(j, sacc, pb, need_ref);
+      }
+      need_ref = false;
+      if (j & 1) {
+        const int t = (j + 1) >> 1;  // the next tile
+        if (t < ntile) {
+          wait_tile(t);
+          lds_barrier_pinned();
+          if (t + 2 < ntile) issue_tile(t + 2);
         }
       }
     }
