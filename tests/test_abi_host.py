@@ -199,13 +199,18 @@ def test_accept_validation(lib):
     assert scall(qs=10) == -2
     assert scall(q=ctypes.c_void_p(0x200001)) == -4
     assert scall(wsb=100) == -5
+    assert scall(B=65536) == -2
     assert scall(B=0) == 0
 
 
 def test_accept_workspace_size(lib):
     f = lib.tv_accept_workspace_size
     assert f(8, 33, 152064, 0) >= 8 * 33 * 10 * 8
-    assert f(8, 33, 32000, 1) >= 8 * 2 * 32000 * 8
+    # Sampling up to V = 32768: per node an accepted child, a bonus and a
+    # decision byte; larger vocabularies keep float64 rows.
+    assert f(8, 33, 32000, 1) >= 8 * 33 * 9
+    assert f(8, 33, 32000, 1) < 8 * 32000
+    assert f(8, 33, 152064, 1) >= 8 * 33 * 152064 * 8
     assert f(8, 33, 32000, 2) == ctypes.c_size_t(-1).value
     assert f(8, 0, 32000, 0) == ctypes.c_size_t(-1).value
 

@@ -11,11 +11,15 @@
 // graph/adaptive modes".
 //
 // Both modes are two launches:
-//   1. a data-parallel pass over the live logits rows, split along the
-//      vocabulary so the whole chip streams the rows once (16-byte loads):
-//      greedy keeps a (max, lowest index) pair per slice; sampling keeps the
-//      slice max and the float64 sum of exp((l - max) / tau);
-//   2. one workgroup per sequence merges the slices and walks the tree.
+//   greedy: a data-parallel pass over the live logits rows, split along the
+//     vocabulary so the whole chip streams the rows once (16-byte loads),
+//     keeps a (max, lowest index) pair per slice; one workgroup per sequence
+//     merges the slices and walks the tree;
+//   sampling (vocabularies up to 32768): one workgroup per live tree node
+//     decides, from that node's rows held in registers, which child the walk
+//     accepts there and which bonus it would draw there; one workgroup per
+//     sequence then follows the accepted children from the root. Larger
+//     vocabularies take a slice-statistics pass and a per-sequence walk.
 // Sequences with n_nodes == 0 read nothing.
 #include <limits.h>
 
@@ -42,12 +46,10 @@ struct ArgBest {
 // Sampling slices are smaller: every entry costs a float64 exp, so the
 // statistics pass wants many short, independent workgroups.
 constexpr int kSliceSample = 2048;
-// Residual entries per thread of the register-resident sampling walk: it
+// Vocabulary entries per thread of the node-parallel sampling path: it
 // covers V <= kRegSlots * kWalkThreads.
 constexpr int kRegSlots = 32;
 static_assert(kSliceSample % kWalkThreads == 0, "a walk block lies in one slice");
-static_assert(kRegSlots * kWalkThreads <= kMaxSplits * kSliceSample,
-              "register walk vocabularies use kSliceSample-wide slices");
 
 int num_splits(int V, int slice = kSlice) {
   int s = (V + slice - 1) / slice;
@@ -367,9 +369,102 @@ __global__ __launch_bounds__(kThreads) void softmax_slices_kernel(
   }
 }
 
+// Cross-lane moves of float64 values on the vector ALU (DPP and the
+// lane-swap instructions), so that reduction steps wait on the vector
+// pipeline instead of on LDS round trips. Lane patterns: kDppXor1 and
+// kDppXor2 exchange within quads (lane ^ 1, lane ^ 2); kDppHalfMirror pairs
+// lane i with 7 - i in each group of 8; kDppRowRor8 is lane ^ 8 within a row
+// of 16; kDppRowShr(n) reads lane - n within the row (lanes below n keep the
+// `old` operand).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppRowRor8 = 0x128;     // row_ror:8
+constexpr int kDppRowShr(int n) { return 0x110 + n; }
+
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), kCtrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), kCtrl, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+// Row-pair exchange (rows of 16 lanes): lanes with bit 4 clear get
+// a(lane) + a(lane ^ 16), lanes with bit 4 set get b(lane ^ 16) + b(lane).
+__device__ __forceinline__ double swap16_sum(double a, double b) {
+  const auto lo = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(__double2loint(a)),
+                                                   static_cast<unsigned>(__double2loint(b)),
+                                                   false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(__double2hiint(a)),
+                                                   static_cast<unsigned>(__double2hiint(b)),
+                                                   false, false);
+  return __hiloint2double(static_cast<int>(hi[0]), static_cast<int>(lo[0])) +
+         __hiloint2double(static_cast<int>(hi[1]), static_cast<int>(lo[1]));
+}
+
+// Half-wave exchange: lanes below 32 get a(lane) + a(lane + 32), lanes from
+// 32 up get b(lane - 32) + b(lane).
+__device__ __forceinline__ double swap32_sum(double a, double b) {
+  const auto lo = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(__double2loint(a)),
+                                                   static_cast<unsigned>(__double2loint(b)),
+                                                   false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(__double2hiint(a)),
+                                                   static_cast<unsigned>(__double2hiint(b)),
+                                                   false, false);
+  return __hiloint2double(static_cast<int>(hi[0]), static_cast<int>(lo[0])) +
+         __hiloint2double(static_cast<int>(hi[1]), static_cast<int>(lo[1]));
+}
+
+// Sum over the wave, in every lane (each step adds a lane and its partner,
+// so all lanes round alike and hold the same value).
+__device__ __forceinline__ double wave_sum_valu(double x) {
+  x += dpp_f64<kDppXor1>(x);
+  x += dpp_f64<kDppXor2>(x);
+  x += dpp_f64<kDppHalfMirror>(x);
+  x += dpp_f64<kDppRowRor8>(x);
+  x = swap16_sum(x, x);
+  return swap32_sum(x, x);
+}
+
+__device__ __forceinline__ float wave_max_valu(float x) {
+  x = fmaxf(x, dpp_f32<kDppXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppXor2>(x));
+  x = fmaxf(x, dpp_f32<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp_f32<kDppRowRor8>(x));
+  const unsigned u = __float_as_uint(x);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  const unsigned v = __float_as_uint(x);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+}
+
+// Inclusive prefix sum over the lanes of a wave: within each row of 16 by
+// shifted adds, then the totals of the earlier rows.
+__device__ __forceinline__ double wave_scan_valu(double x, int lane) {
+  x += dpp_f64<kDppRowShr(1)>(x);
+  x += dpp_f64<kDppRowShr(2)>(x);
+  x += dpp_f64<kDppRowShr(4)>(x);
+  x += dpp_f64<kDppRowShr(8)>(x);
+  const auto row_total = [&](int l) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), l),
+                            __builtin_amdgcn_readlane(__double2loint(x), l));
+  };
+  const double r0 = row_total(15), r1 = row_total(31), r2 = row_total(47);
+  if (lane >= 16) x += r0;
+  if (lane >= 32) x += r1;
+  if (lane >= 48) x += r2;
+  return x;
+}
+
 // Block-wide float64 sum for kWalkThreads threads; every thread gets it.
 __device__ double block_sum_f64(double x, double* s_red) {
-  x = tv::wave_sum_f64(x);
+  x = wave_sum_valu(x);
   const int tid = threadIdx.x;
   __syncthreads();
   if ((tid & 63) == 0) s_red[tid >> 6] = x;
@@ -398,7 +493,7 @@ __device__ int walk_prologue(WalkShared& sh, const StatPart* part, int S,
                              const int32_t* tokens, const int32_t* parent, int n, int T,
                              int V, double tau, int b, int32_t* accept_len, int32_t* path,
                              int32_t* bonus, uint8_t* accept_mask, int8_t* decision,
-                             int32_t* row_status, bool merge = true) {
+                             int32_t* row_status) {
   const int tid = threadIdx.x;
   const int st = validate_seq(parent, tokens, n, T, V, b, &sh.flags);
   const int64_t rbase = static_cast<int64_t>(b) * T;
@@ -416,15 +511,13 @@ __device__ int walk_prologue(WalkShared& sh, const StatPart* part, int S,
     return st == TV_ROW_OK ? -1 : st;
   }
   if (tid < n) {
-    if (merge) {
-      const StatPart* pp = part + (rbase + tid) * S;
-      double M = pp[0].m;
-      for (int s = 1; s < S; ++s) M = fmax(M, pp[s].m);
-      double Z = 0.0;
-      for (int s = 0; s < S; ++s) Z += pp[s].z * exp((pp[s].m - M) / tau);
-      sh.m[tid] = M;
-      sh.z[tid] = Z;
-    }
+    const StatPart* pp = part + (rbase + tid) * S;
+    double M = pp[0].m;
+    for (int s = 1; s < S; ++s) M = fmax(M, pp[s].m);
+    double Z = 0.0;
+    for (int s = 0; s < S; ++s) Z += pp[s].z * exp((pp[s].m - M) / tau);
+    sh.m[tid] = M;
+    sh.z[tid] = Z;
     sh.par[tid] = tid == 0 ? -1 : parent[rbase + tid];
     sh.tok[tid] = tokens[rbase + tid];
   }
@@ -480,19 +573,6 @@ __device__ void walk_finish(const WalkShared& sh, int plen, int bon, int T, int 
   }
 }
 
-// One halving step of the per-wave slot reduction: lanes with bit O set keep
-// the upper M partial sums and hand the lower M to the partner lane^O.
-template <int M, int O, int N>
-__device__ __forceinline__ void slot_fold(double (&a)[N], int lane) {
-  const bool up = (lane & O) != 0;
-#pragma unroll
-  for (int i = 0; i < M; ++i) {
-    const double send = up ? a[i] : a[i + M];
-    const double keep = up ? a[i + M] : a[i];
-    a[i] = keep + __shfl_xor(send, O);
-  }
-}
-
 // dst[k] = row[k * kWalkThreads + threadIdx.x] for a row of V entries, with
 // entries at or past V read as zero by the buffer's range check (no memory
 // access), so the loads of a row need no per-lane predicate and are all in
@@ -515,194 +595,81 @@ __device__ __forceinline__ void load_blocks(const E* row, int V, E (&dst)[kRegSl
   }
 }
 
-typedef unsigned int v2u32_t __attribute__((ext_vector_type(2)));
+// --------------------------------------- sampling, one workgroup per node ---
+// For V <= kRegSlots * kWalkThreads the walk is taken apart by tree node.
+// Its result is fixed by two facts per node j: which child of j the walk
+// accepts if it reaches j, and which bonus token it draws if it stops at j.
+// Both depend on node j's rows alone (p_j, then the draft rows of j's
+// children in ascending order), so one workgroup per (sequence, node) finds
+// them for every live node at once, from registers, and a small second
+// kernel follows the accepted children from the root. Nodes off the final
+// path are evaluated too: every live logits row and every tested draft row
+// is read once; nothing is written per vocabulary entry.
 
-// row[k * kWalkThreads + threadIdx.x] = src[k], stores at or past V dropped
-// by the buffer's range check.
-__device__ __forceinline__ void store_blocks(double* row, int V, const double (&src)[kRegSlots]) {
-  const auto rs = __builtin_amdgcn_make_buffer_rsrc(row, 0, V * 8, 0x00020000);
-  int off = threadIdx.x * 8;
-  asm volatile("" : "+v"(off));
-#pragma unroll
-  for (int k = 0; k < kRegSlots; ++k)
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32_t, src[k]), rs,
-                                          off + k * kWalkThreads * 8, 0, 0);
+// The thread index and V through an empty asm: per-slot indices formed from
+// these copies are recomputed where they are used instead of being shared
+// across the kernel (32 of them would stay in registers throughout).
+__device__ __forceinline__ int opaque_v(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ int opaque_s(int x) {
+  asm volatile("" : "+s"(x));
+  return x;
 }
 
-// Walk for V <= kRegSlots * kWalkThreads. Thread t owns the entries
-// x = k * kWalkThreads + t (slot k). The residual r is either p_cur
-// (implicit: the stored exp terms of the row times its per-slice factor) or
-// held unnormalised in one of two float64 buffers of V entries, the
-// distribution being r * inv. Every pass loads all of a thread's slots at
-// once, so a row is one round trip: a test costs one load of q_c's row, a
-// rejection one store of the new residual and one block reduction, an
-// acceptance nothing but the switch to the new row.
-__global__ __launch_bounds__(kWalkThreads) void sample_walk_one_kernel(
-    const StatPart* __restrict__ part, int S, const float* __restrict__ q, int64_t qstride,
-    const float* __restrict__ u, double tau, const int32_t* __restrict__ tokens,
-    const int32_t* __restrict__ parent, const int32_t* __restrict__ n_nodes, int T, int V,
-    const double* __restrict__ ebuf, double* __restrict__ resid, int32_t* accept_len,
-    int32_t* path, int32_t* bonus, uint8_t* accept_mask, int8_t* decision,
-    int32_t* row_status) {
-  __shared__ WalkShared sh;
-  __shared__ double s_tab[kRegSlots * (kWalkThreads / 64)];
-  constexpr int kSlices = kRegSlots * kWalkThreads / kSliceSample;  // slices of a row, at most
-  __shared__ double s_pscale[TV_MAX_TREE * kSlices];  // per (row, slice) factor of p_row
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = n_nodes[b];
-  if (walk_prologue(sh, part, S, tokens, parent, n, T, V, tau, b, accept_len, path, bonus,
-                    accept_mask, decision, row_status, false) != TV_ROW_OK)
-    return;
-  const int64_t rbase = static_cast<int64_t>(b) * T;
-  // Every row's per-slice factors exp((m_s - M) / tau) / Z up front (slices
-  // past S get 0), so no exp is evaluated inside the walk: a group of kSlices
-  // lanes per row merges the row's slice statistics (max, then the sum of
-  // z_s exp((m_s - M) / tau)) with shuffles.
-  static_assert(kSlices <= 64 && (kSlices & (kSlices - 1)) == 0, "row groups within a wave");
-  for (int r0 = 0; r0 < n; r0 += kWalkThreads / kSlices) {
-    const int row = r0 + tid / kSlices, sl = tid % kSlices;
-    const bool live = row < n && sl < S;
-    StatPart ps{-INFINITY, 0.0};
-    if (live) ps = part[(rbase + row) * S + sl];
-    double M = ps.m;
-#pragma unroll
-    for (int o = 1; o < kSlices; o <<= 1) M = fmax(M, __shfl_xor(M, o));
-    const double f = live ? exp((ps.m - M) / tau) : 0.0;
-    double Z = ps.z * f;
-#pragma unroll
-    for (int o = 1; o < kSlices; o <<= 1) Z += __shfl_xor(Z, o);
-    if (row < n) s_pscale[row * kSlices + sl] = f / Z;
-  }
-  __syncthreads();
-  // Parents of rows lane and lane + 64, for the ballots of next_child.
-  static_assert(TV_MAX_TREE <= 128, "two parent words per lane");
-  const int par_lo = lane < n ? sh.par[lane] : -2;
-  const int par_hi = lane + 64 < n ? sh.par[lane + 64] : -2;
-  double* buf[2] = {resid + static_cast<int64_t>(b) * 2 * V,
-                    resid + static_cast<int64_t>(b) * 2 * V + V};
-  int cur = 0, len = 0, held = -1;  // held: buffer holding r, -1 = implicit p_cur
-  double inv = 1.0;
-  // All of this thread's entries of r (times inv when held >= 0).
-  auto load_r = [&](double (&rv)[kRegSlots]) __attribute__((always_inline)) {
-    if (held < 0) {
-      const int ru = __builtin_amdgcn_readfirstlane(cur);
-      load_blocks(ebuf + (rbase + ru) * V, V, rv);
-      const double* f = s_pscale + ru * kSlices;
-#pragma unroll
-      for (int k = 0; k < kRegSlots; ++k) rv[k] *= f[k / (kSliceSample / kWalkThreads)];
-    } else {
-      load_blocks(buf[held], V, rv);
-    }
-  };
-  // First child of `par` at index >= from (n when there is none): two
-  // wave ballots over the parent words.
-  auto next_child = [&](int from, int par) {
-    const unsigned long long lo = __ballot(par_lo == par && lane >= from);
-    if (lo) return __ffsll(lo) - 1;
-    const unsigned long long hi = __ballot(par_hi == par && lane + 64 >= from);
-    return hi ? 64 + __ffsll(hi) - 1 : n;
-  };
-  int c = next_child(1, 0);
-  // rv holds this thread's entries of r (times inv when held >= 0); after a
-  // rejection with a positive sum they stay in registers (in_regs), so the
-  // next test reloads nothing but q_c's row.
-  double rv[kRegSlots];
-  bool in_regs = false;
-  while (c < n) {
-    const int x = sh.tok[c];
-    // The whole pass's loads go out before the test, which the owner of x
-    // runs on its own copies.
-    float qv[kRegSlots];
-    if (!in_regs) load_r(rv);
-    load_blocks(q + (rbase + __builtin_amdgcn_readfirstlane(c)) * qstride, V, qv);
-    if (tid == (x & (kWalkThreads - 1))) {
-      const int ks = x / kWalkThreads;
-      double rx = 0.0;
-      float qx = 0.f;
-#pragma unroll
-      for (int k = 0; k < kRegSlots; ++k) {
-        rx = k == ks ? rv[k] : rx;
-        qx = k == ks ? qv[k] : qx;
-      }
-      const int acc = accept_test(rx * inv, qx, u[rbase + c]);
-      decision[rbase + c] = static_cast<int8_t>(acc);
-      sh.accept = acc;
-    }
-    __syncthreads();
-    // Both branches pass a barrier before the next test writes sh.accept.
-    if (sh.accept) {
-      ++len;  // uniform: every thread follows the same walk
-      if (tid == 0) sh.path[len] = c;
-      cur = c;
-      held = -1;
-      inv = 1.0;
-      in_regs = false;
-      c = next_child(c + 1, cur);
-      __syncthreads();
-      continue;
-    }
-    // Rejected: r <- max(r inv - q_c, 0) into the free buffer, inv <- 1 /
-    // its sum; a zero sum keeps the old r (reloaded from where it was, as
-    // the registers now hold zeros).
-    const int dst = held == 0 ? 1 : 0;
-    double part_sum = 0.0;
-#pragma unroll
-    for (int k = 0; k < kRegSlots; ++k) {
-      const double d = fmax(fma(rv[k], inv, -static_cast<double>(qv[k])), 0.0);
-      part_sum += d;
-      rv[k] = d;
-    }
-    store_blocks(buf[dst], V, rv);
-    const double tot = block_sum_f64(part_sum, sh.red);
-    if (tot > 0.0) {
-      held = dst;
-      inv = 1.0 / tot;
-    }
-    in_regs = tot > 0.0;
-    c = next_child(c + 1, cur);
-  }
+struct NodeShared {
+  double exp_tab[256];  // 2^(i / 256)
+  float mx[kWalkThreads / 64];
+  double red[kWalkThreads / 64];
+  double tab[kRegSlots * (kWalkThreads / 64)];  // per (slot, wave) sums of r
+  double base, thr;
+  int accept;
+  int hit;
+  int cand;
+};
 
-  // Bonus: smallest x with sum_{y<=x} r(y) > u0 * sum_y r(y). Index order is
-  // slot-major, then wave, then lane. (1) Each wave folds its 32 slots to
-  // per-(slot, wave) sums; (2) wave 0 scans the 512 sums in index order and
-  // finds the first block whose running sum passes the threshold; (3) that
-  // block's wave scans its 64 entries from the block's starting sum.
-  if (!in_regs) load_r(rv);
-  {
-    constexpr int H = kRegSlots / 2;
-    double a[H];
-    const bool up = (lane & 32) != 0;
+// Inverse-CDF draw from r, given as this thread's slots (entry
+// k * kWalkThreads + threadIdx.x in rv[k], zero past V): the smallest x with
+// sum_{y<=x} r(y) > u0 * sum_y r(y). Index order is slot-major, then wave,
+// then lane. (1) Each wave folds its slots to per-(slot, wave) sums; (2) wave
+// 0 scans those sums in index order and finds the first block whose running
+// sum passes the threshold; (3) that block's wave scans its 64 entries from
+// the block's starting sum. Every thread returns the token.
+__device__ int inverse_cdf_draw(const double (&rv)[kRegSlots], double u0, NodeShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Eight slots at a time: after the exchanges across lane bits 5, 4 and 3
+  // each lane holds a partial sum of slot c0 + (lane >> 3), which three more
+  // exchanges complete over the wave.
 #pragma unroll
-    for (int i = 0; i < H; ++i)
-      a[i] = (up ? rv[i + H] : rv[i]) + __shfl_xor(up ? rv[i] : rv[i + H], 32);
-    slot_fold<8, 16>(a, lane);
-    slot_fold<4, 8>(a, lane);
-    slot_fold<2, 4>(a, lane);
-    slot_fold<1, 2>(a, lane);
-    const double tot = a[0] + __shfl_xor(a[0], 1);  // slot lane >> 1 of this wave
-    if ((lane & 1) == 0) s_tab[(lane >> 1) * (kWalkThreads / 64) + wave] = tot;
+  for (int c0 = 0; c0 < kRegSlots; c0 += 8) {
+    double a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = swap32_sum(rv[c0 + i], rv[c0 + i + 4]);
+    a[0] = swap16_sum(a[0], a[2]);
+    a[1] = swap16_sum(a[1], a[3]);
+    const bool up = (lane & 8) != 0;
+    double t = (up ? a[1] : a[0]) + dpp_f64<kDppRowRor8>(up ? a[0] : a[1]);
+    t += dpp_f64<kDppHalfMirror>(t);
+    t += dpp_f64<kDppXor2>(t);
+    t += dpp_f64<kDppXor1>(t);
+    if ((lane & 7) == 0) sh.tab[(c0 + (lane >> 3)) * (kWalkThreads / 64) + wave] = t;
   }
   __syncthreads();
-  const double u0 = static_cast<double>(u[rbase]);
   constexpr int kPer = kRegSlots * (kWalkThreads / 64) / 64;  // table entries per lane
   if (wave == 0) {
     double loc[kPer];
     double lt = 0.0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      loc[j] = s_tab[lane * kPer + j];
+      loc[j] = sh.tab[lane * kPer + j];
       lt += loc[j];
     }
-    double inc = lt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
-    }
-    const double total = __shfl(inc, 63);
+    const double inc = wave_scan_valu(lt, lane);
+    const double total = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(inc), 63),
+                                          __builtin_amdgcn_readlane(__double2loint(inc), 63));
     const double thr = u0 * total;
-    double p = __shfl_up(inc, 1);
+    double p = __shfl_up(inc, 1);  // exclusive prefix
     if (lane == 0) p = 0.0;
     int hit = -1;
     double base = 0.0;
@@ -733,13 +700,7 @@ __global__ __launch_bounds__(kWalkThreads) void sample_walk_one_kernel(
       double val = 0.0;
 #pragma unroll
       for (int k = 0; k < kRegSlots; ++k) val = k == ks ? rv[k] : val;
-      double inc = val;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const double y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
-      }
-      const double run = sh.base + inc;
+      const double run = sh.base + wave_scan_valu(val, lane);
       const unsigned long long m = __ballot(run > sh.thr);
       int pick;
       if (m) {
@@ -756,13 +717,342 @@ __global__ __launch_bounds__(kWalkThreads) void sample_walk_one_kernel(
     // Rounding left the threshold above every running sum (u0 within an ulp
     // of 1): take the last token with positive mass.
     int last = -1;
+    const int t = opaque_v(tid);
 #pragma unroll
     for (int k = 0; k < kRegSlots; ++k)
-      if (rv[k] > 0.0) last = k * kWalkThreads + tid;
+      if (rv[k] > 0.0) last = k * kWalkThreads + t;
     if (last >= 0) atomicMax(&sh.cand, last);
   }
   __syncthreads();
-  walk_finish(sh, len, sh.cand, T, b, accept_len, path, bonus, accept_mask, row_status);
+  return sh.cand;
+}
+
+// exp(y ln 2 / 256) for the row terms, table-driven: with y = N + f (N the
+// nearest integer, |f| <= 1/2), exp = 2^floor(N / 256) * 2^((N mod 256) /
+// 256) * exp(f ln 2 / 256); the last factor minus one is its Taylor series
+// in f to the fourth power (|f ln 2 / 256| <= ln 2 / 512, truncation below
+// 4e-17 relative), coefficients (ln 2 / 256)^k / k!. N is read from the low
+// word of y + 1.5 * 2^52; the power of two is applied by ldexp, which rounds
+// subnormal results and underflows to 0 (y is clamped at -2^19, far below
+// the range, so -inf gives 0); results past the range are +inf. Relative
+// error a few units of 2^-52 for normal results.
+constexpr double kExpScale = 369.3299304675746;   // 256 / ln 2
+constexpr double kExpC1 = 0.0027076061740622863;  // ln 2 / 256
+constexpr double kExpC2 = 3.6655655969101062e-06;  // (ln 2 / 256)^2 / 2
+constexpr double kExpC3 = 3.3083026805413713e-09;  // (ln 2 / 256)^3 / 6
+constexpr double kExpC4 = 2.239395190875157e-12;   // (ln 2 / 256)^4 / 24
+constexpr double kExpRound = 6755399441055744.0;  // 1.5 * 2^52
+
+// The table-free part of exp_scaled: the table index N (low word) and the
+// polynomial factor, for y = arg.
+__device__ __forceinline__ double exp_reduce(double y, int& nn) {
+  y = fmax(y, -524288.0);
+  const double yr = y + kExpRound;
+  nn = __double2loint(yr);
+  const double f = y - (yr - kExpRound);
+  return f * fma(f, fma(f, fma(f, kExpC4, kExpC3), kExpC2), kExpC1);
+}
+
+// The rest: table entry sc = 2^((N mod 256) / 256), power 2^floor(N / 256).
+__device__ __forceinline__ double exp_finish(double sc, double pr, int nn) {
+  return __builtin_amdgcn_ldexp(fma(sc, pr, sc), nn >> 8);
+}
+
+// HBM -> LDS copy of a row in the slot layout (entry k * kWalkThreads + t at
+// s_row[k * kWalkThreads + t]), no register staging: each wave's load of a
+// slot fills 64 consecutive floats. Entries at or past V are not read (the
+// buffer's range check); the caller waits with vmcnt(0) and a barrier.
+__device__ __forceinline__ void row_to_lds(const float* row, int V, float* s_row) {
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, V * 4, 0x00020000);
+  // The wave's first thread index, as a scalar (the LDS address of each
+  // copy is wave-uniform).
+  const int wave_base = __builtin_amdgcn_readfirstlane(threadIdx.x & ~63);
+  const int off = static_cast<int>(threadIdx.x) * 4;
+  // The slot's byte offset goes in the scalar offset, so the lane offset is
+  // the only vector register the copies need.
+#pragma unroll
+  for (int k = 0; k < kRegSlots; ++k)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(s_row + k * kWalkThreads + wave_base), 4,
+        off, k * kWalkThreads * 4, 0, 0);
+}
+
+// Waits until at most n vector-memory operations of this wave are in
+// flight (expcnt and lgkmcnt not waited on).
+#define TV_ACCEPT_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14))
+#define TV_ACCEPT_WAIT_VMCNT0() TV_ACCEPT_WAIT_VMCNT(0)
+
+// Workgroup barrier that waits for this wave's LDS operations only, so that
+// global loads and HBM -> LDS copies stay in flight across it.
+__device__ __forceinline__ void lds_only_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+
+// One workgroup per live (sequence b, node j); thread t owns the entries
+// x = k * kWalkThreads + t (slot k) of every row it touches. p_j is formed in
+// registers as e(x) = exp((l(x) - max l) / tau) with the factor 1 / sum e;
+// the children of j are then tested in ascending index exactly as the walk
+// tests them at j. The residual stays in registers as r = rv * inv (rv
+// unnormalised): a test is one lookup by the owner of x, a rejection copies
+// q_c's row into LDS, sums max(r - q_c, 0) in one pass and keeps it in a
+// second once the sum is known to be positive (a zero sum keeps r
+// unchanged). Outputs per node: node_next (the accepted child, -1 if none),
+// node_dec for each child of j (+1, 0, or -1 when never reached) and, when
+// no child is accepted, node_bonus (the draw from the final r with u[b][0]).
+__global__ __launch_bounds__(kWalkThreads) void sample_node_kernel(
+    const float* __restrict__ logits, int64_t stride, double inv_tau,
+    const float* __restrict__ q, int64_t qstride, const float* __restrict__ u,
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ parent,
+    const int32_t* __restrict__ n_nodes, int T, int V, int8_t* __restrict__ node_dec,
+    int32_t* __restrict__ node_next, int32_t* __restrict__ node_bonus) {
+  __shared__ NodeShared sh;
+  // The logits row, then the draft row of the child under test (slot
+  // layout). Entries at or past V are zeroed once and never written by the
+  // row copies.
+  __shared__ float s_row[kRegSlots * kWalkThreads];
+  const int j = blockIdx.x, b = blockIdx.y;
+  if (!live_row(n_nodes, T, b, j)) return;
+  const int n = n_nodes[b];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t rbase = static_cast<int64_t>(b) * T;
+  // Parents of rows lane and lane + 64 (-2 where there is no such child).
+  static_assert(TV_MAX_TREE <= 128, "two parent words per lane");
+  const int par_lo = lane >= 1 && lane < n ? parent[rbase + lane] : -2;
+  const int par_hi = lane + 64 < n ? parent[rbase + lane + 64] : -2;
+  // First child of j at index >= from (n when there is none).
+  auto next_child = [&](int from) {
+    const unsigned long long lo = __ballot(par_lo == j && lane >= from);
+    if (lo) return __ffsll(lo) - 1;
+    const unsigned long long hi = __ballot(par_hi == j && lane + 64 >= from);
+    return hi ? 64 + __ffsll(hi) - 1 : n;
+  };
+  // The test of child c needs only q_c(x_c): its owner requests that one
+  // value ahead; q_c's row is read only after c is rejected.
+  auto token_of = [&](int cc) { return cc < n ? tokens[rbase + cc] : -1; };
+  auto owner_of = [&](int xx) { return xx >= 0 && xx < V ? (xx & (kWalkThreads - 1)) : 0; };
+  auto probe = [&](int cc, int xx) {
+    return cc < n && xx >= 0 && xx < V && tid == owner_of(xx)
+               ? q[(rbase + cc) * qstride + xx]
+               : 0.f;
+  };
+  int c = next_child(1);
+  int x = token_of(c);
+  float qx = probe(c, x);
+  const float* lrow = logits + (rbase + j) * stride;
+  if (tid < 256) sh.exp_tab[tid] = exp2(tid * (1.0 / 256.0));
+  {
+    const int t = opaque_v(tid), vv = opaque_s(V);
+#pragma unroll
+    for (int k = 0; k < kRegSlots; ++k)
+      if (k * kWalkThreads + kWalkThreads > vv && k * kWalkThreads + t >= vv)
+        s_row[k * kWalkThreads + t] = 0.f;
+  }
+  // The logits row is loaded into registers and its terms are formed slot
+  // by slot as the loads land (the compiler waits for each slot's load
+  // alone), against a reference m0 known before the whole row has arrived:
+  // the largest logit of slot 0. Every ratio the walk uses is of two terms
+  // of one row (p_j = e / sum e), so the common factor exp((max - m0) /
+  // tau) cancels. If a term overflows (a logit more than ~700 tau above m0)
+  // the sums are not finite and the row goes round again with its maximum
+  // as reference.
+  const double ky = inv_tau * kExpScale;
+  double rv[kRegSlots];
+  double z = 0.0;
+  float m0 = -INFINITY;
+#pragma nounroll
+  for (int round = 0; round < 2; ++round) {
+    float lv[kRegSlots];
+    load_blocks(lrow, V, lv);
+    float mr = tid < V ? lv[0] : -INFINITY;
+    if (round == 1)  // the row maximum (a separate pass over the row)
+      for (int v = tid + kWalkThreads; v < V; v += kWalkThreads) mr = fmaxf(mr, lrow[v]);
+    // Barriers on LDS only: the rest of the row is still in flight.
+    mr = wave_max_valu(mr);
+    if (lane == 0) sh.mx[wave] = mr;
+    lds_only_barrier();
+    m0 = sh.mx[0];
+    for (int w = 1; w < kWalkThreads / 64; ++w) m0 = fmaxf(m0, sh.mx[w]);
+    lds_only_barrier();  // sh.mx is written again below
+    // y = (l - m0) / tau * 256 / ln 2 as one fused step.
+    const double nky = -static_cast<double>(m0) * ky;
+    const int t = opaque_v(tid), vv = opaque_s(V);
+    z = 0.0;
+    // Logit of slot k; entries past V (only in the slots that reach V, a
+    // uniform test) read as -inf, whose term is 0.
+    auto logit = [&](int k) {
+      float l = lv[k];
+      if (__builtin_expect(k * kWalkThreads + kWalkThreads > vv, 0)) {
+        if (k * kWalkThreads + t >= vv) l = -INFINITY;
+      }
+      return static_cast<double>(l);
+    };
+    // Two-stage pipeline over the slots: the table read of slot k + 1 is
+    // in flight while slot k is finished.
+    int nn_n;
+    double pr_n = exp_reduce(fma(logit(0), ky, nky), nn_n);
+    double sc_n = sh.exp_tab[nn_n & 255];
+#pragma unroll
+    for (int k = 0; k < kRegSlots; ++k) {
+      const int nn = nn_n;
+      const double pr = pr_n, sc = sc_n;
+      if (k + 1 < kRegSlots) {
+        pr_n = exp_reduce(fma(logit(k + 1), ky, nky), nn_n);
+        sc_n = sh.exp_tab[nn_n & 255];
+      }
+      const double e = exp_finish(sc, pr, nn);
+      rv[k] = e;
+      z += e;
+      // Settle this slot's sum here: left to the compiler, the rest of each
+      // term's evaluation sinks below the loop and every slot's
+      // intermediates stay alive until then.
+      asm volatile("" : "+v"(z));
+    }
+    const bool again = __syncthreads_or(!(z < INFINITY));
+    if (!again || round == 1) break;
+  }
+  // The first child's draft row goes to LDS while the sum and the first
+  // test run (it is read only if that child is rejected). Issued after the
+  // logits, so that the waits for the logits never wait for it.
+  if (c < n) row_to_lds(q + (rbase + c) * qstride, V, s_row);
+  double inv = 1.0 / block_sum_f64(z, sh.red);
+
+  int accepted = -1;
+  bool first = true;  // c is the first child: its row is in LDS already
+  while (c < n) {
+    const bool x_ok = x >= 0 && x < V;
+    if (tid == owner_of(x)) {
+      int acc = 0;
+      if (x_ok) {
+        const int ks = x / kWalkThreads;
+        double rx = 0.0;
+#pragma unroll
+        for (int k = 0; k < kRegSlots; ++k) rx = k == ks ? rv[k] : rx;
+        acc = accept_test(rx * inv, qx, u[rbase + c]);
+      }
+      node_dec[rbase + c] = static_cast<int8_t>(acc);
+      sh.accept = acc;
+    }
+    // This barrier also ends every read of s_row before the copy below
+    // overwrites it.
+    __syncthreads();
+    // Every thread reads sh.accept before the barrier inside block_sum_f64,
+    // which the next test's write comes after.
+    if (sh.accept) {
+      accepted = c;
+      break;
+    }
+    if (!first) row_to_lds(q + (rbase + c) * qstride, V, s_row);
+    first = false;
+    const int cn = next_child(c + 1);
+    x = token_of(cn);
+    qx = probe(cn, x);
+    TV_ACCEPT_WAIT_VMCNT0();
+    __syncthreads();
+    double part_sum = 0.0;
+#pragma unroll
+    for (int k = 0; k < kRegSlots; ++k)
+      part_sum += fmax(fma(rv[k], inv, -static_cast<double>(s_row[k * kWalkThreads + tid])), 0.0);
+    const double tot = block_sum_f64(part_sum, sh.red);
+    if (tot > 0.0) {
+#pragma unroll
+      for (int k = 0; k < kRegSlots; ++k)
+        rv[k] = fmax(fma(rv[k], inv, -static_cast<double>(s_row[k * kWalkThreads + tid])), 0.0);
+      inv = 1.0 / tot;
+    }
+    c = cn;
+  }
+  if (tid == 0) node_next[rbase + j] = accepted;
+  if (accepted >= 0) {
+    // The children after the accepted one are never tested.
+    if (tid > accepted && tid < n && parent[rbase + tid] == j) node_dec[rbase + tid] = -1;
+    return;
+  }
+  const int bon = inverse_cdf_draw(rv, static_cast<double>(u[rbase]), sh);
+  if (tid == 0) node_bonus[rbase + j] = bon;
+}
+
+// One workgroup per sequence (one thread per tree row): validates the
+// sequence, follows node_next from the root and writes the outputs. A
+// child's decision is reported when its parent lies on the path (those are
+// the tests the walk makes); every other entry is -1.
+__global__ __launch_bounds__(TV_MAX_TREE) void sample_path_kernel(
+    const int8_t* __restrict__ node_dec, const int32_t* __restrict__ node_next,
+    const int32_t* __restrict__ node_bonus, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ parent, const int32_t* __restrict__ n_nodes, int T, int V,
+    int32_t* accept_len, int32_t* path, int32_t* bonus, uint8_t* accept_mask,
+    int8_t* decision, int32_t* row_status) {
+  __shared__ int s_flags, s_len, s_end;
+  __shared__ int s_next[TV_MAX_TREE], s_path[TV_MAX_TREE], s_on[TV_MAX_TREE];
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const int64_t row = static_cast<int64_t>(b) * T + i;
+  const bool in_t = i < T;
+  const int n = n_nodes[b];
+  const bool n_ok = n >= 0 && n <= T;
+  const bool live = n_ok && i < n;
+  // Every load is issued before the first barrier; rows of a sequence that
+  // fails validation are read (in bounds) but unused.
+  const int pr = live && i > 0 ? parent[row] : -1;
+  const int tk = live && i > 0 ? tokens[row] : 0;
+  const int nx = live ? node_next[row] : -1;
+  const int dc = live && i > 0 ? node_dec[row] : -1;
+  if (i == 0) s_flags = 0;
+  __syncthreads();
+  int f = 0;
+  if (live && i > 0) {
+    if (pr < 0 || pr >= i) f |= 1;
+    if (tk < 0 || tk >= V) f |= 2;
+  }
+  if (f) atomicOr(&s_flags, f);
+  if (in_t) {
+    s_next[i] = nx;
+    s_path[i] = -1;
+    s_on[i] = 0;
+  }
+  __syncthreads();
+  const int flags = s_flags;
+  const int st = !n_ok ? TV_ROW_NNODES
+                       : ((flags & 1) ? TV_ROW_BAD_PARENT
+                                      : ((flags & 2) ? TV_ROW_BAD_TOKEN : TV_ROW_OK));
+  if (st != TV_ROW_OK || n == 0) {
+    if (in_t) {
+      path[row] = -1;
+      accept_mask[row] = 0;
+      decision[row] = -1;
+    }
+    if (i == 0) {
+      accept_len[b] = 0;
+      bonus[b] = -1;
+      row_status[b] = st;
+    }
+    return;
+  }
+  if (i == 0) {
+    int cur = 0, len = 0;
+    s_path[0] = 0;
+    s_on[0] = 1;
+    // An accepted child lies after its parent, so the walk ends within n.
+    for (int c = s_next[0]; c > cur && c < n; c = s_next[cur]) {
+      s_path[++len] = c;
+      s_on[c] = 1;
+      cur = c;
+    }
+    s_len = len;
+    s_end = cur;
+  }
+  __syncthreads();
+  if (in_t) {
+    path[row] = s_path[i];
+    accept_mask[row] = static_cast<uint8_t>(s_on[i]);
+    decision[row] = static_cast<int8_t>(live && i > 0 && s_on[pr] ? dc : -1);
+  }
+  if (i == 0) {
+    accept_len[b] = s_len;
+    bonus[b] = node_bonus[static_cast<int64_t>(b) * T + s_end];
+    row_status[b] = TV_ROW_OK;
+  }
 }
 
 // Walk for larger vocabularies: the residual r lives in one of two float64
@@ -943,9 +1233,17 @@ size_t greedy_ws(int B, int T, int V) {
 // Vocabularies the one-round-trip walk covers.
 bool sample_one_pass(int V) { return V <= kRegSlots * kWalkThreads; }
 
-// Sampling workspace: slice statistics, the stored exp terms of every row
-// (float64, B T V) and two float64 residual buffers per sequence.
+// Sampling workspace. Vocabularies of the node-parallel path: per node the
+// accepted child, the bonus draw (int32 each) and the decision byte. Larger
+// ones: slice statistics, the stored exp terms of every row (float64, B T V)
+// and two float64 residual buffers per sequence.
+size_t node_ws(int B, int T) {
+  return 2 * tvh::align_up(static_cast<size_t>(B) * T * sizeof(int32_t), 256) +
+         tvh::align_up(static_cast<size_t>(B) * T, 256);
+}
+
 size_t sample_ws(int B, int T, int V) {
+  if (sample_one_pass(V)) return node_ws(B, T);
   return tvh::align_up(static_cast<size_t>(B) * T * sample_splits(V) * sizeof(StatPart), 256) +
          tvh::align_up(static_cast<size_t>(B) * T * V * sizeof(double), 256) +
          tvh::align_up(static_cast<size_t>(B) * 2 * V * sizeof(double), 256);
@@ -1063,7 +1361,8 @@ extern "C" int tv_accept_sample(const float* logits, int64_t logits_row_stride,
   if (!logits || !q || !u || !tokens || !parent || !n_nodes || !accept_len || !path || !bonus ||
       !accept_mask || !decision || !row_status)
     return TV_ERR_NULL;
-  if (!accept_sizes_ok(B, T, V) || logits_row_stride < V || q_row_stride < V)
+  // B is a grid dimension of every launch (at most 65535).
+  if (!accept_sizes_ok(B, T, V) || B > 65535 || logits_row_stride < V || q_row_stride < V)
     return TV_ERR_SHAPE;
   if (!(temperature > 0.f)) return TV_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(logits) & 3u) || (reinterpret_cast<uintptr_t>(q) & 3u))
@@ -1071,24 +1370,31 @@ extern "C" int tv_accept_sample(const float* logits, int64_t logits_row_stride,
   if (B == 0) return TV_OK;
   if (!workspace || ws_bytes < sample_ws(B, T, V) || !tvh::aligned256(workspace))
     return TV_ERR_WORKSPACE;
+  const double tau = static_cast<double>(temperature);
+  char* ws = static_cast<char*>(workspace);
+  if (sample_one_pass(V)) {
+    const size_t words = tvh::align_up(static_cast<size_t>(B) * T * sizeof(int32_t), 256);
+    int32_t* node_next = reinterpret_cast<int32_t*>(ws);
+    int32_t* node_bonus = reinterpret_cast<int32_t*>(ws + words);
+    int8_t* node_dec = reinterpret_cast<int8_t*>(ws + 2 * words);
+    hipLaunchKernelGGL(sample_node_kernel, dim3(T, B), dim3(kWalkThreads), 0, stream, logits,
+                       logits_row_stride, 1.0 / tau, q, q_row_stride, u, tokens, parent, n_nodes,
+                       T, V, node_dec, node_next, node_bonus);
+    hipLaunchKernelGGL(sample_path_kernel, dim3(B), dim3(TV_MAX_TREE), 0, stream, node_dec,
+                       node_next, node_bonus, tokens, parent, n_nodes, T, V, accept_len, path,
+                       bonus, accept_mask, decision, row_status);
+    return tvh::launch_status();
+  }
   const int S = sample_splits(V);
   StatPart* part = static_cast<StatPart*>(workspace);
-  char* base = static_cast<char*>(workspace) +
-               tvh::align_up(static_cast<size_t>(B) * T * S * sizeof(StatPart), 256);
+  char* base = ws + tvh::align_up(static_cast<size_t>(B) * T * S * sizeof(StatPart), 256);
   double* ebuf = reinterpret_cast<double*>(base);
-  const double tau = static_cast<double>(temperature);
   hipLaunchKernelGGL(softmax_slices_kernel, dim3(S, T, B), dim3(kThreads), 0, stream, logits,
                      logits_row_stride, n_nodes, T, V, S, 1.0 / tau, part, ebuf);
   double* resid = reinterpret_cast<double*>(
       base + tvh::align_up(static_cast<size_t>(B) * T * V * sizeof(double), 256));
-  if (sample_one_pass(V)) {
-    hipLaunchKernelGGL(sample_walk_one_kernel, dim3(B), dim3(kWalkThreads), 0, stream, part, S,
-                       q, q_row_stride, u, tau, tokens, parent, n_nodes, T, V, ebuf, resid,
-                       accept_len, path, bonus, accept_mask, decision, row_status);
-  } else {
-    hipLaunchKernelGGL(sample_walk_kernel, dim3(B), dim3(kWalkThreads), 0, stream, part, S, q,
-                       q_row_stride, u, tau, tokens, parent, n_nodes, T, V, ebuf, resid,
-                       accept_len, path, bonus, accept_mask, decision, row_status);
-  }
+  hipLaunchKernelGGL(sample_walk_kernel, dim3(B), dim3(kWalkThreads), 0, stream, part, S, q,
+                     q_row_stride, u, tau, tokens, parent, n_nodes, T, V, ebuf, resid,
+                     accept_len, path, bonus, accept_mask, decision, row_status);
   return tvh::launch_status();
 }
