@@ -10,16 +10,16 @@
 // of the IluvatarLabs/vllm page "Introduce SCV vectorized masking with
 // graph/adaptive modes".
 //
-// Both modes are two launches:
-//   greedy: a data-parallel pass over the live logits rows, split along the
-//     vocabulary so the whole chip streams the rows once (16-byte loads),
-//     keeps a (max, lowest index) pair per slice; one workgroup per sequence
-//     merges the slices and walks the tree;
-//   sampling (vocabularies up to 32768): one workgroup per live tree node
-//     decides, from that node's rows held in registers, which child the walk
-//     accepts there and which bonus it would draw there; one workgroup per
-//     sequence then follows the accepted children from the root. Larger
-//     vocabularies take a slice-statistics pass and a per-sequence walk.
+// greedy: two launches. A data-parallel pass over the live logits rows,
+//   split along the vocabulary so the whole chip streams the rows once
+//   (16-byte loads), keeps a (max, lowest index) pair per slice; one
+//   workgroup per sequence merges the slices and walks the tree.
+// sampling, vocabularies up to 32768: two launches. One workgroup per live
+//   tree node decides, from that node's rows held in registers, which child
+//   the walk accepts there and which bonus it would draw there; one
+//   workgroup per sequence then follows the accepted children from the
+//   root. Larger vocabularies take a slice-statistics pass and a
+//   per-sequence walk.
 // Sequences with n_nodes == 0 read nothing.
 #include <limits.h>
 
@@ -462,13 +462,22 @@ __device__ __forceinline__ double wave_scan_valu(double x, int lane) {
   return x;
 }
 
+// Workgroup barrier that waits for this wave's LDS operations only, so that
+// global loads and HBM -> LDS copies stay in flight across it.
+__device__ __forceinline__ void lds_only_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Block-wide float64 sum for kWalkThreads threads; every thread gets it.
+// kLdsOnly: the barriers order LDS only (callers that exchange nothing
+// through global memory, and keep copies in flight across the sum).
+template <bool kLdsOnly = false>
 __device__ double block_sum_f64(double x, double* s_red) {
   x = wave_sum_valu(x);
   const int tid = threadIdx.x;
-  __syncthreads();
+  if (kLdsOnly) lds_only_barrier(); else __syncthreads();
   if ((tid & 63) == 0) s_red[tid >> 6] = x;
-  __syncthreads();
+  if (kLdsOnly) lds_only_barrier(); else __syncthreads();
   double t = 0.0;
   for (int w = 0; w < kWalkThreads / 64; ++w) t += s_red[w];
   return t;
@@ -573,25 +582,35 @@ __device__ void walk_finish(const WalkShared& sh, int plen, int bon, int T, int 
   }
 }
 
-// dst[k] = row[k * kWalkThreads + threadIdx.x] for a row of V entries, with
+// Wave-major slot layout of the node-parallel sampling path: wave w of a
+// workgroup owns the vocabulary range [w * kWaveSpan, (w + 1) * kWaveSpan),
+// and slot k of its lane l is entry w * kWaveSpan + 64 k + l (a wave's slot
+// is 64 consecutive entries: coalesced loads and conflict-free LDS access).
+constexpr int kWaveSpan = kRegSlots * 64;
+
+__device__ __forceinline__ int slot_entry(int t, int k) {
+  return (t >> 6) * kWaveSpan + k * 64 + (t & 63);
+}
+
+// dst[k] = row[slot_entry(threadIdx.x, k)] for a row of V entries, with
 // entries at or past V read as zero by the buffer's range check (no memory
 // access), so the loads of a row need no per-lane predicate and are all in
-// flight together. The thread offset passes through an empty asm so that the
-// kRegSlots offsets are formed per call, next to their loads, instead of
-// being kept live across the whole walk.
-template <typename E>
+// flight together. Slots K0 .. K1 - 1 only. The thread offset passes through
+// an empty asm so that it is formed per call, next to its loads.
+template <int K0 = 0, int K1 = kRegSlots, typename E>
 __device__ __forceinline__ void load_blocks(const E* row, int V, E (&dst)[kRegSlots]) {
   const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(row), 0,
                                                     V * static_cast<int>(sizeof(E)), 0x00020000);
-  int off = threadIdx.x * static_cast<int>(sizeof(E));
+  int off = slot_entry(threadIdx.x, 0) * static_cast<int>(sizeof(E));
   asm volatile("" : "+v"(off));
 #pragma unroll
-  for (int k = 0; k < kRegSlots; ++k) {
-    const int o = off + k * kWalkThreads * static_cast<int>(sizeof(E));
+  for (int k = K0; k < K1; ++k) {
+    // The slot's byte offset goes in the scalar offset.
+    const int so = k * 64 * static_cast<int>(sizeof(E));
     if constexpr (sizeof(E) == 8)
-      dst[k] = __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0));
+      dst[k] = __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b64(rs, off, so, 0));
     else
-      dst[k] = __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0));
+      dst[k] = __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b32(rs, off, so, 0));
   }
 }
 
@@ -606,6 +625,40 @@ __device__ __forceinline__ void load_blocks(const E* row, int V, E (&dst)[kRegSl
 // path are evaluated too: every live logits row and every tested draft row
 // is read once; nothing is written per vocabulary entry.
 
+// exp(y ln 2 / 1024) for the row terms, table-driven: with y = N + f (N
+// the nearest integer, |f| <= 1/2), exp = 2^floor(N / 1024) *
+// 2^((N mod 1024) / 1024) * exp(f ln 2 / 1024); the last factor minus one
+// is its Taylor series in f to the cube (|f ln 2 / 1024| <= ln 2 / 2048,
+// truncation below 6e-16 relative), coefficients (ln 2 / 1024)^k / k!. N is
+// read from the low word of y + 1.5 * 2^52 (|y| < 2^31); the power of two is
+// applied by ldexp, which rounds subnormal results and underflows to 0;
+// results past the range are +inf. Relative error a few units of 2^-52 for
+// normal results.
+constexpr int kExpTab = 1024;
+constexpr double kExpScale = 1477.3197218702985;   // 1024 / ln 2
+constexpr double kExpC1 = 0.0006769015435155716;   // ln 2 / 1024
+constexpr double kExpC2 = 2.2909784980688164e-07;  // (ln 2 / 1024)^2 / 2
+constexpr double kExpC3 = 5.1692229383458926e-11;  // (ln 2 / 1024)^3 / 6
+constexpr double kExpRound = 6755399441055744.0;   // 1.5 * 2^52
+// Logits more than this many tau below the reference give a term below
+// 2^-1075 (0 after rounding); they are clamped there.
+constexpr double kExpFloorTau = 752.0;
+
+// The table-free part: the table index N (low word) and the polynomial
+// factor.
+__device__ __forceinline__ double exp_reduce(double y, int& nn) {
+  const double yr = y + kExpRound;
+  nn = __double2loint(yr);
+  const double f = y - (yr - kExpRound);
+  return f * fma(f, fma(f, kExpC3, kExpC2), kExpC1);
+}
+
+// The rest: table entry sc = 2^((N mod 1024) / 1024), power
+// 2^floor(N / 1024).
+__device__ __forceinline__ double exp_finish(double sc, double pr, int nn) {
+  return __builtin_amdgcn_ldexp(fma(sc, pr, sc), nn >> 10);
+}
+
 // The thread index and V through an empty asm: per-slot indices formed from
 // these copies are recomputed where they are used instead of being shared
 // across the kernel (32 of them would stay in registers throughout).
@@ -619,162 +672,148 @@ __device__ __forceinline__ int opaque_s(int x) {
 }
 
 struct NodeShared {
-  double exp_tab[256];  // 2^(i / 256)
+  double exp_tab[kExpTab];  // 2^(i / 1024)
   float mx[kWalkThreads / 64];
   double red[kWalkThreads / 64];
-  double tab[kRegSlots * (kWalkThreads / 64)];  // per (slot, wave) sums of r
-  double base, thr;
+  double wtot[kWalkThreads / 64];  // per-wave sums of r (bonus draw)
+  double ssum[kRegSlots];          // per-slot sums of r in one wave (bonus draw)
   int accept;
-  int hit;
   int cand;
+  int dec[TV_MAX_TREE];  // decisions on this node's children (-1: not reached)
 };
 
 // Inverse-CDF draw from r, given as this thread's slots (entry
-// k * kWalkThreads + threadIdx.x in rv[k], zero past V): the smallest x with
-// sum_{y<=x} r(y) > u0 * sum_y r(y). Index order is slot-major, then wave,
-// then lane. (1) Each wave folds its slots to per-(slot, wave) sums; (2) wave
-// 0 scans those sums in index order and finds the first block whose running
-// sum passes the threshold; (3) that block's wave scans its 64 entries from
-// the block's starting sum. Every thread returns the token.
+// slot_entry(threadIdx.x, k) in rv[k], zero past V): the smallest x with
+// sum_{y<=x} r(y) > u0 * sum_y r(y). In the wave-major layout index order
+// is wave, then slot, then lane: (1) every thread finds, from the sixteen
+// wave totals, the first wave whose running total passes the threshold;
+// (2) that wave alone folds its slots into per-slot sums and finds the
+// first slot to pass it; (3) it scans that slot's 64 entries. Where
+// rounding leaves a finer level short of the threshold that a coarser
+// level passed, the draw is the last positive entry of the coarser block
+// (the threshold sits at its end). Every thread returns the token.
 __device__ int inverse_cdf_draw(const double (&rv)[kRegSlots], double u0, NodeShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Eight slots at a time: after the exchanges across lane bits 5, 4 and 3
-  // each lane holds a partial sum of slot c0 + (lane >> 3), which three more
-  // exchanges complete over the wave.
+  double ts = 0.0;
 #pragma unroll
-  for (int c0 = 0; c0 < kRegSlots; c0 += 8) {
-    double a[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = swap32_sum(rv[c0 + i], rv[c0 + i + 4]);
-    a[0] = swap16_sum(a[0], a[2]);
-    a[1] = swap16_sum(a[1], a[3]);
-    const bool up = (lane & 8) != 0;
-    double t = (up ? a[1] : a[0]) + dpp_f64<kDppRowRor8>(up ? a[0] : a[1]);
-    t += dpp_f64<kDppHalfMirror>(t);
-    t += dpp_f64<kDppXor2>(t);
-    t += dpp_f64<kDppXor1>(t);
-    if ((lane & 7) == 0) sh.tab[(c0 + (lane >> 3)) * (kWalkThreads / 64) + wave] = t;
-  }
-  __syncthreads();
-  constexpr int kPer = kRegSlots * (kWalkThreads / 64) / 64;  // table entries per lane
-  if (wave == 0) {
-    double loc[kPer];
-    double lt = 0.0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      loc[j] = sh.tab[lane * kPer + j];
-      lt += loc[j];
-    }
-    const double inc = wave_scan_valu(lt, lane);
-    const double total = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(inc), 63),
-                                          __builtin_amdgcn_readlane(__double2loint(inc), 63));
-    const double thr = u0 * total;
-    double p = __shfl_up(inc, 1);  // exclusive prefix
-    if (lane == 0) p = 0.0;
-    int hit = -1;
-    double base = 0.0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const double nx = p + loc[j];
-      if (hit < 0 && nx > thr) {
-        hit = lane * kPer + j;
-        base = p;
+  for (int k = 0; k < kRegSlots; ++k) ts += rv[k];
+  ts = wave_sum_valu(ts);
+  if (lane == 0) sh.wtot[wave] = ts;
+  if (tid == 0) sh.cand = -1;
+  lds_only_barrier();
+  // (1) The same sums in the same order in every thread.
+  double total = 0.0;
+  for (int w = 0; w < kWalkThreads / 64; ++w) total += sh.wtot[w];
+  const double thr = u0 * total;
+  int ws = -1;
+  double base = 0.0;
+  {
+    double run = 0.0;
+    for (int w = 0; w < kWalkThreads / 64; ++w) {
+      const double nx = run + sh.wtot[w];
+      if (ws < 0 && nx > thr) {
+        ws = w;
+        base = run;
       }
-      p = nx;
+      run = nx;
     }
-    const unsigned long long m = __ballot(hit >= 0);
-    const int first = m ? __ffsll(m) - 1 : -1;
-    if (lane == 0) sh.hit = -1;
-    if (lane == first) {
-      sh.hit = hit;
-      sh.base = base;
-      sh.thr = thr;
-    }
-    if (tid == 0) sh.cand = -1;
   }
-  __syncthreads();
-  const int e = sh.hit;
-  if (e >= 0) {
-    if (wave == e % (kWalkThreads / 64)) {
-      const int ks = e / (kWalkThreads / 64);
-      double val = 0.0;
-#pragma unroll
-      for (int k = 0; k < kRegSlots; ++k) val = k == ks ? rv[k] : val;
-      const double run = sh.base + wave_scan_valu(val, lane);
-      const unsigned long long m = __ballot(run > sh.thr);
-      int pick;
-      if (m) {
-        pick = __ffsll(m) - 1;
-      } else {
-        // Rounding kept the lane scan under the threshold that the block sum
-        // passed: the draw sits at the block's end; take its last positive.
-        const unsigned long long pos = __ballot(val > 0.0);
-        pick = 63 - __clzll(pos);
-      }
-      if (lane == 0) sh.cand = ks * kWalkThreads + wave * 64 + pick;
-    }
-  } else {
-    // Rounding left the threshold above every running sum (u0 within an ulp
-    // of 1): take the last token with positive mass.
+  // Last positive entry of this thread's slots in [k0, k1) (-1 if none).
+  auto last_positive = [&](int k0, int k1) {
     int last = -1;
     const int t = opaque_v(tid);
 #pragma unroll
     for (int k = 0; k < kRegSlots; ++k)
-      if (rv[k] > 0.0) last = k * kWalkThreads + t;
+      if (k >= k0 && k < k1 && rv[k] > 0.0) last = slot_entry(t, k);
+    return last;
+  };
+  if (ws < 0) {
+    // Rounding left the threshold at the total (u0 within an ulp of 1):
+    // the last token with positive mass.
+    const int last = last_positive(0, kRegSlots);
     if (last >= 0) atomicMax(&sh.cand, last);
+  } else if (wave == ws) {
+    // (2) Per-slot sums of this wave, eight slots at a time: after the
+    // exchanges across lane bits 5, 4 and 3 each lane holds a partial sum
+    // of slot c0 + (lane >> 3), which three more exchanges complete.
+#pragma unroll
+    for (int c0 = 0; c0 < kRegSlots; c0 += 8) {
+      double a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = swap32_sum(rv[c0 + i], rv[c0 + i + 4]);
+      a[0] = swap16_sum(a[0], a[2]);
+      a[1] = swap16_sum(a[1], a[3]);
+      const bool up = (lane & 8) != 0;
+      double t = (up ? a[1] : a[0]) + dpp_f64<kDppRowRor8>(up ? a[0] : a[1]);
+      t += dpp_f64<kDppHalfMirror>(t);
+      t += dpp_f64<kDppXor2>(t);
+      t += dpp_f64<kDppXor1>(t);
+      if ((lane & 7) == 0) sh.ssum[c0 + (lane >> 3)] = t;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes
+    const double sv = lane < kRegSlots ? sh.ssum[lane] : 0.0;
+    const double inc = wave_scan_valu(sv, lane);
+    const unsigned long long hit = __ballot(lane < kRegSlots && base + inc > thr);
+    int pick = -1;
+    if (hit) {
+      const int ks = __ffsll(hit) - 1;
+      // This wave's running total before slot ks.
+      const double ex = __shfl(inc, ks > 0 ? ks - 1 : 0);
+      const double sbase = ks > 0 ? base + ex : base;
+      double val = 0.0;
+#pragma unroll
+      for (int k = 0; k < kRegSlots; ++k) val = k == ks ? rv[k] : val;
+      // (3) The lanes of slot ks.
+      const double run = sbase + wave_scan_valu(val, lane);
+      const unsigned long long m = __ballot(run > thr);
+      if (m) {
+        pick = slot_entry(ws * 64, ks) + __ffsll(m) - 1;
+      } else {
+        const unsigned long long pos = __ballot(val > 0.0);
+        if (pos) pick = slot_entry(ws * 64, ks) + 63 - __clzll(pos);
+      }
+      if (lane == 0) sh.cand = pick;
+    } else {
+      const int last = last_positive(0, kRegSlots);
+      if (last >= 0) atomicMax(&sh.cand, last);
+    }
   }
   __syncthreads();
   return sh.cand;
 }
 
-// exp(y ln 2 / 256) for the row terms, table-driven: with y = N + f (N the
-// nearest integer, |f| <= 1/2), exp = 2^floor(N / 256) * 2^((N mod 256) /
-// 256) * exp(f ln 2 / 256); the last factor minus one is its Taylor series
-// in f to the fourth power (|f ln 2 / 256| <= ln 2 / 512, truncation below
-// 4e-17 relative), coefficients (ln 2 / 256)^k / k!. N is read from the low
-// word of y + 1.5 * 2^52; the power of two is applied by ldexp, which rounds
-// subnormal results and underflows to 0 (y is clamped at -2^19, far below
-// the range, so -inf gives 0); results past the range are +inf. Relative
-// error a few units of 2^-52 for normal results.
-constexpr double kExpScale = 369.3299304675746;   // 256 / ln 2
-constexpr double kExpC1 = 0.0027076061740622863;  // ln 2 / 256
-constexpr double kExpC2 = 3.6655655969101062e-06;  // (ln 2 / 256)^2 / 2
-constexpr double kExpC3 = 3.3083026805413713e-09;  // (ln 2 / 256)^3 / 6
-constexpr double kExpC4 = 2.239395190875157e-12;   // (ln 2 / 256)^4 / 24
-constexpr double kExpRound = 6755399441055744.0;  // 1.5 * 2^52
-
-// The table-free part of exp_scaled: the table index N (low word) and the
-// polynomial factor, for y = arg.
-__device__ __forceinline__ double exp_reduce(double y, int& nn) {
-  y = fmax(y, -524288.0);
-  const double yr = y + kExpRound;
-  nn = __double2loint(yr);
-  const double f = y - (yr - kExpRound);
-  return f * fma(f, fma(f, fma(f, kExpC4, kExpC3), kExpC2), kExpC1);
-}
-
-// The rest: table entry sc = 2^((N mod 256) / 256), power 2^floor(N / 256).
-__device__ __forceinline__ double exp_finish(double sc, double pr, int nn) {
-  return __builtin_amdgcn_ldexp(fma(sc, pr, sc), nn >> 8);
-}
-
-// HBM -> LDS copy of a row in the slot layout (entry k * kWalkThreads + t at
-// s_row[k * kWalkThreads + t]), no register staging: each wave's load of a
-// slot fills 64 consecutive floats. Entries at or past V are not read (the
-// buffer's range check); the caller waits with vmcnt(0) and a barrier.
-__device__ __forceinline__ void row_to_lds(const float* row, int V, float* s_row) {
+// HBM -> LDS copy of a row: entry v lands at s_row[v] (thread t reads its
+// slot k at s_row[slot_entry(t, k)]). Without register staging. Entries at or past V are not read (the buffer's range
+// check); the caller waits with vmcnt(0) and a barrier before reading.
+// x4: 16-byte copies (the row 16-byte aligned, V a multiple of 4), eight
+// per wave, each filling 256 consecutive entries; otherwise 4-byte copies,
+// thirty-two per wave, each filling one of the wave's own slots.
+__device__ __forceinline__ void row_to_lds(const float* row, int V, float* s_row, bool x4) {
   const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, V * 4, 0x00020000);
-  // The wave's first thread index, as a scalar (the LDS address of each
-  // copy is wave-uniform).
-  const int wave_base = __builtin_amdgcn_readfirstlane(threadIdx.x & ~63);
-  const int off = static_cast<int>(threadIdx.x) * 4;
-  // The slot's byte offset goes in the scalar offset, so the lane offset is
-  // the only vector register the copies need.
+  // The wave index as a scalar (the LDS address of each copy is
+  // wave-uniform); the copy's byte offset goes in the scalar offset, so
+  // the lane offset is the only vector register the copies need.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (x4) {
+    constexpr int kWaves = kWalkThreads / 64;
+    constexpr int kCopies = kRegSlots * kWalkThreads / (256 * kWaves);
 #pragma unroll
-  for (int k = 0; k < kRegSlots; ++k)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (__attribute__((address_space(3))) void*)(s_row + k * kWalkThreads + wave_base), 4,
-        off, k * kWalkThreads * 4, 0, 0);
+    for (int i = 0; i < kCopies; ++i) {
+      const int first = (i * kWaves + wave) * 256;  // first entry of this copy
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(s_row + first), 16, lane * 16, first * 4,
+          0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kRegSlots; ++k) {
+      const int first = wave * kWaveSpan + k * 64;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(s_row + first), 4, lane * 4, first * 4, 0,
+          0);
+    }
+  }
 }
 
 // Waits until at most n vector-memory operations of this wave are in
@@ -783,236 +822,52 @@ __device__ __forceinline__ void row_to_lds(const float* row, int V, float* s_row
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14))
 #define TV_ACCEPT_WAIT_VMCNT0() TV_ACCEPT_WAIT_VMCNT(0)
 
-// Workgroup barrier that waits for this wave's LDS operations only, so that
-// global loads and HBM -> LDS copies stay in flight across it.
-__device__ __forceinline__ void lds_only_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-
-// One workgroup per live (sequence b, node j); thread t owns the entries
-// x = k * kWalkThreads + t (slot k) of every row it touches. p_j is formed in
-// registers as e(x) = exp((l(x) - max l) / tau) with the factor 1 / sum e;
-// the children of j are then tested in ascending index exactly as the walk
-// tests them at j. The residual stays in registers as r = rv * inv (rv
-// unnormalised): a test is one lookup by the owner of x, a rejection copies
-// q_c's row into LDS, sums max(r - q_c, 0) in one pass and keeps it in a
-// second once the sum is known to be positive (a zero sum keeps r
-// unchanged). Outputs per node: node_next (the accepted child, -1 if none),
-// node_dec for each child of j (+1, 0, or -1 when never reached) and, when
-// no child is accepted, node_bonus (the draw from the final r with u[b][0]).
-__global__ __launch_bounds__(kWalkThreads) void sample_node_kernel(
-    const float* __restrict__ logits, int64_t stride, double inv_tau,
-    const float* __restrict__ q, int64_t qstride, const float* __restrict__ u,
-    const int32_t* __restrict__ tokens, const int32_t* __restrict__ parent,
-    const int32_t* __restrict__ n_nodes, int T, int V, int8_t* __restrict__ node_dec,
-    int32_t* __restrict__ node_next, int32_t* __restrict__ node_bonus) {
-  __shared__ NodeShared sh;
-  // The logits row, then the draft row of the child under test (slot
-  // layout). Entries at or past V are zeroed once and never written by the
-  // row copies.
-  __shared__ float s_row[kRegSlots * kWalkThreads];
-  const int j = blockIdx.x, b = blockIdx.y;
-  if (!live_row(n_nodes, T, b, j)) return;
-  const int n = n_nodes[b];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t rbase = static_cast<int64_t>(b) * T;
-  // Parents of rows lane and lane + 64 (-2 where there is no such child).
-  static_assert(TV_MAX_TREE <= 128, "two parent words per lane");
-  const int par_lo = lane >= 1 && lane < n ? parent[rbase + lane] : -2;
-  const int par_hi = lane + 64 < n ? parent[rbase + lane + 64] : -2;
-  // First child of j at index >= from (n when there is none).
-  auto next_child = [&](int from) {
-    const unsigned long long lo = __ballot(par_lo == j && lane >= from);
-    if (lo) return __ffsll(lo) - 1;
-    const unsigned long long hi = __ballot(par_hi == j && lane + 64 >= from);
-    return hi ? 64 + __ffsll(hi) - 1 : n;
-  };
-  // The test of child c needs only q_c(x_c): its owner requests that one
-  // value ahead; q_c's row is read only after c is rejected.
-  auto token_of = [&](int cc) { return cc < n ? tokens[rbase + cc] : -1; };
-  auto owner_of = [&](int xx) { return xx >= 0 && xx < V ? (xx & (kWalkThreads - 1)) : 0; };
-  auto probe = [&](int cc, int xx) {
-    return cc < n && xx >= 0 && xx < V && tid == owner_of(xx)
-               ? q[(rbase + cc) * qstride + xx]
-               : 0.f;
-  };
-  int c = next_child(1);
-  int x = token_of(c);
-  float qx = probe(c, x);
-  const float* lrow = logits + (rbase + j) * stride;
-  if (tid < 256) sh.exp_tab[tid] = exp2(tid * (1.0 / 256.0));
-  {
-    const int t = opaque_v(tid), vv = opaque_s(V);
-#pragma unroll
-    for (int k = 0; k < kRegSlots; ++k)
-      if (k * kWalkThreads + kWalkThreads > vv && k * kWalkThreads + t >= vv)
-        s_row[k * kWalkThreads + t] = 0.f;
-  }
-  // The logits row is loaded into registers and its terms are formed slot
-  // by slot as the loads land (the compiler waits for each slot's load
-  // alone), against a reference m0 known before the whole row has arrived:
-  // the largest logit of slot 0. Every ratio the walk uses is of two terms
-  // of one row (p_j = e / sum e), so the common factor exp((max - m0) /
-  // tau) cancels. If a term overflows (a logit more than ~700 tau above m0)
-  // the sums are not finite and the row goes round again with its maximum
-  // as reference.
-  const double ky = inv_tau * kExpScale;
-  double rv[kRegSlots];
-  double z = 0.0;
-  float m0 = -INFINITY;
-#pragma nounroll
-  for (int round = 0; round < 2; ++round) {
-    float lv[kRegSlots];
-    load_blocks(lrow, V, lv);
-    float mr = tid < V ? lv[0] : -INFINITY;
-    if (round == 1)  // the row maximum (a separate pass over the row)
-      for (int v = tid + kWalkThreads; v < V; v += kWalkThreads) mr = fmaxf(mr, lrow[v]);
-    // Barriers on LDS only: the rest of the row is still in flight.
-    mr = wave_max_valu(mr);
-    if (lane == 0) sh.mx[wave] = mr;
-    lds_only_barrier();
-    m0 = sh.mx[0];
-    for (int w = 1; w < kWalkThreads / 64; ++w) m0 = fmaxf(m0, sh.mx[w]);
-    lds_only_barrier();  // sh.mx is written again below
-    // y = (l - m0) / tau * 256 / ln 2 as one fused step.
-    const double nky = -static_cast<double>(m0) * ky;
-    const int t = opaque_v(tid), vv = opaque_s(V);
-    z = 0.0;
-    // Logit of slot k; entries past V (only in the slots that reach V, a
-    // uniform test) read as -inf, whose term is 0.
-    auto logit = [&](int k) {
-      float l = lv[k];
-      if (__builtin_expect(k * kWalkThreads + kWalkThreads > vv, 0)) {
-        if (k * kWalkThreads + t >= vv) l = -INFINITY;
-      }
-      return static_cast<double>(l);
-    };
-    // Two-stage pipeline over the slots: the table read of slot k + 1 is
-    // in flight while slot k is finished.
-    int nn_n;
-    double pr_n = exp_reduce(fma(logit(0), ky, nky), nn_n);
-    double sc_n = sh.exp_tab[nn_n & 255];
-#pragma unroll
-    for (int k = 0; k < kRegSlots; ++k) {
-      const int nn = nn_n;
-      const double pr = pr_n, sc = sc_n;
-      if (k + 1 < kRegSlots) {
-        pr_n = exp_reduce(fma(logit(k + 1), ky, nky), nn_n);
-        sc_n = sh.exp_tab[nn_n & 255];
-      }
-      const double e = exp_finish(sc, pr, nn);
-      rv[k] = e;
-      z += e;
-      // Settle this slot's sum here: left to the compiler, the rest of each
-      // term's evaluation sinks below the loop and every slot's
-      // intermediates stay alive until then.
-      asm volatile("" : "+v"(z));
-    }
-    const bool again = __syncthreads_or(!(z < INFINITY));
-    if (!again || round == 1) break;
-  }
-  // The first child's draft row goes to LDS while the sum and the first
-  // test run (it is read only if that child is rejected). Issued after the
-  // logits, so that the waits for the logits never wait for it.
-  if (c < n) row_to_lds(q + (rbase + c) * qstride, V, s_row);
-  double inv = 1.0 / block_sum_f64(z, sh.red);
-
-  int accepted = -1;
-  bool first = true;  // c is the first child: its row is in LDS already
-  while (c < n) {
-    const bool x_ok = x >= 0 && x < V;
-    if (tid == owner_of(x)) {
-      int acc = 0;
-      if (x_ok) {
-        const int ks = x / kWalkThreads;
-        double rx = 0.0;
-#pragma unroll
-        for (int k = 0; k < kRegSlots; ++k) rx = k == ks ? rv[k] : rx;
-        acc = accept_test(rx * inv, qx, u[rbase + c]);
-      }
-      node_dec[rbase + c] = static_cast<int8_t>(acc);
-      sh.accept = acc;
-    }
-    // This barrier also ends every read of s_row before the copy below
-    // overwrites it.
-    __syncthreads();
-    // Every thread reads sh.accept before the barrier inside block_sum_f64,
-    // which the next test's write comes after.
-    if (sh.accept) {
-      accepted = c;
-      break;
-    }
-    if (!first) row_to_lds(q + (rbase + c) * qstride, V, s_row);
-    first = false;
-    const int cn = next_child(c + 1);
-    x = token_of(cn);
-    qx = probe(cn, x);
-    TV_ACCEPT_WAIT_VMCNT0();
-    __syncthreads();
-    double part_sum = 0.0;
-#pragma unroll
-    for (int k = 0; k < kRegSlots; ++k)
-      part_sum += fmax(fma(rv[k], inv, -static_cast<double>(s_row[k * kWalkThreads + tid])), 0.0);
-    const double tot = block_sum_f64(part_sum, sh.red);
-    if (tot > 0.0) {
-#pragma unroll
-      for (int k = 0; k < kRegSlots; ++k)
-        rv[k] = fmax(fma(rv[k], inv, -static_cast<double>(s_row[k * kWalkThreads + tid])), 0.0);
-      inv = 1.0 / tot;
-    }
-    c = cn;
-  }
-  if (tid == 0) node_next[rbase + j] = accepted;
-  if (accepted >= 0) {
-    // The children after the accepted one are never tested.
-    if (tid > accepted && tid < n && parent[rbase + tid] == j) node_dec[rbase + tid] = -1;
-    return;
-  }
-  const int bon = inverse_cdf_draw(rv, static_cast<double>(u[rbase]), sh);
-  if (tid == 0) node_bonus[rbase + j] = bon;
-}
 
 // One workgroup per sequence (one thread per tree row): validates the
 // sequence, follows node_next from the root and writes the outputs. A
 // child's decision is reported when its parent lies on the path (those are
-// the tests the walk makes); every other entry is -1.
+// the tests the walk makes); every other entry is -1. Sequences with n
+// outside [1, T] read nothing of the node arrays.
 __global__ __launch_bounds__(TV_MAX_TREE) void sample_path_kernel(
-    const int8_t* __restrict__ node_dec, const int32_t* __restrict__ node_next,
+    const int32_t* __restrict__ node_dec, const int32_t* __restrict__ node_next,
     const int32_t* __restrict__ node_bonus, const int32_t* __restrict__ tokens,
     const int32_t* __restrict__ parent, const int32_t* __restrict__ n_nodes, int T, int V,
     int32_t* accept_len, int32_t* path, int32_t* bonus, uint8_t* accept_mask,
     int8_t* decision, int32_t* row_status) {
-  __shared__ int s_flags, s_len, s_end;
+  __shared__ int s_flags[1], s_len[1], s_end[1];
   __shared__ int s_next[TV_MAX_TREE], s_path[TV_MAX_TREE], s_on[TV_MAX_TREE];
+  __shared__ int s_bon[TV_MAX_TREE];
   const int b = blockIdx.x;
+  const int n = n_nodes[b];
   const int i = threadIdx.x;
   const int64_t row = static_cast<int64_t>(b) * T + i;
   const bool in_t = i < T;
-  const int n = n_nodes[b];
   const bool n_ok = n >= 0 && n <= T;
   const bool live = n_ok && i < n;
-  // Every load is issued before the first barrier; rows of a sequence that
-  // fails validation are read (in bounds) but unused.
-  const int pr = live && i > 0 ? parent[row] : -1;
-  const int tk = live && i > 0 ? tokens[row] : 0;
-  const int nx = live ? node_next[row] : -1;
-  const int dc = live && i > 0 ? node_dec[row] : -1;
-  if (i == 0) s_flags = 0;
+  // One round trip: every row's entries are requested together with
+  // n_nodes (rows of [0, T) are in bounds; those past n are read but
+  // unused).
+  const int pr = in_t && i > 0 ? parent[row] : -1;
+  const int tk = in_t && i > 0 ? tokens[row] : 0;
+  const int nx = in_t ? node_next[row] : -1;
+  const int dc = in_t && i > 0 ? node_dec[row] : -1;
+  const int bn = in_t ? node_bonus[row] : -1;
+  if (i == 0) *s_flags = 0;
   __syncthreads();
   int f = 0;
   if (live && i > 0) {
     if (pr < 0 || pr >= i) f |= 1;
     if (tk < 0 || tk >= V) f |= 2;
   }
-  if (f) atomicOr(&s_flags, f);
+  if (f) atomicOr(s_flags, f);
   if (in_t) {
     s_next[i] = nx;
     s_path[i] = -1;
     s_on[i] = 0;
+    s_bon[i] = bn;
   }
   __syncthreads();
-  const int flags = s_flags;
+  const int flags = *s_flags;
   const int st = !n_ok ? TV_ROW_NNODES
                        : ((flags & 1) ? TV_ROW_BAD_PARENT
                                       : ((flags & 2) ? TV_ROW_BAD_TOKEN : TV_ROW_OK));
@@ -1039,8 +894,8 @@ __global__ __launch_bounds__(TV_MAX_TREE) void sample_path_kernel(
       s_on[c] = 1;
       cur = c;
     }
-    s_len = len;
-    s_end = cur;
+    *s_len = len;
+    *s_end = cur;
   }
   __syncthreads();
   if (in_t) {
@@ -1049,11 +904,224 @@ __global__ __launch_bounds__(TV_MAX_TREE) void sample_path_kernel(
     decision[row] = static_cast<int8_t>(live && i > 0 && s_on[pr] ? dc : -1);
   }
   if (i == 0) {
-    accept_len[b] = s_len;
-    bonus[b] = node_bonus[static_cast<int64_t>(b) * T + s_end];
+    accept_len[b] = *s_len;
+    bonus[b] = s_bon[*s_end];
     row_status[b] = TV_ROW_OK;
   }
 }
+
+// One workgroup per live (sequence b, node j); thread t owns the entries
+// x = slot_entry(t, k) (slot k) of every row it touches. p_j is formed in
+// registers as e(x) = exp((l(x) - max l) / tau) with the factor 1 / sum e;
+// the children of j are then tested in ascending index exactly as the walk
+// tests them at j. The residual stays in registers as r = rv * inv (rv
+// unnormalised): a test is one lookup by the owner of x, a rejection copies
+// q_c's row into LDS, sums max(r - q_c, 0) in one pass and keeps it in a
+// second once the sum is known to be positive (a zero sum keeps r
+// unchanged). Outputs per node: node_next (the accepted child, -1 if none),
+// node_dec for each child of j (+1, 0, or -1 when never reached) and, when
+// no child is accepted, node_bonus (the draw from the final r with u[b][0]).
+__global__ __launch_bounds__(kWalkThreads) void sample_node_kernel(
+    const float* __restrict__ logits, int64_t stride, double inv_tau,
+    const float* __restrict__ q, int64_t qstride, bool q_x4, const float* __restrict__ u,
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ parent,
+    const int32_t* __restrict__ n_nodes, int T, int V, int32_t* __restrict__ node_dec,
+    int32_t* __restrict__ node_next, int32_t* __restrict__ node_bonus) {
+  __shared__ NodeShared sh;
+  // The logits row, then the draft row of the child under test (slot
+  // layout). Entries at or past V are zeroed once and never written by the
+  // row copies.
+  __shared__ float s_row[kRegSlots * kWalkThreads];
+  const int j = blockIdx.x, b = blockIdx.y;
+  if (!live_row(n_nodes, T, b, j)) return;
+  const int n = n_nodes[b];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t rbase = static_cast<int64_t>(b) * T;
+  // Parents of rows lane and lane + 64 (-2 where there is no such child).
+  static_assert(TV_MAX_TREE <= 128, "two parent words per lane");
+  const int par_lo = lane >= 1 && lane < n ? parent[rbase + lane] : -2;
+  const int par_hi = lane + 64 < n ? parent[rbase + lane + 64] : -2;
+  // First child of j at index >= from (n when there is none).
+  auto next_child = [&](int from) {
+    const unsigned long long lo = __ballot(par_lo == j && lane >= from);
+    if (lo) return __ffsll(lo) - 1;
+    const unsigned long long hi = __ballot(par_hi == j && lane + 64 >= from);
+    return hi ? 64 + __ffsll(hi) - 1 : n;
+  };
+  // The test of child c needs only q_c(x_c): its owner requests that one
+  // value ahead; q_c's row is read only after c is rejected.
+  auto token_of = [&](int cc) { return cc < n ? tokens[rbase + cc] : -1; };
+  // Owner of entry xx: lane xx mod 64 of wave xx / kWaveSpan (slot
+  // (xx mod kWaveSpan) / 64).
+  auto owner_of = [&](int xx) {
+    return xx >= 0 && xx < V ? (xx / kWaveSpan) * 64 + (xx & 63) : 0;
+  };
+  auto probe = [&](int cc, int xx) {
+    return cc < n && xx >= 0 && xx < V && tid == owner_of(xx)
+               ? q[(rbase + cc) * qstride + xx]
+               : 0.f;
+  };
+  int c = next_child(1);
+  int x = token_of(c);
+  float qx = probe(c, x);
+  const float u0 = u[rbase];  // the bonus draw's uniform, requested early
+  if (tid < TV_MAX_TREE) sh.dec[tid] = -1;
+  const float* lrow = logits + (rbase + j) * stride;
+  sh.exp_tab[tid] = exp2(tid * (1.0 / kExpTab));
+  static_assert(kExpTab == kWalkThreads, "one table entry per thread");
+  {
+    const int t = opaque_v(tid), vv = opaque_s(V);
+    const int wb = (tid >> 6) * kWaveSpan;  // first entry of this wave
+#pragma unroll
+    for (int k = 0; k < kRegSlots; ++k)
+      if (wb + k * 64 + 64 > vv && slot_entry(t, k) >= vv) s_row[slot_entry(t, k)] = 0.f;
+  }
+  // The terms are formed against a reference m0 known before the whole row
+  // has arrived: the largest logit of slot 0. Every ratio the walk uses is
+  // of two terms of one row (p_j = e / sum e), so the common factor
+  // exp((max - m0) / tau) cancels. Logits are clamped to
+  // [m0 - 752 tau, m0 + 1e5 tau] (both rounded down): below, the term is 0
+  // in any case; above, the term overflows like every logit more than
+  // ~710 tau above m0, the sum is not finite and the row goes round again
+  // with its maximum as reference (also when m0 + 1e5 tau rounds to m0).
+  const double ky = inv_tau * kExpScale;
+  const double tau = 1.0 / inv_tau;
+  double rv[kRegSlots];
+  double z = 0.0;
+  float m0 = -INFINITY;
+#pragma nounroll
+  for (int round = 0; round < 2; ++round) {
+    // The row in two halves: the second half's loads are issued once the
+    // first half has landed, so that its transfer overlaps the first
+    // half's terms.
+    float lv[kRegSlots];
+    load_blocks<0, kRegSlots / 2>(lrow, V, lv);
+    TV_ACCEPT_WAIT_VMCNT0();
+    load_blocks<kRegSlots / 2, kRegSlots>(lrow, V, lv);
+    float mr = slot_entry(tid, 0) < V ? lv[0] : -INFINITY;
+    if (round == 1)  // the row maximum (a separate pass over the row)
+      for (int v = tid; v < V; v += kWalkThreads) mr = fmaxf(mr, lrow[v]);
+    // Barriers on LDS only: the second half is still in flight.
+    mr = wave_max_valu(mr);
+    if (lane == 0) sh.mx[wave] = mr;
+    lds_only_barrier();
+    m0 = sh.mx[0];
+    for (int w = 1; w < kWalkThreads / 64; ++w) m0 = fmaxf(m0, sh.mx[w]);
+    lds_only_barrier();  // sh.mx is written again below
+    const float lo = __double2float_rd(static_cast<double>(m0) - kExpFloorTau * tau);
+    const float hi = __double2float_rd(static_cast<double>(m0) + 1e5 * tau);
+    // y = (l - m0) / tau * 1024 / ln 2 as one fused step.
+    const double nky = -static_cast<double>(m0) * ky;
+    const int t = opaque_v(tid), vv = opaque_s(V);
+    const int wb = __builtin_amdgcn_readfirstlane((tid >> 6) * kWaveSpan);
+    z = 0.0;
+    // Logit of slot k, clamped; entries past V (only in the slots that
+    // reach V, a wave-uniform test) read as the lower bound, whose term is
+    // 0.
+    auto logit = [&](int k) {
+      float l = __builtin_amdgcn_fmed3f(lv[k], lo, hi);
+      if (__builtin_expect(wb + k * 64 + 64 > vv, 0)) {
+        if (slot_entry(t, k) >= vv) l = lo;
+      }
+      return static_cast<double>(l);
+    };
+    // Two-stage pipeline over the slots: the table read of slot k + 1 is
+    // in flight while slot k is finished.
+    int nn_n;
+    double pr_n = exp_reduce(fma(logit(0), ky, nky), nn_n);
+    double sc_n = sh.exp_tab[nn_n & (kExpTab - 1)];
+#pragma unroll
+    for (int k = 0; k < kRegSlots; ++k) {
+      const int nn = nn_n;
+      const double pr = pr_n, sc = sc_n;
+      if (k + 1 < kRegSlots) {
+        pr_n = exp_reduce(fma(logit(k + 1), ky, nky), nn_n);
+        sc_n = sh.exp_tab[nn_n & (kExpTab - 1)];
+      }
+      const double e = exp_finish(sc, pr, nn);
+      rv[k] = e;
+      z += e;
+      // Settle this slot's sum here: left to the compiler, the rest of each
+      // term's evaluation sinks below the loop and every slot's
+      // intermediates stay alive until then.
+      asm volatile("" : "+v"(z));
+    }
+    const bool again = __syncthreads_or(!(z < INFINITY) || !(hi > m0));
+    if (!again || round == 1) break;
+  }
+  // The first child's draft row goes to LDS while the sum and the first
+  // test run (it is read only if that child is rejected). Issued after the
+  // logits, so that the waits for the logits never wait for it.
+  if (c < n) row_to_lds(q + (rbase + c) * qstride, V, s_row, q_x4);
+  double inv = 1.0 / block_sum_f64<true>(z, sh.red);
+
+  int accepted = -1;
+  bool first = true;  // c is the first child: its row is in LDS already
+  while (c < n) {
+    const bool x_ok = x >= 0 && x < V;
+    if (tid == owner_of(x)) {
+      int acc = 0;
+      if (x_ok) {
+        const int ks = (x % kWaveSpan) / 64;
+        double rx = 0.0;
+#pragma unroll
+        for (int k = 0; k < kRegSlots; ++k) rx = k == ks ? rv[k] : rx;
+        acc = accept_test(rx * inv, qx, u[rbase + c]);
+      }
+      sh.dec[c] = acc;
+      sh.accept = acc;
+    }
+    // This barrier also ends every read of s_row before the copy below
+    // overwrites it (LDS only: a copy in flight stays in flight).
+    lds_only_barrier();
+    // Every thread reads sh.accept before the barrier inside block_sum_f64,
+    // which the next test's write comes after.
+    if (sh.accept) {
+      accepted = c;
+      break;
+    }
+    if (!first) row_to_lds(q + (rbase + c) * qstride, V, s_row, q_x4);
+    first = false;
+    const int cn = next_child(c + 1);
+    x = token_of(cn);
+    qx = probe(cn, x);
+    TV_ACCEPT_WAIT_VMCNT0();
+    __syncthreads();
+    double part_sum = 0.0;
+#pragma unroll
+    for (int k = 0; k < kRegSlots; ++k)
+      part_sum += fmax(fma(rv[k], inv, -static_cast<double>(s_row[slot_entry(tid, k)])), 0.0);
+    const double tot = block_sum_f64<true>(part_sum, sh.red);
+    if (tot > 0.0) {
+#pragma unroll
+      for (int k = 0; k < kRegSlots; ++k)
+        rv[k] = fmax(fma(rv[k], inv, -static_cast<double>(s_row[slot_entry(tid, k)])), 0.0);
+      inv = 1.0 / tot;
+    }
+    c = cn;
+  }
+  int bon = -1;
+  if (accepted >= 0) {
+    // The first child's row copy may still be in flight: it must land
+    // before the LDS is reused.
+    TV_ACCEPT_WAIT_VMCNT0();
+  } else {
+    bon = inverse_cdf_draw(rv, static_cast<double>(u0), sh);
+  }
+  __syncthreads();  // sh.dec complete
+  // Wave 0 stores this node's results: the decisions on the node's children
+  // (found from the parent words it holds), the accepted child and the
+  // bonus.
+  if (wave == 0) {
+    if (par_lo == j) node_dec[rbase + lane] = sh.dec[lane];
+    if (par_hi == j) node_dec[rbase + lane + 64] = sh.dec[lane + 64];
+    if (lane == 0) {
+      node_next[rbase + j] = accepted;
+      if (accepted < 0) node_bonus[rbase + j] = bon;
+    }
+  }
+}
+
 
 // Walk for larger vocabularies: the residual r lives in one of two float64
 // buffers of V entries per sequence, or stays implicit as p_cur (the stored
@@ -1234,12 +1302,11 @@ size_t greedy_ws(int B, int T, int V) {
 bool sample_one_pass(int V) { return V <= kRegSlots * kWalkThreads; }
 
 // Sampling workspace. Vocabularies of the node-parallel path: per node the
-// accepted child, the bonus draw (int32 each) and the decision byte. Larger
+// accepted child, the bonus draw and the decision (int32 each). Larger
 // ones: slice statistics, the stored exp terms of every row (float64, B T V)
 // and two float64 residual buffers per sequence.
 size_t node_ws(int B, int T) {
-  return 2 * tvh::align_up(static_cast<size_t>(B) * T * sizeof(int32_t), 256) +
-         tvh::align_up(static_cast<size_t>(B) * T, 256);
+  return 3 * tvh::align_up(static_cast<size_t>(B) * T * sizeof(int32_t), 256);
 }
 
 size_t sample_ws(int B, int T, int V) {
@@ -1376,10 +1443,12 @@ extern "C" int tv_accept_sample(const float* logits, int64_t logits_row_stride,
     const size_t words = tvh::align_up(static_cast<size_t>(B) * T * sizeof(int32_t), 256);
     int32_t* node_next = reinterpret_cast<int32_t*>(ws);
     int32_t* node_bonus = reinterpret_cast<int32_t*>(ws + words);
-    int8_t* node_dec = reinterpret_cast<int8_t*>(ws + 2 * words);
+    int32_t* node_dec = reinterpret_cast<int32_t*>(ws + 2 * words);
+    // Draft rows copied 16 bytes at a time when every row is 16-byte aligned.
+    const bool q_x4 = (V & 3) == 0 && (q_row_stride & 3) == 0 && tvh::aligned16(q);
     hipLaunchKernelGGL(sample_node_kernel, dim3(T, B), dim3(kWalkThreads), 0, stream, logits,
-                       logits_row_stride, 1.0 / tau, q, q_row_stride, u, tokens, parent, n_nodes,
-                       T, V, node_dec, node_next, node_bonus);
+                       logits_row_stride, 1.0 / tau, q, q_row_stride, q_x4, u, tokens, parent,
+                       n_nodes, T, V, node_dec, node_next, node_bonus);
     hipLaunchKernelGGL(sample_path_kernel, dim3(B), dim3(TV_MAX_TREE), 0, stream, node_dec,
                        node_next, node_bonus, tokens, parent, n_nodes, T, V, accept_len, path,
                        bonus, accept_mask, decision, row_status);
