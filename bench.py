@@ -30,6 +30,11 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 METRIC = "verified draft nodes/sec + achieved HBM GB/s (B=8, 8k ctx, N=32 tree)"
+# Cold timing: the rotated input copies together exceed three times the
+# 256 MiB Infinity Cache, so no call finds its inputs left there by the
+# previous ones.
+MIN_SETS = 10
+COLD_MIB = 768
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
@@ -43,14 +48,18 @@ def parse():
                     help="timed steps (a step is ~75 us: fewer leave the wall clock to jitter)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="C3", help="workload (C1..C5); C3 is the headline")
-    ap.add_argument("--sets", type=int, default=4, help="input copies rotated for cold timing")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input copies rotated for cold timing (0: at least %d and at least "
+                         "%d MiB of inputs, three times the Infinity Cache)" % (MIN_SETS,
+                                                                                  COLD_MIB))
     ap.add_argument("--chunk", type=int, default=0, help="attention chunk_keys (0 = auto)")
     ap.add_argument("--parts", type=int, default=3,
                     help="probability_parts (3: fp32-faithful probabilities, the page's "
                          "setting; 1: the lossy fast mode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="target host time of the oracle baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="target host time of each oracle baseline sample (the step, then "
+                         "attention and acceptance each on one thread and on all cores)")
     ap.add_argument("--no-sampling", action="store_true",
                     help="skip the secondary sampling-acceptance measurement")
     ap.add_argument("--no-projections", action="store_true",
@@ -66,6 +75,8 @@ def parse():
                          "are graph-capturable); 0: launch them one by one")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the streaming-read measurement")
     return ap.parse_args()
 
 
@@ -96,13 +107,24 @@ def attention_flops(w):
 
 
 def accept_alg_bytes(w):
+    """Inputs of the acceptance read once: every live logits row, and in
+    sampling mode the draft row and uniform of every non-root live node,
+    plus the small per-node words (parent, token, outputs)."""
     tot = 0
     for b in range(w.B):
         n = int(w.n_nodes[b])
-        tot += n * w.V * 4 + n * 8 * 4  # logits rows + parent/token/outputs
+        tot += n * w.V * 4 + n * 8 * 4
         if w.qdraft is not None:
-            tot += max(n - 1, 0) * 4  # u
+            tot += max(n - 1, 0) * (w.V * 4 + 4)
     return tot
+
+
+def cold_sets(per_set_bytes, requested=0):
+    """Number of input copies to rotate: `requested`, else enough that they
+    total COLD_MIB MiB, and at least MIN_SETS."""
+    if requested:
+        return requested
+    return max(MIN_SETS, -(-(COLD_MIB << 20) // max(1, per_set_bytes)))
 
 
 def kernel_source_hash():
@@ -123,41 +145,69 @@ def measured_traffic():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, seconds):
-    """Time the float64 oracle (mask, attention, greedy acceptance) one live
-    sequence at a time until about `seconds` of host time have passed."""
+def _oracle_rate(w, seconds, parts):
+    """Verified draft nodes per second of the float64 oracle running `parts`
+    ("mask", "attention", "accept") one live sequence at a time until about
+    `seconds` of host time have passed. Returns (rate, sequences, seconds)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = os.cpu_count() or 1
     live = [b for b in range(w.B) if w.n_nodes[b] > 0]
-    nodes = 0
-    seqs = 0
+    nodes = seqs = i = 0
     t0 = time.perf_counter()
-    i = 0
     while True:
         b = live[i % len(live)]
         sl = slice(b, b + 1)
-        oracle.build_tree_mask(w.parent[sl], w.n_nodes[sl], w.T)
-        oracle.tree_attention(w.q[sl], w.k[sl], w.v[sl], w.dtype, w.ctx_len[sl], w.n_nodes[sl],
-                              w.parent[sl], w.scale)
-        if w.mode == "greedy":
-            oracle.accept_greedy(w.logits[sl], w.tokens[sl], w.parent[sl], w.n_nodes[sl])
-        else:
-            oracle.accept_sample(w.logits[sl], w.temperature, w.qdraft[sl], w.u[sl],
-                                 w.tokens[sl], w.parent[sl], w.n_nodes[sl])
+        if "mask" in parts:
+            oracle.build_tree_mask(w.parent[sl], w.n_nodes[sl], w.T)
+        if "attention" in parts:
+            oracle.tree_attention(w.q[sl], w.k[sl], w.v[sl], w.dtype, w.ctx_len[sl],
+                                  w.n_nodes[sl], w.parent[sl], w.scale)
+        if "accept" in parts:
+            if w.mode == "greedy":
+                oracle.accept_greedy(w.logits[sl], w.tokens[sl], w.parent[sl], w.n_nodes[sl])
+            else:
+                oracle.accept_sample(w.logits[sl], w.temperature, w.qdraft[sl], w.u[sl],
+                                     w.tokens[sl], w.parent[sl], w.n_nodes[sl])
         nodes += int(w.n_nodes[b]) - 1
         seqs += 1
         i += 1
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
-    return {"value": nodes / el, "unit": "verified draft nodes/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": "%d sequence(s) of workload %s (mask + float64 attention over all "
-                      "%d KV heads + acceptance), %.1f s" % (seqs, w.name, w.Hkv, el)}
+            return nodes / el, seqs, el
+
+
+def cpu_baseline(w, seconds):
+    """The float64 oracle on the host: the whole step on all cores (the
+    reported value), then attention and acceptance apart, each on one thread
+    and on all cores. Each sample runs whole live sequences of the workload
+    for about `seconds`."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threadpool_limits = None
+        threads = os.cpu_count() or 1
+    rate, seqs, el = _oracle_rate(w, seconds, ("mask", "attention", "accept"))
+    res = {"value": rate, "unit": "verified draft nodes/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": "%d sequence(s) of workload %s (mask + float64 attention over all %d KV "
+                     "heads + %s acceptance), %.1f s, all cores" % (seqs, w.name, w.Hkv, w.mode,
+                                                                   el)}
+    for part in ("attention", "accept"):
+        entry = {}
+        for label, limit in (("one_thread", 1), ("all_cores", None)):
+            if limit is not None and threadpool_limits is None:
+                continue
+            if limit is None:
+                r, n_s, e = _oracle_rate(w, seconds / 2, (part,))
+                cores = threads
+            else:
+                with threadpool_limits(limits=limit):
+                    r, n_s, e = _oracle_rate(w, seconds / 2, (part,))
+                cores = limit
+            entry[label] = {"value": round(r, 2), "unit": "verified draft nodes/s",
+                            "cores": int(cores), "sample": "%d sequence(s), %.1f s" % (n_s, e)}
+        res["attention" if part == "attention" else "acceptance"] = entry
+    return res
 
 
 def main():
@@ -205,7 +255,8 @@ def main():
     if w.mode == "sample":
         host["qd"] = torch.from_numpy(w.qdraft)
         host["u"] = torch.from_numpy(w.u)
-    sets = [{k: t.to(dev) for k, t in host.items()} for _ in range(max(1, args.sets))]
+    per_set = sum(t.numel() * t.element_size() for t in host.values())
+    sets = [{k: t.to(dev) for k, t in host.items()} for _ in range(cold_sets(per_set, args.sets))]
     B, T = w.B, w.T
     W = (T + 31) // 32
     bufs = []
@@ -339,8 +390,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded; cold: %d rotating input copies)%s" % (
-            len(sets), "; steps replayed from a HIP graph" if graph is not None else ""),
+        "data": "synthetic (seeded; cold: %d rotating input copies, %.0f MiB)%s" % (
+            len(sets), len(sets) * per_set / 2 ** 20,
+            "; steps replayed from a HIP graph" if graph is not None else ""),
         "config": {
             "workload": "%s: B=%d (%d live), Hq/Hkv=%d/%d, D=%d, ctx %d..%d, N=%d draft nodes "
                         "(T=%d), V=%d, %s acceptance" % (
@@ -393,6 +445,11 @@ def main():
     if not args.no_long_context and args.config == "C3":
         res["long_context"] = long_context_secondary(tv, torch, dev, args)
 
+    if not args.no_read_ceiling:
+        ceil = read_ceiling(tv, torch, dev)
+        res["roofline"]["measured_read_ceiling_GBps"] = ceil["GBps"]
+        res["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceil["GBps"], 4)
+        res["read_ceiling"] = ceil
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(res), flush=True)
@@ -541,14 +598,17 @@ def packed_secondary(tv, torch, dev, w, sets, bufs, ws_attn, acc_out, t_padded, 
 def long_context_secondary(tv, torch, dev, args):
     """Tree attention at the long-context workload (one sequence, 32768
     committed keys, 65-row tree): the compute-heavier shape, reported against
-    the bf16 MFMA peak beside its HBM fraction; warm (one input set)."""
+    the bf16 MFMA peak beside its HBM fraction; cold (rotating input copies
+    of the query and KV cache)."""
     from workloads import make_config
 
     w = make_config("C4")
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
-        torch.bfloat16).to(dev)
+        torch.bfloat16)
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa: E731
-    q, k, v = bf(w.q), bf(w.k), bf(w.v)
+    host = [bf(w.q), bf(w.k), bf(w.v)]
+    per_set = sum(t.numel() * t.element_size() for t in host)
+    sets = [[t.to(dev) for t in host] for _ in range(cold_sets(per_set))]
     ctx, n, par = i32(w.ctx_len), i32(w.n_nodes), i32(w.parent)
     mask = tv.build_tree_mask(par, n)[0]
     ws = torch.empty(max(1, tv.attention_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, w.max_ctx, 0)),
@@ -558,12 +618,14 @@ def long_context_secondary(tv, torch, dev, args):
     st = torch.empty((w.B,), dtype=torch.int32, device=dev)
 
     def call(i):
+        q, k, v = sets[i % len(sets)]
         tv.tree_attention(q, k, v, ctx, n, mask, w.max_ctx, scale=float(w.scale), out=out,
                           lse=lse, row_status=st, workspace=ws)
 
-    t = time_calls(torch, call, max(20, min(args.steps, 100)))
+    t = time_calls(torch, call, 4 * len(sets))
     by, fl = attention_alg_bytes(w), attention_flops(w)
     return {"workload": "C4: B=1, Hq/Hkv=28/4, D=128, ctx 32768, N=64 draft nodes (T=65)",
+            "cold": "%d rotating input copies, %.0f MiB" % (len(sets), len(sets) * per_set / 2 ** 20),
             "attention_us": round(t * 1e6, 3), "alg_bytes": by, "flops": fl,
             "GBps": round(by / t / 1e9, 1), "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4),
             "TFLOPs": round(fl / t / 1e12, 1),
@@ -571,32 +633,44 @@ def long_context_secondary(tv, torch, dev, args):
 
 
 def sampling_secondary(tv, torch, dev, args):
-    """Sampling acceptance at its own workload (8 sequences, V=32000), warm."""
+    """Sampling acceptance at its own workload (8 sequences, V=32000,
+    temperature 0.7): cold (rotating copies of the logits and draft rows),
+    timed from graph replays like the other calls."""
     from workloads import make_config
 
     w = make_config("C5")
-    lg = torch.from_numpy(w.logits).to(dev)
-    qd = torch.from_numpy(w.qdraft).to(dev)
+    host = [torch.from_numpy(w.logits), torch.from_numpy(w.qdraft)]
+    per_set = sum(t.numel() * t.element_size() for t in host)
+    sets = [[t.to(dev) for t in host] for _ in range(cold_sets(per_set))]
     u = torch.from_numpy(w.u).to(dev)
     tok = torch.from_numpy(w.tokens).to(dev)
     par = torch.from_numpy(w.parent).to(dev)
     n = torch.from_numpy(w.n_nodes).to(dev)
     ws = torch.empty(tv.accept_workspace_size(w.B, w.T, w.V, 1), dtype=torch.uint8, device=dev)
-    for _ in range(3):
-        tv.accept_sample(lg, float(w.temperature), qd, u, tok, par, n, workspace=ws)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    reps = max(5, min(args.steps, 50))
-    e0.record()
-    for _ in range(reps):
-        tv.accept_sample(lg, float(w.temperature), qd, u, tok, par, n, workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / reps
+    outs = tv.accept_sample(sets[0][0], float(w.temperature), sets[0][1], u, tok, par, n,
+                            workspace=ws)
+
+    def call(i):
+        lg, qd = sets[i % len(sets)]
+        tv.accept_sample(lg, float(w.temperature), qd, u, tok, par, n, outputs=outs, workspace=ws)
+
+    t = time_calls(torch, call, 4 * len(sets))
     by = accept_alg_bytes(w)
-    return {"workload": "C5: B=8, V=32000, N=32, temperature 0.7", "accept_us": round(t * 1e6, 3),
-            "alg_bytes": by, "GBps_warm": round(by / t / 1e9, 1)}
+    return {"workload": "C5: B=8, V=32000, N=32, temperature 0.7",
+            "cold": "%d rotating input copies, %.0f MiB" % (len(sets), len(sets) * per_set / 2 ** 20),
+            "accept_us": round(t * 1e6, 3), "alg_bytes": by, "GBps": round(by / t / 1e9, 1),
+            "hbm_frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def read_ceiling(tv, torch, dev):
+    """The chip's streaming-read rate: one read of a 4 GiB buffer (coalesced
+    16-byte non-temporal loads), timed over graph replays."""
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(7)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    t = time_calls(torch, lambda i: tv.read_probe(buf, sink), 10)
+    del buf
+    return {"bytes": nbytes, "us": round(t * 1e6, 1), "GBps": round(nbytes / t / 1e9, 1)}
 
 
 if __name__ == "__main__":

@@ -432,6 +432,18 @@ int tv_adapt_tree_budget(const int32_t* accept_len, const int32_t* n_nodes,
                          int n_max, float* ratio_ema, int32_t* budget, int32_t* row_start,
                          int32_t* rows_total, hipStream_t stream);
 
+/*
+ * tv_read_probe — a measurement helper, not a step of the verification:
+ * reads `bytes` of device memory at `buf` once (coalesced 16-byte
+ * non-temporal loads over up to 1024 workgroups) and XORs all of it into
+ * *sink (device memory, which the caller zeroes first if it wants the
+ * value). Its time gives the chip's streaming-read rate, the ceiling that
+ * the library's HBM-bound kernels are compared with.
+ *   buf  16-byte aligned (else TV_ERR_ALIGN); bytes > 0 and a multiple of
+ *        16 (else TV_ERR_SHAPE); buf or sink NULL: TV_ERR_NULL.
+ */
+int tv_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* Static, human-readable name of a tv_status or tv_row_status value. */
 const char* tv_status_string(int code);
 

@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.SIGNATURES) == names
@@ -334,3 +334,13 @@ def test_accept_greedy_noalloc_validation(lib):
     assert big > (2 << 20)
     assert call(B=1024) == -5
     assert lib.tv_accept_workspace_size(512, 33, 152064, 0) <= (2 << 20)
+
+
+def test_read_probe_validation(lib):
+    f = lib.tv_read_probe
+    P = ctypes.c_void_p(0x100000)
+    assert f(None, 1024, P, STREAM) == -1
+    assert f(P, 1024, None, STREAM) == -1
+    assert f(P, 0, P, STREAM) == -2
+    assert f(P, 1000, P, STREAM) == -2
+    assert f(ctypes.c_void_p(0x100004), 1024, P, STREAM) == -4

@@ -35,6 +35,7 @@ from .binding import (  # noqa: F401
     linear_rows,
     linear_swiglu_rows,
     load,
+    read_probe,
     tree_attention,
     tree_attention_packed,
 )

@@ -60,6 +60,7 @@ SIGNATURES = {
                                    _I, _P, _P, _P]),
     "tv_linear_rows": (_I, [_P, _L, _P, _L, _I, _I, _I, _P, _L, _P]),
     "tv_linear_swiglu_rows": (_I, [_P, _L, _P, _P, _L, _I, _I, _I, _P, _L, _P]),
+    "tv_read_probe": (_I, [_P, _S, _P, _P]),
     "tv_status_string": (ctypes.c_char_p, [_I]),
     "tv_version": (_I, []),
 }
@@ -637,3 +638,17 @@ def linear_swiglu_rows(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor
                                      w_gate.stride(0), M, K, N, _ptr(out), out.stride(0),
                                      _stream(x.device)), "tv_linear_swiglu_rows")
     return out
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor):
+    """Stream `buf` (a contiguous device tensor, 16-byte aligned, a multiple
+    of 16 bytes) once and XOR it into sink[0] (int32 on the same device): a
+    measurement of the streaming-read rate, not a verification step."""
+    lib = load()
+    if not isinstance(buf, torch.Tensor) or not buf.is_contiguous() or buf.device.type != "cuda":
+        raise TVError("buf must be a contiguous device tensor")
+    _need(sink, "sink", torch.int32, buf.device)
+    if sink.numel() < 1:
+        raise TVError("sink must hold at least one int32")
+    _check(lib.tv_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                             _stream(buf.device)), "tv_read_probe")
