@@ -369,18 +369,13 @@ __global__ __launch_bounds__(kThreads) void softmax_slices_kernel(
   }
 }
 
-// Cross-lane moves of float64 values on the vector ALU (DPP and the
-// lane-swap instructions), so that reduction steps wait on the vector
-// pipeline instead of on LDS round trips. Lane patterns: kDppXor1 and
-// kDppXor2 exchange within quads (lane ^ 1, lane ^ 2); kDppHalfMirror pairs
-// lane i with 7 - i in each group of 8; kDppRowRor8 is lane ^ 8 within a row
-// of 16; kDppRowShr(n) reads lane - n within the row (lanes below n keep the
-// `old` operand).
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
-constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
-constexpr int kDppRowRor8 = 0x128;     // row_ror:8
-constexpr int kDppRowShr(int n) { return 0x110 + n; }
+// Cross-lane moves of float64 values on the vector ALU, with the DPP lane
+// patterns of tv_common.h.
+using tv::kDppHalfMirror;
+using tv::kDppRowRor8;
+using tv::kDppRowShr;
+using tv::kDppXor1;
+using tv::kDppXor2;
 
 template <int kCtrl>
 __device__ __forceinline__ double dpp_f64(double x) {

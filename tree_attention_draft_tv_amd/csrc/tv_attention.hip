@@ -196,8 +196,8 @@ __device__ void finish_non_live(const P& p, int st0, int n0, int s0) {
     for (uint64_t m = __ballot(has && st != TV_ROW_OK && nclr > 0); m; m &= m - 1) {
       const int bl = __builtin_ctzll(m);
       const int b = b0 + bl;
-      const int rows = __shfl(nclr, bl);
-      const int64_t r0 = seq_row0(p, b, __shfl(start, bl));
+      const int rows = __builtin_amdgcn_readlane(nclr, bl);
+      const int64_t r0 = seq_row0(p, b, __builtin_amdgcn_readlane(start, bl));
       const int64_t o0 = r0 * p.Hq * D;
       float* l = p.lse + r0 * p.Hq;
       const int per_seq = rows * p.Hq * D4;
@@ -225,12 +225,6 @@ template <class P>
 __device__ __forceinline__ int live_len(const P& p, int b) {
   int n, L, start;
   return seq_check(p, b, n, L, start) == TV_ROW_OK ? L : -1;
-}
-
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
 }
 
 // Every wave loads the committed lengths of the first 64 sequences once
@@ -304,7 +298,7 @@ template <class P>
 __device__ int total_units(const P& p, int len0, int K) {
   int acc = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) acc += units_of(p, block_len(p, b0, len0), K);
-  return wave_sum_i(acc);
+  return tv::wave_sum_i32(acc);
 }
 
 // Keys per unit: the caller's fixed chunk, else the smallest multiple of 64
@@ -321,9 +315,8 @@ __device__ int choose_unit(const P& p, int len0) {
     maxl = max(maxl, L);
     keys += max(L, 0);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) maxl = max(maxl, __shfl_xor(maxl, o));
-  keys = wave_sum_i(keys);
+  maxl = tv::wave_max_i32(maxl);
+  keys = tv::wave_sum_i32(keys);
   // One unit per pair (L + kTreeExtra <= hi). Also the only choice when the
   // caller passed no workspace for partials.
   const int hi = max(kMinUnit, (maxl + kTreeExtra + 63) / 64 * 64);
@@ -364,19 +357,15 @@ __device__ bool decode_unit(const P& p, int len0, int K, int u, int& b, int& kvh
   int base = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     const int cnt = units_of(p, block_len(p, b0, len0), K);
-    int inc = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
-    }
-    const int tot = __shfl(inc, 63);
+    const int inc = tv::wave_scan_i32(cnt, lane);
+    const int tot = __builtin_amdgcn_readlane(inc, 63);
     if (u < base + tot) {
       const uint64_t hit = __ballot(base + inc > u);
       const int l = __builtin_ctzll(hit);
       b = b0 + l;
-      const int per_pair = __shfl(cnt, l) / (p.Hkv * p.RG);
-      const int local = u - base - (__shfl(inc, l) - __shfl(cnt, l));
+      const int cnt_l = __builtin_amdgcn_readlane(cnt, l);
+      const int per_pair = cnt_l / (p.Hkv * p.RG);
+      const int local = u - base - (__builtin_amdgcn_readlane(inc, l) - cnt_l);
       nch = per_pair;
       const int pair = local / per_pair;
       c = local - pair * per_pair;
@@ -397,14 +386,9 @@ __device__ void write_sched(const P& p, int len0, int K) {
   int base = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     const int cnt = units_of(p, block_len(p, b0, len0), K);
-    int inc = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
-    }
+    const int inc = tv::wave_scan_i32(cnt, lane);
     if (b0 + lane < p.B) p.sched[1 + b0 + lane] = base + inc - cnt;
-    base += __shfl(inc, 63);
+    base += __builtin_amdgcn_readlane(inc, 63);
   }
 }
 
@@ -452,6 +436,22 @@ __device__ __forceinline__ int v_swz(int key) {
 // every outstanding global load (vmcnt(0)), which drains the HBM->LDS copies
 // of the tiles still in flight; the ring's explicit TV_WAIT_VMCNT waits
 // already guarantee that the tile about to be read has landed.
+// A 16-byte store at device scope (sc1): written through the XCD's L2 to
+// memory instead of staying dirty there. Used for the split-KV partials,
+// which only the combine reads: the end of the split kernel then has no L2
+// write-back of ~30 MB to wait for (-2 us per call at C3). The compiler does
+// not see the store inside the asm, so the asm itself supplies the wait
+// states that a VALU write to the data registers of a preceding store of
+// more than 8 bytes needs (2 on gfx950; s_nop 2 gives 3): the registers are
+// free for reuse right after the statement. (Two agent-scope atomic 8-byte
+// stores, which the compiler does track, cost the C3 kernel 39 spilled
+// registers, some inside the main loop.) V is a 16-byte vector type.
+template <class V>
+__device__ __forceinline__ void store_wt16(void* ptr, V v) {
+  static_assert(sizeof(V) == 16, "16-byte stores");
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 2" ::"v"(ptr), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -981,16 +981,15 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
         for (int dp = 0; dp < DT / 2; ++dp) {
           const f32x4_t v0 = o[2 * dp][rt];
           const f32x4_t v1 = o[2 * dp + 1][rt];
-          *reinterpret_cast<uint4*>(dst + 8 * dp) =
-              make_uint4(pack2(v0[0], v0[1]), pack2(v0[2], v0[3]), pack2(v1[0], v1[1]),
-                         pack2(v1[2], v1[3]));
+          typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+          store_wt16(dst + 8 * dp, u32x4_t{pack2(v0[0], v0[1]), pack2(v0[2], v0[3]),
+                                           pack2(v1[0], v1[1]), pack2(v1[2], v1[3])});
         }
       } else {
         float* dst = p.part_o + prow * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const f32x4_t v = o[dt][rt];
-          *reinterpret_cast<float4*>(dst + 16 * dt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+          store_wt16(dst + 16 * dt + 4 * g, o[dt][rt]);
         }
       }
       if (g == 0)
@@ -1167,6 +1166,33 @@ constexpr int combine_rows_per_block() {
   return kThreadsCombine / (D / combine_epl<Q16>());
 }
 
+// op-reduction over the LPR (8, 16, 32 or 64) lanes of an aligned lane
+// group, in every lane of the group: DPP steps within groups of 8 and rows of
+// 16, then the row-pair and half-wave swaps (vector ALU only; __shfl_xor
+// would be an LDS round trip per step).
+template <int LPR, class Op>
+__device__ __forceinline__ float row_reduce(float x, Op op) {
+  static_assert(LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "lane groups of 8 to 64");
+  auto dpp = [](float v, auto ctrl) __attribute__((always_inline)) {
+    return __int_as_float(tv::dpp_i32<decltype(ctrl)::value>(__float_as_int(v)));
+  };
+  x = op(x, dpp(x, std::integral_constant<int, tv::kDppXor1>()));
+  x = op(x, dpp(x, std::integral_constant<int, tv::kDppXor2>()));
+  x = op(x, dpp(x, std::integral_constant<int, tv::kDppHalfMirror>()));
+  if constexpr (LPR >= 16) x = op(x, dpp(x, std::integral_constant<int, tv::kDppRowRor8>()));
+  if constexpr (LPR >= 32) {
+    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                      false, false);
+    x = op(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  }
+  if constexpr (LPR == 64) {
+    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                      false, false);
+    x = op(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+  }
+  return x;
+}
+
 template <int D, bool Q16, bool PACKED>
 __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParamsT<PACKED> p) {
   constexpr int EPL = combine_epl<Q16>();                        // entries per lane
@@ -1256,8 +1282,7 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < MPL; ++j) m = fmaxf(m, valid[j] ? mine[j].x : -INFINITY);
-#pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, LPR));
+    m = row_reduce<LPR>(m, [](float a, float b) { return fmaxf(a, b); });
     m = fmaxf(m, mstar);  // units with finite m only (a live row's reference always is)
     const float sc = mstar == -INFINITY ? 0.f : exp2f(mstar - m);
     float wo[MPL];
@@ -1268,8 +1293,7 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
       ls = fmaf(mine[j].y, wk, ls);
       wo[j] = Q16 ? wk * (mine[j].z * (1.f / 32767.f)) : wk;
     }
-#pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) ls += __shfl_xor(ls, o, LPR);
+    ls = row_reduce<LPR>(ls, [](float a, float b) { return a + b; });
     lstar = fmaf(lstar, sc, ls);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] *= sc;
