@@ -998,7 +998,13 @@ def test_attention_packed_more_than_64_sequences():
     fin = live & (l_ref > -np.inf)
     assert np.all(l[live & ~fin] == -np.inf)
     assert np.abs(l[fin] - l_ref[fin]).max() <= 1e-4
-    # And bitwise equal to the padded call for every live sequence.
+    # And bitwise equal to the padded call for every live sequence, given the
+    # same live set: the balanced partition spans every live sequence, so
+    # the sequence whose packed start is out of bounds (not live here) is
+    # made not live in the padded call too (context past its bound).
+    ctx_pad = ctx.copy()
+    ctx_pad[live_late[1]] = w.max_ctx + 1
+    d["ctx_len"] = torch.from_numpy(ctx_pad.astype(np.int32)).cuda()
     o_pad, l_pad, _ = run_attention(w, d, mask)
     for b in range(w.B):
         n = int(w.n_nodes[b])

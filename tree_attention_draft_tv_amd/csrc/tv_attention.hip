@@ -92,7 +92,7 @@ struct AttnParams {
   void* out;        // [rows][Hq][D] fp32, or bf16 when out_bf16
   int out_bf16;
   float* lse;
-  int32_t* sched;   // [0] keys per unit, [1 + b] first unit of sequence b
+  int32_t* sched;   // table for the combine (see write_sched)
   float* part_o;    // [unit][rows_wg][D], un-normalised: fp32 in d order, or int16 fixed
                     // point (q16) with each row as [g][dt][e] (d = 16 dt + 4 g + e)
   float4* part_ml;  // per pair [rows_wg][unit of the pair]: (reference max in log2 units, sum,
@@ -210,13 +210,25 @@ __device__ void finish_non_live(const P& p, int st0, int n0, int s0) {
 }
 
 // ------------------------------------------------------------ schedule ---
-// The keys of every live (sequence, KV head, row group) pair are cut into
-// units of K keys (the last unit of a pair also holds the tree block); one
-// workgroup processes one unit at a time. Units are numbered by sequence,
-// then pair, then chunk, so the units of a pair are consecutive. Every wave
-// derives the schedule from ctx_len / n_nodes by itself (no host sync, no
-// inter-workgroup communication); the combine kernel reads K and the first
-// unit of each sequence from the table workgroup 0 writes.
+// The keys of every live (sequence, KV head, row group) pair are processed
+// as pieces, one workgroup per piece at a time, under one of two partitions:
+//  * units (a caller-fixed chunk_keys, or one unit per pair when the caller
+//    passed no workspace for partials): a pair's keys cut into units of K
+//    keys, numbered pair-major; workgroup w takes units w', w' + nw, ...
+//    With a fixed chunk a row's result does not depend on the other
+//    sequences of the batch.
+//    With chunk_keys == 0 (balanced, the default) K is the smallest size
+//    that gives at most one unit per workgroup: units then split each pair
+//    evenly and never straddle pairs.
+//  * stream-K (balanced, when even one unit per pair leaves more units than
+//    workgroups): every pair is a run of tiles on one line (below); each
+//    active workgroup takes an equal share of the line, which cuts at most a
+//    few pairs (whole pairs as units left a second pass to a few
+//    workgroups). Units are kept while they fit: a workgroup whose share
+//    straddles two pairs pays a second piece's start and epilogue.
+// Every wave derives the partition from ctx_len / n_nodes by itself (no host
+// sync, no communication between workgroups); the combine kernel reads the
+// table workgroup 0 writes.
 
 constexpr int kMinUnit = 256;  // smallest balanced unit (keys)
 
@@ -301,9 +313,11 @@ __device__ int total_units(const P& p, int len0, int K) {
   return tv::wave_sum_i32(acc);
 }
 
-// Keys per unit: the caller's fixed chunk, else the smallest multiple of 64
+// Keys per unit: the caller's fixed chunk; else the smallest multiple of 64
 // (at least kMinUnit) that cuts the launch into at most nw units, so that a
-// single pass of the nw workgroups covers it with the least work per unit.
+// single pass of the nw workgroups covers it with the least work per unit;
+// else (more pairs than workgroups, or no workspace for partials) one unit
+// per pair: L + kTreeExtra <= K for every sequence.
 template <class P>
 __device__ int choose_unit(const P& p, int len0) {
   if (p.kunit > 0) return p.kunit;
@@ -317,8 +331,6 @@ __device__ int choose_unit(const P& p, int len0) {
   }
   maxl = tv::wave_max_i32(maxl);
   keys = tv::wave_sum_i32(keys);
-  // One unit per pair (L + kTreeExtra <= hi). Also the only choice when the
-  // caller passed no workspace for partials.
   const int hi = max(kMinUnit, (maxl + kTreeExtra + 63) / 64 * 64);
   if (p.part_o == nullptr) return hi;
   // Lower bound: the committed keys of all pairs spread evenly over nw
@@ -344,6 +356,97 @@ __device__ int choose_unit(const P& p, int len0) {
       bad = mid;
   }
   return good;
+}
+
+// ---- stream-K line. Every live pair is a run of pair_tiles(L) tiles:
+// ceil(L / 64) of committed keys, then kTreeTiles standing for its masked
+// tree block (about what it costs); pairs lie pair-major along the line
+// (the pairs of a sequence consecutive, KV head major, then row group).
+// Active workgroup v < nwa takes tiles [sk_start(v), sk_start(v + 1)),
+// sk_start(v) = floor(v W / nwa): equal shares of at least kMinPieceTiles
+// tiles (nwa = W / kMinPieceTiles, at least 1 and at most nw, so that every
+// share holds at least one tile). The piece of pair p that workgroup v holds
+// keeps its partial rows in
+// slot p + v: slots increase along the line, so the slots of a pair are
+// consecutive from p + v_lo and there are at most pairs + nw of them.
+constexpr int kTreeTiles = kTreeExtra / kKB;
+constexpr int kMinPieceTiles = kMinUnit / kKB;
+
+struct SkLine {
+  int W;    // tiles on the line (the host keeps it below 2^31)
+  int nwa;  // active workgroups, 0 when the line is empty
+};
+
+__device__ __forceinline__ int pair_tiles(int L) { return (L + kKB - 1) / kKB + kTreeTiles; }
+
+__device__ __forceinline__ int sk_start(const SkLine& s, int v) {
+  return v >= s.nwa ? s.W : static_cast<int>(static_cast<int64_t>(v) * s.W / s.nwa);
+}
+
+// The workgroup whose share holds tile x (0 <= x < W): the largest v with
+// sk_start(v) <= x.
+__device__ __forceinline__ int sk_owner(const SkLine& s, int x) {
+  return static_cast<int>((static_cast<int64_t>(x + 1) * s.nwa - 1) / s.W);
+}
+
+// Tiles on the line and active workgroups (wave-uniform; every lane calls).
+template <class P>
+__device__ SkLine sk_line(const P& p, int len0) {
+  const int per = p.Hkv * p.RG;
+  int w = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int L = block_len(p, b0, len0);
+    w += L < 0 ? 0 : per * pair_tiles(L);
+  }
+  SkLine s;
+  s.W = tv::wave_sum_i32(w);
+  s.nwa = s.W == 0 ? 0 : min(p.nw, max(1, s.W / kMinPieceTiles));
+  return s;
+}
+
+// The live sequence b whose tiles hold tile x, with the tiles (sb) and pairs
+// (pb) before it on the line: lane scans of the per-sequence tiles and live
+// flags, 64 sequences a block, and a ballot (wave-uniform).
+template <class P>
+__device__ void sk_locate(const P& p, int len0, int x, int& b, int& sb, int& pb) {
+  const int lane = threadIdx.x & 63;
+  const int per = p.Hkv * p.RG;
+  int base = 0, pbase = 0;
+  b = -1;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int L = block_len(p, b0, len0);
+    const int live = L < 0 ? 0 : 1;
+    const int work = live * per * pair_tiles(max(L, 0));
+    const int inc = tv::wave_scan_i32(work, lane);
+    const int linc = tv::wave_scan_i32(live, lane);
+    const int tot = __builtin_amdgcn_readlane(inc, 63);
+    if (x < base + tot) {
+      const int l = __builtin_ctzll(__ballot(base + inc > x));
+      b = b0 + l;
+      sb = base + __builtin_amdgcn_readlane(inc - work, l);
+      pb = pbase + per * __builtin_amdgcn_readlane(linc - live, l);
+      return;
+    }
+    base += tot;
+    pbase += per * __builtin_amdgcn_readlane(linc, 63);
+  }
+}
+
+// The pieces of the pair whose tiles start at sp (wp tiles, first pair index
+// pidx on the line): first slot, piece count and the index of the first
+// empty piece. Pieces jt .. np - 2 hold only tree-cost tiles without the
+// pair's end, so no keys: they are skipped by the split and the combine.
+struct SkPair {
+  int base, np, jt, v_lo;
+};
+__device__ __forceinline__ SkPair sk_pair(const SkLine& s, int sp, int wp, int pidx) {
+  SkPair r;
+  r.v_lo = sk_owner(s, sp);
+  r.np = sk_owner(s, sp + wp - 1) - r.v_lo + 1;
+  r.base = pidx + r.v_lo;
+  const int ct = wp - kTreeTiles;  // committed tiles
+  r.jt = ct > 0 ? sk_owner(s, sp + ct - 1) - r.v_lo + 1 : 0;
+  return r;
 }
 
 // Unit u -> (b, kvh, rg, c) and the pair's unit count nch; false past the
@@ -378,17 +481,30 @@ __device__ bool decode_unit(const P& p, int len0, int K, int u, int& b, int& kvh
   return false;
 }
 
-// Table for the combine kernel: K, then the first unit of every sequence.
+// Table for the combine kernel. Unit mode: [0] = K, [1] = 0, [2 + 2 b] =
+// first unit of sequence b. Stream-K: [0] = W, [1] = nwa (> 0), [2 + 2 b] =
+// tiles before sequence b on the line, [3 + 2 b] = pairs before it.
 template <class P>
-__device__ void write_sched(const P& p, int len0, int K) {
+__device__ void write_sched(const P& p, int len0, int K, const SkLine& s, bool stream_k) {
   const int lane = threadIdx.x & 63;
-  if (lane == 0) p.sched[0] = K;
-  int base = 0;
+  const int per = p.Hkv * p.RG;
+  if (lane == 0) {
+    p.sched[0] = stream_k ? s.W : K;
+    p.sched[1] = stream_k ? s.nwa : 0;
+  }
+  int base = 0, pbase = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
-    const int cnt = units_of(p, block_len(p, b0, len0), K);
+    const int L = block_len(p, b0, len0);
+    const int live = L < 0 ? 0 : 1;
+    const int cnt = stream_k ? live * per * pair_tiles(max(L, 0)) : units_of(p, L, K);
     const int inc = tv::wave_scan_i32(cnt, lane);
-    if (b0 + lane < p.B) p.sched[1 + b0 + lane] = base + inc - cnt;
+    const int linc = tv::wave_scan_i32(live, lane);
+    if (b0 + lane < p.B) {
+      p.sched[2 + 2 * (b0 + lane)] = base + inc - cnt;
+      p.sched[3 + 2 * (b0 + lane)] = pbase + per * (linc - live);
+    }
     base += __builtin_amdgcn_readlane(inc, 63);
+    pbase += per * __builtin_amdgcn_readlane(linc, 63);
   }
 }
 
@@ -399,6 +515,116 @@ __device__ __forceinline__ int first_unit(const AttnParams& p) {
   const int w = blockIdx.x;
   return (w & 7) * (p.nw >> 3) + (w >> 3);
 }
+
+// One piece of work: pair (b, kvh, rg), keys from kbeg: to kcut, or with
+// `last` (it holds the tree block) through the committed keys and the tree
+// block (to L + n). Partial rows in slot `slot`, the (m, l) records of the
+// pair's np pieces from slot `base` (this one is piece j); np == 1: the piece
+// is the whole pair and is written directly.
+struct Piece {
+  int b, kvh, rg;
+  int kbeg, kcut;
+  bool last;
+  int slot, base, np, j;
+};
+
+// Committed length of sequence b (live): from the lane cache for b < 64.
+template <class P>
+__device__ __forceinline__ int seq_len(const P& p, int b, int len0) {
+  return b < 64 ? __builtin_amdgcn_readlane(len0, b) : live_len(p, b);
+}
+
+// Unit mode: unit u as a piece; false past the last unit (wave-uniform).
+template <class P>
+__device__ bool unit_piece(const P& p, int len0, int K, int u, Piece& pc) {
+  int b, kvh, rg, c, nch;
+  if (!decode_unit(p, len0, K, u, b, kvh, rg, c, nch)) return false;
+  const int L = seq_len(p, b, len0);
+  pc.b = b;
+  pc.kvh = kvh;
+  pc.rg = rg;
+  pc.last = c == nch - 1;
+  pc.kbeg = unit_start(p, L, K, nch, c);
+  pc.kcut = pc.last ? L : unit_start(p, L, K, nch, c + 1);
+  pc.slot = u;
+  pc.base = u - c;
+  pc.np = nch;
+  pc.j = c;
+  return true;
+}
+
+// Stream-K: the next non-empty piece of workgroup v's share from tile x on;
+// next_x is the tile after it. False when the share holds no more.
+template <class P>
+__device__ bool sk_piece(const P& p, int len0, const SkLine& s, int v, int x, Piece& pc,
+                         int& next_x) {
+  const int e = sk_start(s, v + 1);
+  while (x < e) {
+    int b, sb, pb;
+    sk_locate(p, len0, x, b, sb, pb);
+    if (b < 0) return false;
+    const int L = seq_len(p, b, len0);
+    const int wp = pair_tiles(L);
+    const int q = (x - sb) / wp;
+    const int sp = sb + q * wp;
+    const int x1 = min(e - sp, wp);
+    next_x = sp + x1;
+    const bool last = x1 == wp;
+    const int kbeg = min((x - sp) * kKB, L);
+    const int kcut = last ? L : min(x1 * kKB, L);
+    if (!last && kbeg >= kcut) {  // tree-cost tiles only, without the pair's end
+      x = next_x;
+      continue;
+    }
+    const SkPair pr = sk_pair(s, sp, wp, pb + q);
+    pc.b = b;
+    pc.kvh = q / p.RG;
+    pc.rg = q - pc.kvh * p.RG;
+    pc.kbeg = kbeg;
+    pc.kcut = kcut;
+    pc.last = last;
+    pc.np = pr.np;
+    pc.base = pr.base;
+    pc.j = v - pr.v_lo;
+    pc.slot = pr.base + pc.j;
+    return true;
+  }
+  return false;
+}
+
+// Runs run(piece) for every piece of this workgroup, with a barrier between
+// pieces (the previous piece's LDS reads are done). Stream-K: workgroup
+// blockIdx takes share v = (blockIdx mod 8) c + blockIdx / 8 (c = ceil(nwa /
+// 8)) if v < nwa and blockIdx / 8 < c, so that neighbouring shares (which cut
+// the same pairs) run on one XCD under round-robin dispatch. Unit mode:
+// units first_unit(blockIdx) + k nw.
+template <class P, class Run>
+__device__ __forceinline__ void for_each_piece(const P& p, int len0, int K, const SkLine& s,
+                                               bool stream_k, Run run) {
+  Piece pc;
+  bool first = true;
+  if (stream_k) {
+    const int per_xcd = (s.nwa + 7) >> 3;
+    const int k = blockIdx.x >> 3;
+    const int v = (blockIdx.x & 7) * per_xcd + k;
+    if (k >= per_xcd || v >= s.nwa) return;
+    int x = sk_start(s, v), nx;
+    while (sk_piece(p, len0, s, v, x, pc, nx)) {
+      if (!first) __syncthreads();
+      first = false;
+      run(pc);
+      x = nx;
+    }
+  } else {
+    for (int u = first_unit(p);; u += p.nw) {
+      if (!unit_piece(p, len0, K, u, pc)) break;
+      if (!first) __syncthreads();
+      first = false;
+      run(pc);
+    }
+  }
+}
+
 
 __device__ __forceinline__ bool tree_visible(const uint32_t* s_mask, int W, int node, int j) {
   return (s_mask[node * W + (j >> 5)] >> (j & 31)) & 1u;
@@ -540,17 +766,21 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
   int n0, s0, st0;
   const int len0 = lane_len(p, n0, s0, st0);
   const int K = choose_unit(p, len0);
-  if (p.sched && blockIdx.x == 0 && wave == 0) write_sched(p, len0, K);
+  const bool stream_k =
+      p.kunit == 0 && p.part_o != nullptr && total_units(p, len0, K) > p.nw;
+  SkLine sk{0, 0};
+  if (stream_k) sk = sk_line(p, len0);
+  if (p.sched && blockIdx.x == 0 && wave == 0) write_sched(p, len0, K, sk, stream_k);
 
-  // ---- one unit: keys [c K, ...) of (b, kvh), packed rows of row group rg ----
-  auto run_unit = [&](int u, int b, int kvh, int rg, int c, int nch)
-                      __attribute__((always_inline)) {
+  // ---- one piece: keys [kbeg, kend) of (b, kvh), packed rows of row group rg ----
+  auto run_unit = [&](const Piece& pc) __attribute__((always_inline)) {
+  const int b = pc.b, kvh = pc.kvh, rg = pc.rg;
   int n, L;
   int64_t srow0;  // output row of tree row 0
   unit_seq(p, b, len0, n0, s0, n, L, srow0);
-  const bool last = (c == nch - 1);
-  const int kbeg = unit_start(p, L, K, nch, c);
-  const int kend = last ? L + n : unit_start(p, L, K, nch, c + 1);
+  const bool last = pc.last;
+  const int kbeg = pc.kbeg;
+  const int kend = last ? L + n : pc.kcut;
   const int ntile = (kend - kbeg + kKB - 1) / kKB;
   const int kv_ss = static_cast<int>(p.kv_ss);  // host checks capacity * stride < 2^31
 
@@ -931,7 +1161,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
 
   // ---- epilogue ----
   if (!wave_active) return;
-  const bool direct = (nch == 1);
+  const bool direct = (pc.np == 1);
   // With one probability part the unit partials are stored as 16-bit fixed
   // point against the row's largest |O| (error at most that / 65534 per
   // entry, i.e. max|v| / 65534 after normalisation); more parts keep fp32.
@@ -967,7 +1197,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
       }
       if (g == 0) p.lse[orow] = seen ? (mref[rt] + __log2f(l_tot[rt])) * kLn2 : -INFINITY;
     } else {
-      const int64_t prow = static_cast<int64_t>(u) * p.rows_wg + (r - rg * kRowsWG);
+      const int64_t prow = static_cast<int64_t>(pc.slot) * p.rows_wg + (r - rg * kRowsWG);
       if constexpr (kQ16) {
         // Row layout [g][dt][e] (the lane's 4 DT entries contiguous: 16-byte
         // stores); entry (g, dt, e) is d = 16 dt + 4 g + e.
@@ -993,7 +1223,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
         }
       }
       if (g == 0)
-        p.part_ml[static_cast<int64_t>(u - c) * p.rows_wg + (r - rg * kRowsWG) * nch + c] =
+        p.part_ml[static_cast<int64_t>(pc.base) * p.rows_wg + (r - rg * kRowsWG) * pc.np + pc.j] =
             make_float4(mref[rt], l_tot[rt], amax[rt], 0.f);
     }
   }
@@ -1001,13 +1231,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
 
   // Padding outputs first: their stores drain while the first tiles load.
   finish_non_live<D>(p, st0, n0, s0);
-  const int u0 = first_unit(p);
-  for (int u = u0;; u += p.nw) {
-    int b, kvh, rg, c, nch;
-    if (!decode_unit(p, len0, K, u, b, kvh, rg, c, nch)) break;
-    if (u != u0) __syncthreads();  // the previous unit's LDS reads are done
-    run_unit(u, b, kvh, rg, c, nch);
-  }
+  for_each_piece(p, len0, K, sk, stream_k, run_unit);
 }
 
 // ---------------------------------------------------------- fp32 (VALU) ---
@@ -1027,16 +1251,20 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParamsT
   int n0, s0, st0;
   const int len0 = lane_len(p, n0, s0, st0);
   const int K = choose_unit(p, len0);
-  if (p.sched && blockIdx.x == 0 && tid < tv::kWave) write_sched(p, len0, K);
+  const bool stream_k =
+      p.kunit == 0 && p.part_o != nullptr && total_units(p, len0, K) > p.nw;
+  SkLine sk{0, 0};
+  if (stream_k) sk = sk_line(p, len0);
+  if (p.sched && blockIdx.x == 0 && tid < tv::kWave) write_sched(p, len0, K, sk, stream_k);
 
-  auto run_unit = [&](int u, int b, int kvh, int rg, int c, int nch)
-                      __attribute__((always_inline)) {
+  auto run_unit = [&](const Piece& pc) __attribute__((always_inline)) {
+  const int b = pc.b, kvh = pc.kvh, rg = pc.rg;
   int n, L;
   int64_t srow0;  // output row of tree row 0
   unit_seq(p, b, len0, n0, s0, n, L, srow0);
-  const bool last = (c == nch - 1);
-  const int kbeg = unit_start(p, L, K, nch, c);
-  const int kend = last ? L + n : unit_start(p, L, K, nch, c + 1);
+  const bool last = pc.last;
+  const int kbeg = pc.kbeg;
+  const int kend = last ? L + n : pc.kcut;
   if (last) {
     const uint32_t* mrow = p.mask + static_cast<int64_t>(b) * p.T * p.W;
     for (int idx = tid; idx < n * p.W; idx += kThreadsF32) sMask[idx] = mrow[idx];
@@ -1111,7 +1339,7 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParamsT
 
   if (r >= p.R) return;
   const int i = row_node(p, r);
-  if (nch == 1) {
+  if (pc.np == 1) {
     const bool live = node >= 0;
     if (PACKED && !live) return;  // packed: rows past n do not exist
     const int64_t orow = (srow0 + i) * p.Hq + h;
@@ -1123,24 +1351,18 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParamsT
                  ov[d + 3] * inv);
     if (quarter == 0) p.lse[orow] = seen ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
   } else {
-    const int64_t prow = static_cast<int64_t>(u) * p.rows_wg + (r - rg * kRowsWGf32);
+    const int64_t prow = static_cast<int64_t>(pc.slot) * p.rows_wg + (r - rg * kRowsWGf32);
 #pragma unroll
     for (int d = 0; d < DQ; ++d) p.part_o[prow * D + quarter * DQ + d] = ov[d];
     if (quarter == 0)
-      p.part_ml[static_cast<int64_t>(u - c) * p.rows_wg + (r - rg * kRowsWGf32) * nch + c] =
+      p.part_ml[static_cast<int64_t>(pc.base) * p.rows_wg + (r - rg * kRowsWGf32) * pc.np + pc.j] =
           make_float4(m_run, l_run, 0.f, 0.f);
   }
   };
 
   // Padding outputs first: their stores drain while the first tiles load.
   finish_non_live<D>(p, st0, n0, s0);
-  const int u0 = first_unit(p);
-  for (int u = u0;; u += p.nw) {
-    int b, kvh, rg, c, nch;
-    if (!decode_unit(p, len0, K, u, b, kvh, rg, c, nch)) break;
-    if (u != u0) __syncthreads();  // the previous unit's LDS reads are done
-    run_unit(u, b, kvh, rg, c, nch);
-  }
+  for_each_piece(p, len0, K, sk, stream_k, run_unit);
 }
 
 // ----------------------------------------------------- log-sum-exp merge ---
@@ -1208,17 +1430,35 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   // Every scalar input in one round trip.
   const int n = p.n_nodes[b];
   const int L = p.ctx_len[b];
-  const int K = p.sched[0];
-  const int first = p.sched[1 + b];
+  const int t0 = p.sched[0];
+  const int t1 = p.sched[1];
+  const int t2 = p.sched[2 + 2 * b];
+  const int t3 = p.sched[3 + 2 * b];
   const int start = PACKED ? p.row_start[b] : 0;
   // Keeps the loads ahead of the branches below (the compiler would
   // otherwise sink each one into the branch that first needs it and wait
   // for them one by one).
-  asm volatile("" ::"s"(n), "s"(L), "s"(K), "s"(first), "s"(start));
+  asm volatile("" ::"s"(n), "s"(L), "s"(t0), "s"(t1), "s"(t2), "s"(t3), "s"(start));
   if (r >= p.R) return;
   if (seq_status(p, n, L, start) != TV_ROW_OK) return;  // padded / invalid: done by the split
-  const int nch = pair_units(p, L, K);
-  if (nch == 1) return;                           // written directly by the split
+  const int rg = r / p.rows_wg;
+  const int rl = r - rg * p.rows_wg;
+  const int q = kvh * p.RG + rg;
+  // The pair's pieces: first slot u0, count nch; pieces jt .. nch - 2 hold
+  // no keys (stream-K only) and are skipped.
+  int nch, u0, jt;
+  if (t1 == 0) {  // unit mode: K = t0, first unit of the sequence = t2
+    nch = pair_units(p, L, t0);
+    u0 = t2 + q * nch;
+    jt = nch;
+  } else {  // stream-K: W = t0, nwa = t1, tiles and pairs before the sequence = t2, t3
+    const int wp = pair_tiles(L);
+    const SkPair pr = sk_pair(SkLine{t0, t1}, t2 + q * wp, wp, t3 + q);
+    nch = pr.np;
+    u0 = pr.base;
+    jt = pr.jt;
+  }
+  if (nch == 1) return;  // written directly by the split
   const int i = row_node(p, r);
   const int h = kvh * p.G + (r - i * p.G);
   if (i >= n && PACKED) return;  // packed: rows past n do not exist
@@ -1243,12 +1483,14 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
     if (sub == 0) p.lse[orow] = -INFINITY;
     return;
   }
-  const int rg = r / p.rows_wg;
-  const int rl = r - rg * p.rows_wg;
-  const int64_t u0 = first + static_cast<int64_t>(kvh * p.RG + rg) * nch;
-  const int64_t row_elem = (u0 * p.rows_wg + rl) * D + EPL * sub;  // entry offset of unit 0
-  const int64_t ustride = static_cast<int64_t>(p.rows_wg) * D;      // entries between units
-  const float4* pml = p.part_ml + u0 * p.rows_wg + static_cast<int64_t>(rl) * nch;
+  const int64_t row_elem =
+      (static_cast<int64_t>(u0) * p.rows_wg + rl) * D + EPL * sub;  // entry offset of piece 0
+  const int64_t ustride = static_cast<int64_t>(p.rows_wg) * D;      // entries between pieces
+  const float4* pml = p.part_ml + static_cast<int64_t>(u0) * p.rows_wg +
+                      static_cast<int64_t>(rl) * nch;
+  // Piece k holds keys: its record and partial row are read; an empty piece
+  // reads the last one (which always holds the tree block) with weight 0.
+  auto held = [&](int k) { return k < nch && (k < jt || k == nch - 1); };
   float mstar = -INFINITY, lstar = 0.f;
   float acc[EPL];
 #pragma unroll
@@ -1265,14 +1507,14 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
 #pragma unroll
     for (int j = 0; j < MPL; ++j) {
       const int kl = sub + j * LPR;
-      valid[j] = kl < U && c0 + kl < nch;
-      mine[j] = pml[min(c0 + kl, nch - 1)];
+      valid[j] = kl < U && held(c0 + kl);
+      mine[j] = pml[valid[j] ? c0 + kl : nch - 1];
     }
     using Raw = typename std::conditional<Q16, uint4, float4>::type;
     Raw v[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      const int kk = min(c0 + k, nch - 1);
+      const int kk = held(c0 + k) ? c0 + k : nch - 1;
       const int64_t off = row_elem + kk * ustride;
       if constexpr (Q16)
         v[k] = *reinterpret_cast<const uint4*>(reinterpret_cast<const int16_t*>(p.part_o) + off);
@@ -1345,26 +1587,24 @@ int grid_workgroups() {
 
 int host_chunks(int64_t L, int64_t K) { return L == 0 ? 1 : static_cast<int>((L + K - 1) / K); }
 
-// The unit size the device picks when every sequence is live with max_ctx
-// committed keys (bf16 row groups): the smallest multiple of 64, at least
-// kMinUnit, that gives at most one unit per workgroup.
-int auto_chunk(int B, int T, int Hq, int Hkv, int max_ctx) {
+// Tiles on the stream-K line when every sequence is live with max_ctx
+// committed keys, for the given packed rows per workgroup.
+int64_t line_tiles(int B, int T, int Hq, int Hkv, int max_ctx, int rows_wg) {
   const int64_t R = static_cast<int64_t>(Hq / Hkv) * T;
-  const int64_t pairs = static_cast<int64_t>(B) * Hkv * ((R + kRowsWG - 1) / kRowsWG);
-  const int64_t nw = grid_workgroups();
-  auto units = [&](int K) { return pairs * host_chunks(max_ctx, K); };
-  int lo = kMinUnit;
-  int hi = std::max(kMinUnit, (max_ctx + 63) / 64 * 64);
-  if (units(lo) <= nw) return lo;
-  if (units(hi) > nw) return hi;
-  while (hi - lo > 64) {
-    const int mid = (lo / 64 + hi / 64) / 2 * 64;
-    if (units(mid) <= nw)
-      hi = mid;
-    else
-      lo = mid;
-  }
-  return hi;
+  const int64_t pairs = static_cast<int64_t>(B) * Hkv * ((R + rows_wg - 1) / rows_wg);
+  return pairs * ((static_cast<int64_t>(max_ctx) + kKB - 1) / kKB + kTreeTiles);
+}
+
+// Keys per active workgroup of the balanced (stream-K) partition when every
+// sequence is live with max_ctx committed keys (bf16 row groups), rounded up
+// to whole tiles: a fixed chunk_keys of about that size cuts the same
+// number of units.
+int auto_chunk(int B, int T, int Hq, int Hkv, int max_ctx) {
+  const int64_t W = line_tiles(B, T, Hq, Hkv, max_ctx, kRowsWG);
+  if (W == 0) return kMinUnit;
+  const int64_t nwa =
+      std::min<int64_t>(grid_workgroups(), std::max<int64_t>(1, W / kMinPieceTiles));
+  return static_cast<int>(std::min<int64_t>((W + nwa - 1) / nwa * kKB, 1 << 30));
 }
 
 bool valid_sizes(int B, int T, int Hq, int Hkv, int D, int max_ctx, int chunk_keys) {
@@ -1375,12 +1615,15 @@ bool valid_sizes(int B, int T, int Hq, int Hkv, int D, int max_ctx, int chunk_ke
   return true;
 }
 
-// Workspace layout: the schedule table ((1 + B) int32), then partial O
-// [unit][rows_wg][D] (fp32, or int16 fixed point in the same space, each
-// row in the split lanes' order), then
-// (m, l, scale, 0) per pair as [rows_wg][unit of the pair]. Sized for the larger
-// of the bf16 (256 rows per unit) and fp32 (64 rows per unit) kernels. No
-// workspace when every pair is a single unit (written directly).
+// Workspace layout: the schedule table ((2 + 2 B) int32), then partial O
+// [slot][rows_wg][D] (fp32, or int16 fixed point in the same space, each
+// row in the split lanes' order), then (m, l, scale, 0) per pair as
+// [rows_wg][piece of the pair] from the pair's first slot. Fixed chunks use
+// one slot per unit; the balanced (stream-K) partition at most pairs + nw.
+// Sized for the larger of the bf16 (256 rows per workgroup) and fp32 (64)
+// kernels. No workspace when every pair is a single unit (written directly):
+// max_ctx <= chunk_keys, or max_ctx + kTreeExtra <= kMinUnit when balanced
+// (the kernels then take one unit per pair).
 struct WsLayout {
   size_t sched = 0, part_o = 0, part_ml = 0, total = 0;
 };
@@ -1397,14 +1640,13 @@ WsLayout workspace_layout(int B, int T, int Hq, int Hkv, int D, int max_ctx, int
       const int64_t nch = host_chunks(max_ctx, chunk_keys);
       units = nch > 1 ? pairs * nch : 0;
     } else {
-      // Every pair is one unit when max_ctx + kTreeExtra <= kMinUnit.
-      units = max_ctx + kTreeExtra > kMinUnit ? std::max(nw, pairs) : 0;
+      units = max_ctx + kTreeExtra > kMinUnit ? pairs + nw : 0;
     }
     rows_max = std::max(rows_max, units * rows_wg);
   }
   if (rows_max == 0) return w;
   w.sched = 0;
-  w.part_o = tvh::align_up(static_cast<size_t>(1 + B) * sizeof(int32_t), 256);
+  w.part_o = tvh::align_up(static_cast<size_t>(2 + 2 * static_cast<int64_t>(B)) * sizeof(int32_t), 256);
   w.part_ml = w.part_o + tvh::align_up(static_cast<size_t>(rows_max) * D * sizeof(float), 256);
   w.total = w.part_ml + tvh::align_up(static_cast<size_t>(rows_max) * sizeof(float4), 256);
   return w;
@@ -1481,6 +1723,8 @@ int attention_call(const void* q, int64_t q_sb, int64_t q_st, int64_t q_sh, cons
   if (kv_ss < 0 || static_cast<int64_t>(kv_capacity) * kv_ss + D > INT32_MAX) return TV_ERR_SHAPE;
   if (B == 0) return TV_OK;
   if (static_cast<int64_t>(B) * Hkv > 65535) return TV_ERR_SHAPE;
+  // The stream-K line is indexed with 32-bit tiles.
+  if (line_tiles(B, T, Hq, Hkv, max_ctx, kRowsWGf32) >= INT32_MAX) return TV_ERR_SHAPE;
   const WsLayout ws = workspace_layout(B, T, Hq, Hkv, D, max_ctx, chunk_keys);
   if (ws.total > 0 && (!workspace || ws_bytes < ws.total || !tvh::aligned256(workspace)))
     return TV_ERR_WORKSPACE;
