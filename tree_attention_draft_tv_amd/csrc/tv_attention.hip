@@ -220,12 +220,12 @@ __device__ void finish_non_live(const P& p, int st0, int n0, int s0) {
 //    With chunk_keys == 0 (balanced, the default) K is the smallest size
 //    that gives at most one unit per workgroup: units then split each pair
 //    evenly and never straddle pairs.
-//  * stream-K (balanced, when even one unit per pair leaves more units than
-//    workgroups): every pair is a run of tiles on one line (below); each
-//    active workgroup takes an equal share of the line, which cuts at most a
-//    few pairs (whole pairs as units left a second pass to a few
-//    workgroups). Units are kept while they fit: a workgroup whose share
-//    straddles two pairs pays a second piece's start and epilogue.
+//  * stream-K (balanced, when the live pairs P outnumber the workgroups):
+//    every workgroup takes floor(P / nw) whole pairs (written directly),
+//    and the other P mod nw pairs, laid on a line of tiles (below), are
+//    shared out equally over the workgroups, which cuts them into pieces
+//    (whole pairs alone left a second pass to a few workgroups). Units are
+//    kept while they fit: a piece costs its own start and epilogue.
 // Every wave derives the partition from ctx_len / n_nodes by itself (no host
 // sync, no communication between workgroups); the combine kernel reads the
 // table workgroup 0 writes.
@@ -305,6 +305,12 @@ __device__ __forceinline__ int units_of(const AttnParams& p, int L, int K) {
   return L < 0 ? 0 : pair_units(p, L, K) * p.Hkv * p.RG;
 }
 
+// Committed length of sequence b (live): from the lane cache for b < 64.
+template <class P>
+__device__ __forceinline__ int seq_len(const P& p, int b, int len0) {
+  return b < 64 ? __builtin_amdgcn_readlane(len0, b) : live_len(p, b);
+}
+
 // Units of the whole launch (wave-uniform; every lane must call).
 template <class P>
 __device__ int total_units(const P& p, int len0, int K) {
@@ -362,19 +368,20 @@ __device__ int choose_unit(const P& p, int len0) {
 // ceil(L / 64) of committed keys, then kTreeTiles standing for its masked
 // tree block (about what it costs); pairs lie pair-major along the line
 // (the pairs of a sequence consecutive, KV head major, then row group).
-// Active workgroup v < nwa takes tiles [sk_start(v), sk_start(v + 1)),
-// sk_start(v) = floor(v W / nwa): equal shares of at least kMinPieceTiles
-// tiles (nwa = W / kMinPieceTiles, at least 1 and at most nw, so that every
-// share holds at least one tile). The piece of pair p that workgroup v holds
-// keeps its partial rows in
-// slot p + v: slots increase along the line, so the slots of a pair are
-// consecutive from p + v_lo and there are at most pairs + nw of them.
+// The first p0 = nw floor(P / nw) pairs are whole-pair units; the rest of
+// the line, from tile off, holds W tiles. Active workgroup v < nwa takes
+// tiles off + [sk_start(v), sk_start(v + 1)), sk_start(v) = floor(v W /
+// nwa), nwa = min(nw, W): equal shares of at least one tile. The piece of
+// pair p that workgroup v holds keeps its partial rows in slot (p - p0) +
+// v: slots increase along the line, so the slots of a pair are consecutive
+// from (p - p0) + v_lo and there are fewer than P + nw of them.
 constexpr int kTreeTiles = kTreeExtra / kKB;
-constexpr int kMinPieceTiles = kMinUnit / kKB;
 
 struct SkLine {
-  int W;    // tiles on the line (the host keeps it below 2^31)
-  int nwa;  // active workgroups, 0 when the line is empty
+  int W;    // tiles of the shared part of the line (the host keeps the line below 2^31)
+  int nwa;  // active workgroups of the shared part, 0 when it is empty
+  int off;  // line tiles before it
+  int p0;   // pairs before it (whole-pair units)
 };
 
 __device__ __forceinline__ int pair_tiles(int L) { return (L + kKB - 1) / kKB + kTreeTiles; }
@@ -383,32 +390,18 @@ __device__ __forceinline__ int sk_start(const SkLine& s, int v) {
   return v >= s.nwa ? s.W : static_cast<int>(static_cast<int64_t>(v) * s.W / s.nwa);
 }
 
-// The workgroup whose share holds tile x (0 <= x < W): the largest v with
-// sk_start(v) <= x.
+// The workgroup whose share holds tile x of the shared part (0 <= x < W):
+// the largest v with sk_start(v) <= x.
 __device__ __forceinline__ int sk_owner(const SkLine& s, int x) {
   return static_cast<int>((static_cast<int64_t>(x + 1) * s.nwa - 1) / s.W);
 }
 
-// Tiles on the line and active workgroups (wave-uniform; every lane calls).
+// The live sequence b whose tiles hold line tile `key` (by_pair: whose
+// pairs hold pair index `key`), with the tiles (sb) and pairs (pb) before it
+// on the line: lane scans of the per-sequence tiles and live flags, 64
+// sequences a block, and a ballot (wave-uniform; b = -1 past the line).
 template <class P>
-__device__ SkLine sk_line(const P& p, int len0) {
-  const int per = p.Hkv * p.RG;
-  int w = 0;
-  for (int b0 = 0; b0 < p.B; b0 += 64) {
-    const int L = block_len(p, b0, len0);
-    w += L < 0 ? 0 : per * pair_tiles(L);
-  }
-  SkLine s;
-  s.W = tv::wave_sum_i32(w);
-  s.nwa = s.W == 0 ? 0 : min(p.nw, max(1, s.W / kMinPieceTiles));
-  return s;
-}
-
-// The live sequence b whose tiles hold tile x, with the tiles (sb) and pairs
-// (pb) before it on the line: lane scans of the per-sequence tiles and live
-// flags, 64 sequences a block, and a ballot (wave-uniform).
-template <class P>
-__device__ void sk_locate(const P& p, int len0, int x, int& b, int& sb, int& pb) {
+__device__ void sk_locate(const P& p, int len0, int key, bool by_pair, int& b, int& sb, int& pb) {
   const int lane = threadIdx.x & 63;
   const int per = p.Hkv * p.RG;
   int base = 0, pbase = 0;
@@ -420,16 +413,42 @@ __device__ void sk_locate(const P& p, int len0, int x, int& b, int& sb, int& pb)
     const int inc = tv::wave_scan_i32(work, lane);
     const int linc = tv::wave_scan_i32(live, lane);
     const int tot = __builtin_amdgcn_readlane(inc, 63);
-    if (x < base + tot) {
-      const int l = __builtin_ctzll(__ballot(base + inc > x));
+    const int ltot = __builtin_amdgcn_readlane(linc, 63);
+    if (by_pair ? key < pbase + per * ltot : key < base + tot) {
+      const int l = __builtin_ctzll(__ballot(by_pair ? pbase + per * linc > key : base + inc > key));
       b = b0 + l;
       sb = base + __builtin_amdgcn_readlane(inc - work, l);
       pb = pbase + per * __builtin_amdgcn_readlane(linc - live, l);
       return;
     }
     base += tot;
-    pbase += per * __builtin_amdgcn_readlane(linc, 63);
+    pbase += per * ltot;
   }
+}
+
+// The shared part of the line (wave-uniform; every lane calls).
+template <class P>
+__device__ SkLine sk_line(const P& p, int len0) {
+  const int per = p.Hkv * p.RG;
+  int w = 0, live = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int L = block_len(p, b0, len0);
+    w += L < 0 ? 0 : per * pair_tiles(L);
+    live += L < 0 ? 0 : 1;
+  }
+  const int total = tv::wave_sum_i32(w);
+  const int pairs = per * tv::wave_sum_i32(live);
+  SkLine s;
+  s.p0 = pairs / p.nw * p.nw;
+  s.off = total;
+  if (s.p0 < pairs) {
+    int b, sb, pb;
+    sk_locate(p, len0, s.p0, true, b, sb, pb);
+    s.off = sb + (s.p0 - pb) * pair_tiles(seq_len(p, b, len0));
+  }
+  s.W = total - s.off;
+  s.nwa = min(p.nw, s.W);
+  return s;
 }
 
 // The pieces of the pair whose tiles start at sp (wp tiles, first pair index
@@ -481,16 +500,18 @@ __device__ bool decode_unit(const P& p, int len0, int K, int u, int& b, int& kvh
   return false;
 }
 
-// Table for the combine kernel. Unit mode: [0] = K, [1] = 0, [2 + 2 b] =
-// first unit of sequence b. Stream-K: [0] = W, [1] = nwa (> 0), [2 + 2 b] =
-// tiles before sequence b on the line, [3 + 2 b] = pairs before it.
+// Table for the combine kernel. Unit mode: [0] = K, [1] = -1, [4 + 2 b] =
+// first unit of sequence b. Stream-K: [0] = W, [1] = nwa, [2] = off, [3] =
+// p0, [4 + 2 b] = line tiles before sequence b, [5 + 2 b] = pairs before it.
 template <class P>
 __device__ void write_sched(const P& p, int len0, int K, const SkLine& s, bool stream_k) {
   const int lane = threadIdx.x & 63;
   const int per = p.Hkv * p.RG;
   if (lane == 0) {
     p.sched[0] = stream_k ? s.W : K;
-    p.sched[1] = stream_k ? s.nwa : 0;
+    p.sched[1] = stream_k ? s.nwa : -1;
+    p.sched[2] = s.off;
+    p.sched[3] = s.p0;
   }
   int base = 0, pbase = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
@@ -500,8 +521,8 @@ __device__ void write_sched(const P& p, int len0, int K, const SkLine& s, bool s
     const int inc = tv::wave_scan_i32(cnt, lane);
     const int linc = tv::wave_scan_i32(live, lane);
     if (b0 + lane < p.B) {
-      p.sched[2 + 2 * (b0 + lane)] = base + inc - cnt;
-      p.sched[3 + 2 * (b0 + lane)] = pbase + per * (linc - live);
+      p.sched[4 + 2 * (b0 + lane)] = base + inc - cnt;
+      p.sched[5 + 2 * (b0 + lane)] = pbase + per * (linc - live);
     }
     base += __builtin_amdgcn_readlane(inc, 63);
     pbase += per * __builtin_amdgcn_readlane(linc, 63);
@@ -528,12 +549,6 @@ struct Piece {
   int slot, base, np, j;
 };
 
-// Committed length of sequence b (live): from the lane cache for b < 64.
-template <class P>
-__device__ __forceinline__ int seq_len(const P& p, int b, int len0) {
-  return b < 64 ? __builtin_amdgcn_readlane(len0, b) : live_len(p, b);
-}
-
 // Unit mode: unit u as a piece; false past the last unit (wave-uniform).
 template <class P>
 __device__ bool unit_piece(const P& p, int len0, int K, int u, Piece& pc) {
@@ -553,15 +568,15 @@ __device__ bool unit_piece(const P& p, int len0, int K, int u, Piece& pc) {
   return true;
 }
 
-// Stream-K: the next non-empty piece of workgroup v's share from tile x on;
-// next_x is the tile after it. False when the share holds no more.
+// Stream-K: the next non-empty piece of workgroup v's share from line tile
+// x on; next_x is the tile after it. False when the share holds no more.
 template <class P>
 __device__ bool sk_piece(const P& p, int len0, const SkLine& s, int v, int x, Piece& pc,
                          int& next_x) {
-  const int e = sk_start(s, v + 1);
+  const int e = s.off + sk_start(s, v + 1);
   while (x < e) {
     int b, sb, pb;
-    sk_locate(p, len0, x, b, sb, pb);
+    sk_locate(p, len0, x, false, b, sb, pb);
     if (b < 0) return false;
     const int L = seq_len(p, b, len0);
     const int wp = pair_tiles(L);
@@ -576,7 +591,7 @@ __device__ bool sk_piece(const P& p, int len0, const SkLine& s, int v, int x, Pi
       x = next_x;
       continue;
     }
-    const SkPair pr = sk_pair(s, sp, wp, pb + q);
+    const SkPair pr = sk_pair(s, sp - s.off, wp, pb + q - s.p0);
     pc.b = b;
     pc.kvh = q / p.RG;
     pc.rg = q - pc.kvh * p.RG;
@@ -593,22 +608,31 @@ __device__ bool sk_piece(const P& p, int len0, const SkLine& s, int v, int x, Pi
 }
 
 // Runs run(piece) for every piece of this workgroup, with a barrier between
-// pieces (the previous piece's LDS reads are done). Stream-K: workgroup
-// blockIdx takes share v = (blockIdx mod 8) c + blockIdx / 8 (c = ceil(nwa /
-// 8)) if v < nwa and blockIdx / 8 < c, so that neighbouring shares (which cut
-// the same pairs) run on one XCD under round-robin dispatch. Unit mode:
-// units first_unit(blockIdx) + k nw.
+// pieces (the previous piece's LDS reads are done). Unit mode: units
+// first_unit(blockIdx) + k nw. Stream-K: the whole pairs first_unit(blockIdx)
+// + k nw below p0, then share v = (blockIdx mod 8) c + blockIdx / 8 (c =
+// ceil(nwa / 8)) if v < nwa and blockIdx / 8 < c, so that neighbouring
+// shares (which cut the same pairs) run on one XCD under round-robin
+// dispatch.
 template <class P, class Run>
 __device__ __forceinline__ void for_each_piece(const P& p, int len0, int K, const SkLine& s,
                                                bool stream_k, Run run) {
   Piece pc;
   bool first = true;
   if (stream_k) {
+    // Whole pairs first (units of one pair each: K fits every pair), then
+    // this workgroup's share of the rest of the line.
+    for (int u = first_unit(p); u < s.p0; u += p.nw) {
+      unit_piece(p, len0, K, u, pc);
+      if (!first) __syncthreads();
+      first = false;
+      run(pc);
+    }
     const int per_xcd = (s.nwa + 7) >> 3;
     const int k = blockIdx.x >> 3;
     const int v = (blockIdx.x & 7) * per_xcd + k;
     if (k >= per_xcd || v >= s.nwa) return;
-    int x = sk_start(s, v), nx;
+    int x = s.off + sk_start(s, v), nx;
     while (sk_piece(p, len0, s, v, x, pc, nx)) {
       if (!first) __syncthreads();
       first = false;
@@ -768,7 +792,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
   const int K = choose_unit(p, len0);
   const bool stream_k =
       p.kunit == 0 && p.part_o != nullptr && total_units(p, len0, K) > p.nw;
-  SkLine sk{0, 0};
+  SkLine sk{0, 0, 0, 0};
   if (stream_k) sk = sk_line(p, len0);
   if (p.sched && blockIdx.x == 0 && wave == 0) write_sched(p, len0, K, sk, stream_k);
 
@@ -1253,7 +1277,7 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParamsT
   const int K = choose_unit(p, len0);
   const bool stream_k =
       p.kunit == 0 && p.part_o != nullptr && total_units(p, len0, K) > p.nw;
-  SkLine sk{0, 0};
+  SkLine sk{0, 0, 0, 0};
   if (stream_k) sk = sk_line(p, len0);
   if (p.sched && blockIdx.x == 0 && tid < tv::kWave) write_sched(p, len0, K, sk, stream_k);
 
@@ -1432,13 +1456,16 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   const int L = p.ctx_len[b];
   const int t0 = p.sched[0];
   const int t1 = p.sched[1];
-  const int t2 = p.sched[2 + 2 * b];
-  const int t3 = p.sched[3 + 2 * b];
+  const int t_off = p.sched[2];
+  const int t_p0 = p.sched[3];
+  const int t2 = p.sched[4 + 2 * b];
+  const int t3 = p.sched[5 + 2 * b];
   const int start = PACKED ? p.row_start[b] : 0;
   // Keeps the loads ahead of the branches below (the compiler would
   // otherwise sink each one into the branch that first needs it and wait
   // for them one by one).
-  asm volatile("" ::"s"(n), "s"(L), "s"(t0), "s"(t1), "s"(t2), "s"(t3), "s"(start));
+  asm volatile("" ::"s"(n), "s"(L), "s"(t0), "s"(t1), "s"(t_off), "s"(t_p0), "s"(t2), "s"(t3),
+               "s"(start));
   if (r >= p.R) return;
   if (seq_status(p, n, L, start) != TV_ROW_OK) return;  // padded / invalid: done by the split
   const int rg = r / p.rows_wg;
@@ -1447,13 +1474,17 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   // The pair's pieces: first slot u0, count nch; pieces jt .. nch - 2 hold
   // no keys (stream-K only) and are skipped.
   int nch, u0, jt;
-  if (t1 == 0) {  // unit mode: K = t0, first unit of the sequence = t2
+  if (t1 < 0) {  // unit mode: K = t0, first unit of the sequence = t2
     nch = pair_units(p, L, t0);
     u0 = t2 + q * nch;
     jt = nch;
-  } else {  // stream-K: W = t0, nwa = t1, tiles and pairs before the sequence = t2, t3
+  } else if (t3 + q < t_p0) {  // stream-K, a whole-pair unit
+    nch = 1;
+    u0 = jt = 0;
+  } else {  // stream-K, shared part: line tiles and pairs before the sequence = t2, t3
     const int wp = pair_tiles(L);
-    const SkPair pr = sk_pair(SkLine{t0, t1}, t2 + q * wp, wp, t3 + q);
+    const SkPair pr =
+        sk_pair(SkLine{t0, t1, t_off, t_p0}, t2 + q * wp - t_off, wp, t3 + q - t_p0);
     nch = pr.np;
     u0 = pr.base;
     jt = pr.jt;
@@ -1595,16 +1626,26 @@ int64_t line_tiles(int B, int T, int Hq, int Hkv, int max_ctx, int rows_wg) {
   return pairs * ((static_cast<int64_t>(max_ctx) + kKB - 1) / kKB + kTreeTiles);
 }
 
-// Keys per active workgroup of the balanced (stream-K) partition when every
-// sequence is live with max_ctx committed keys (bf16 row groups), rounded up
-// to whole tiles: a fixed chunk_keys of about that size cuts the same
-// number of units.
+// The unit size the device picks when every sequence is live with max_ctx
+// committed keys (bf16 row groups): the smallest multiple of 64, at least
+// kMinUnit, that gives at most one unit per workgroup.
 int auto_chunk(int B, int T, int Hq, int Hkv, int max_ctx) {
-  const int64_t W = line_tiles(B, T, Hq, Hkv, max_ctx, kRowsWG);
-  if (W == 0) return kMinUnit;
-  const int64_t nwa =
-      std::min<int64_t>(grid_workgroups(), std::max<int64_t>(1, W / kMinPieceTiles));
-  return static_cast<int>(std::min<int64_t>((W + nwa - 1) / nwa * kKB, 1 << 30));
+  const int64_t R = static_cast<int64_t>(Hq / Hkv) * T;
+  const int64_t pairs = static_cast<int64_t>(B) * Hkv * ((R + kRowsWG - 1) / kRowsWG);
+  const int64_t nw = grid_workgroups();
+  auto units = [&](int K) { return pairs * host_chunks(max_ctx, K); };
+  int lo = kMinUnit;
+  int hi = std::max(kMinUnit, (max_ctx + 63) / 64 * 64);
+  if (units(lo) <= nw) return lo;
+  if (units(hi) > nw) return hi;
+  while (hi - lo > 64) {
+    const int mid = (lo / 64 + hi / 64) / 2 * 64;
+    if (units(mid) <= nw)
+      hi = mid;
+    else
+      lo = mid;
+  }
+  return hi;
 }
 
 bool valid_sizes(int B, int T, int Hq, int Hkv, int D, int max_ctx, int chunk_keys) {
@@ -1615,7 +1656,7 @@ bool valid_sizes(int B, int T, int Hq, int Hkv, int D, int max_ctx, int chunk_ke
   return true;
 }
 
-// Workspace layout: the schedule table ((2 + 2 B) int32), then partial O
+// Workspace layout: the schedule table ((4 + 2 B) int32), then partial O
 // [slot][rows_wg][D] (fp32, or int16 fixed point in the same space, each
 // row in the split lanes' order), then (m, l, scale, 0) per pair as
 // [rows_wg][piece of the pair] from the pair's first slot. Fixed chunks use
@@ -1646,7 +1687,7 @@ WsLayout workspace_layout(int B, int T, int Hq, int Hkv, int D, int max_ctx, int
   }
   if (rows_max == 0) return w;
   w.sched = 0;
-  w.part_o = tvh::align_up(static_cast<size_t>(2 + 2 * static_cast<int64_t>(B)) * sizeof(int32_t), 256);
+  w.part_o = tvh::align_up(static_cast<size_t>(4 + 2 * static_cast<int64_t>(B)) * sizeof(int32_t), 256);
   w.part_ml = w.part_o + tvh::align_up(static_cast<size_t>(rows_max) * D * sizeof(float), 256);
   w.total = w.part_ml + tvh::align_up(static_cast<size_t>(rows_max) * sizeof(float4), 256);
   return w;
