@@ -565,6 +565,25 @@ def test_linear_rows_batch_invariant():
                           full)
 
 
+def test_linear_batch_invariant_across_tilings():
+    # N = 18944 (1184 tiles of 16 features): 193..272 rows run the kernel that
+    # keeps every row in each workgroup, fewer rows the 96-row groups; the
+    # bits of a row do not change between them (same MFMA chains, k in order).
+    rng = np.random.default_rng(9)
+    M, K, N = 264, 512, 18944
+    x, _ = _bf16_dev(rng.normal(size=(M, K)))
+    wg, _ = _bf16_dev(rng.normal(size=(N, K)) / np.sqrt(K))
+    wu, _ = _bf16_dev(rng.normal(size=(N, K)) / np.sqrt(K))
+    full_l = tv.linear_rows(x, wg).cpu().view(torch.int16).numpy()
+    full_s = tv.linear_swiglu_rows(x, wg, wu).cpu().view(torch.int16).numpy()
+    for lo, hi in ((0, 1), (0, 192), (40, 233), (70, 264), (263, 264)):
+        xs = x[lo:hi].contiguous()
+        assert np.array_equal(tv.linear_rows(xs, wg).cpu().view(torch.int16).numpy(),
+                              full_l[lo:hi]), (lo, hi)
+        assert np.array_equal(tv.linear_swiglu_rows(xs, wg, wu).cpu().view(torch.int16).numpy(),
+                              full_s[lo:hi]), (lo, hi)
+
+
 @pytest.mark.parametrize("M,K,N", [(9, 64, 64), (100, 448, 320), (264, 3584, 1024),
                                    (264, 3584, 18944)])
 def test_linear_swiglu_rows(M, K, N):

@@ -1600,21 +1600,8 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
   if (sub == 0) p.lse[orow] = lstar > 0.f ? (mstar + __log2f(lstar)) * kLn2 : -INFINITY;
 }
 
-// Workgroups per launch: one per compute unit (a multiple of 8), cached per
-// device. 256 (MI355X) if the device cannot be queried.
-int grid_workgroups() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int cu = 0;
-    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cu < 8)
-      cu = 256;
-    cache[dev] = cu / 8 * 8;
-  }
-  return cache[dev];
-}
+// Workgroups per launch: one per compute unit (a multiple of 8).
+int grid_workgroups() { return tvh::grid_workgroups(); }
 
 int host_chunks(int64_t L, int64_t K) { return L == 0 ? 1 : static_cast<int>((L + K - 1) / K); }
 

@@ -117,6 +117,22 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Compute units of the current device rounded down to a multiple of 8 (the
+// XCDs of a gfx950), cached per device; 256 (MI355X) if it cannot be queried.
+inline int grid_workgroups() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cu < 8)
+      cu = 256;
+    cache[dev] = cu / 8 * 8;
+  }
+  return cache[dev];
+}
+
 inline int launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? TV_OK : TV_ERR_HIP;

@@ -221,6 +221,203 @@ __global__ __launch_bounds__(64 * WAVES) void linear_rows_kernel(LinParams p) {
   }
 }
 
+// ---- All rows per workgroup (gate/up: large N, M up to 272) ----
+// The batch's rows and the weight rows of the workgroup's feature tiles both
+// go through LDS, in chunks of 32 k, and are shared by the eight waves: wave
+// w owns row tiles w and w + 8 (rows 16 w .. and 16 (w + 8) ..) for every
+// feature tile of the workgroup and, with a 17th row tile, the products of
+// that tile with feature tile w. Each workgroup takes a contiguous run of
+// ceil or floor N / (16 nwg) feature tiles (at most FTMAX), so a single pass
+// of one workgroup per compute unit covers N, and each weight byte crosses
+// from L2 to the compute units once (the 96-row groups above stream every
+// weight slice through three of them, in two passes). The input rows,
+// re-read by every workgroup, stay in L2. Same MFMA operands and k order as
+// linear_rows_kernel, so every output has the same bits.
+constexpr int kAllRowTiles = 17;              // rows per workgroup: up to 272
+constexpr int kAllRows = 16 * kAllRowTiles;
+constexpr int kAllThreads = 512;
+constexpr int kAllStages = 4;                 // register stages (chunks of 32 k)
+
+struct LinAllParams {
+  const uint16_t* x;
+  const uint16_t* w0;
+  const uint16_t* w1;
+  int64_t x_stride, w_stride, y_stride;
+  int M, K, ntiles, nwg;
+  uint16_t* y;
+};
+
+// 16-byte piece c (k-group of 8) of LDS row r of a 32-k chunk (4 pieces per
+// 64-byte row, XOR-swizzled by (r / 2) mod 4): the eight consecutive rows
+// that one phase of an MFMA operand read touches (eight lanes, 16 bytes
+// each) land on eight different 16-byte slots modulo 128 bytes, so the read
+// is free of bank conflicts (with r / 4 instead, rows r and r + 2 collided).
+__device__ __forceinline__ int all_slot(int r, int c) { return r * 4 + (c ^ ((r >> 1) & 3)); }
+
+template <bool SWIGLU, int FTMAX, int NST>
+__global__ __launch_bounds__(kAllThreads) void linear_allrows_kernel(LinAllParams p) {
+  constexpr int NMAT = SWIGLU ? 2 : 1;
+  constexpr int WROWS = 16 * FTMAX * NMAT;                          // weight rows per chunk
+  constexpr int XPIECES = kAllRows * 4;                             // 16-byte pieces per chunk
+  constexpr int WPIECES = WROWS * 4;
+  constexpr int XL = (XPIECES + kAllThreads - 1) / kAllThreads;     // per thread
+  constexpr int WL = (WPIECES + kAllThreads - 1) / kAllThreads;
+  __shared__ __attribute__((aligned(16))) u16x8_t sX[2][XPIECES + 1];
+  __shared__ __attribute__((aligned(16))) u16x8_t sW[2][WPIECES + 1];
+  const int g = blockIdx.x;
+  if (g >= p.nwg) return;
+  const int ft0 = static_cast<int>(static_cast<int64_t>(g) * p.ntiles / p.nwg);
+  const int ft1 = static_cast<int>(static_cast<int64_t>(g + 1) * p.ntiles / p.nwg);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // Wave-uniform (a scalar register): the extra products below are skipped
+  // by a scalar branch; an MFMA does not honour the EXEC mask, so a per-lane
+  // condition around it would not skip it.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i16 = lane & 15;
+  const int kg = lane >> 4;
+  const int nchunks = p.K / 32;
+
+  // Staging: thread t copies pieces t, t + 512, ... (row = s / 4, piece =
+  // s % 4). Input rows past M re-read row M - 1; weight rows past the
+  // workgroup's tiles re-read its last row (their products are not stored);
+  // threads past the last piece re-read it into the spare slot.
+  // Element offsets below 2^31 (the host checks), from uniform bases.
+  int xoff[XL], xslot[XL];
+#pragma unroll
+  for (int j = 0; j < XL; ++j) {
+    const int sraw = tid + kAllThreads * j;
+    const int sidx = min(sraw, XPIECES - 1);
+    const int row = sidx >> 2, c = sidx & 3;
+    xoff[j] = min(row, p.M - 1) * static_cast<int>(p.x_stride) + 8 * c;
+    xslot[j] = sraw >= XPIECES ? XPIECES : all_slot(row, c);
+  }
+  int woff[WL], wslot[WL];
+  bool wup[WL];
+  const int nfeat = 16 * (ft1 - ft0);
+  const uint16_t* wbase0 = p.w0 + static_cast<int64_t>(16 * ft0) * p.w_stride;
+  const uint16_t* wbase1 = SWIGLU ? p.w1 + static_cast<int64_t>(16 * ft0) * p.w_stride : nullptr;
+#pragma unroll
+  for (int j = 0; j < WL; ++j) {
+    const int sraw = tid + kAllThreads * j;
+    const int sidx = min(sraw, WPIECES - 1);
+    const int row = sidx >> 2, c = sidx & 3;  // row = mat * 16 FTMAX + feature
+    const int mat = row / (16 * FTMAX);
+    const int f = min(row - mat * 16 * FTMAX, nfeat - 1);
+    woff[j] = f * static_cast<int>(p.w_stride) + 8 * c;
+    wup[j] = SWIGLU && mat;
+    wslot[j] = sraw >= WPIECES ? WPIECES : all_slot(row, c);
+  }
+
+  struct Stage {
+    u16x8_t x[XL];
+    u16x8_t w[WL];
+  };
+  auto load_chunk = [&](Stage& st, int c) __attribute__((always_inline)) {
+    const int k0 = 32 * c;
+#pragma unroll
+    for (int j = 0; j < XL; ++j) st.x[j] = *reinterpret_cast<const u16x8_t*>(p.x + xoff[j] + k0);
+#pragma unroll
+    for (int j = 0; j < WL; ++j)
+      st.w[j] = *reinterpret_cast<const u16x8_t*>((wup[j] ? wbase1 : wbase0) + woff[j] + k0);
+  };
+  auto store_chunk = [&](const Stage& st, int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < XL; ++j) sX[stage][xslot[j]] = st.x[j];
+#pragma unroll
+    for (int j = 0; j < WL; ++j) sW[stage][wslot[j]] = st.w[j];
+  };
+
+  // Accumulators: [row tile w, w + 8][feature tile][matrix], and the extra
+  // (row tile 16, feature tile = wave) pair.
+  f32x4_t acc[2][FTMAX][NMAT], ext[NMAT];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int f = 0; f < FTMAX; ++f)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) acc[a][f][m] = f32x4_t(0.f);
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) ext[m] = f32x4_t(0.f);
+  const bool has_ext = wave < FTMAX;
+  auto compute = [&](int stage) __attribute__((always_inline)) {
+    bf16x8_t xf[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      const int rt = a < 2 ? wave + 8 * a : 16;
+      xf[a] = __builtin_bit_cast(bf16x8_t, sX[stage][all_slot(16 * rt + i16, kg)]);
+    }
+#pragma unroll
+    for (int f = 0; f < FTMAX; ++f) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const bf16x8_t wf = __builtin_bit_cast(
+            bf16x8_t, sW[stage][all_slot(m * 16 * FTMAX + 16 * f + i16, kg)]);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+          acc[a][f][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[a], acc[a][f][m], 0, 0, 0);
+        if (f == wave)
+          ext[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[2], ext[m], 0, 0, 0);
+      }
+    }
+  };
+
+  // Chunk c lives in register stage c % NST and LDS stage c % 2 (see
+  // linear_rows_kernel: loads run NST - 1 chunks ahead, no branch around
+  // them, the last chunk re-read past the end).
+  Stage r[NST];
+#pragma unroll
+  for (int j = 0; j < NST - 1; ++j) load_chunk(r[j], min(j, nchunks - 1));
+  store_chunk(r[0], 0);
+  __syncthreads();
+  int c = 0;
+  for (; c + NST <= nchunks; c += NST) {
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      load_chunk(r[(j + NST - 1) % NST], min(c + j + NST - 1, nchunks - 1));
+      store_chunk(r[(j + 1) % NST], ((j + 1) & 1) ^ (c & 1));
+      compute((j & 1) ^ (c & 1));
+      lds_barrier();
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NST - 1; ++j) {
+    if (c + j < nchunks) {
+      if (c + j + NST - 1 < nchunks) load_chunk(r[(j + NST - 1) % NST], c + j + NST - 1);
+      if (c + j + 1 < nchunks) store_chunk(r[(j + 1) % NST], ((j + 1) & 1) ^ (c & 1));
+      compute((j & 1) ^ (c & 1));
+      lds_barrier();
+    }
+  }
+
+  // Lane holds output features 4 kg + e (e = 0..3) of a feature tile for row
+  // i16 of a row tile.
+  auto store_tile = [&](const f32x4_t* a, int rt, int f) __attribute__((always_inline)) {
+    const int m = 16 * rt + i16;
+    if (m >= p.M || ft0 + f >= ft1) return;
+    uint32_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v;
+      if constexpr (SWIGLU) {
+        const float gr = tv::bf16_to_f32(tv::f32_to_bf16_rne(a[0][e]));
+        const float ur = tv::bf16_to_f32(tv::f32_to_bf16_rne(a[1][e]));
+        v = silu(gr) * ur;
+      } else {
+        v = a[0][e];
+      }
+      h[e] = tv::f32_to_bf16_rne(v);
+    }
+    *reinterpret_cast<uint2*>(p.y + static_cast<int64_t>(m) * p.y_stride + 16 * (ft0 + f) + 4 * kg) =
+        make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  };
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int f = 0; f < FTMAX; ++f) store_tile(acc[a][f], wave + 8 * a, f);
+  if (has_ext) store_tile(ext, 16, wave);
+}
+
 int launch_linear(const void* x, int64_t x_stride, const void* w0, const void* w1,
                   int64_t w_stride, int M, int K, int N, void* y, int64_t y_stride,
                   bool swiglu, hipStream_t stream) {
@@ -254,6 +451,40 @@ int launch_linear(const void* x, int64_t x_stride, const void* w0, const void* w
     return TV_OK;
   };
   int rc;
+  // All rows per workgroup when they are many (193..272) and N gives every
+  // workgroup of one pass 4 or 5 feature tiles.
+  const int ntiles = N / 16;
+  const int nw = tvh::grid_workgroups();
+  const int ftmax = (ntiles + nw - 1) / nw;
+  if (M > 192 && M <= kAllRows && (ftmax == 4 || ftmax == 5) &&
+      static_cast<int64_t>(M) * x_stride < INT32_MAX &&
+      static_cast<int64_t>(16 * ftmax) * w_stride < INT32_MAX) {
+    LinAllParams a;
+    a.x = p.x;
+    a.w0 = p.w0;
+    a.w1 = p.w1;
+    a.x_stride = x_stride;
+    a.w_stride = w_stride;
+    a.y_stride = y_stride;
+    a.M = M;
+    a.K = K;
+    a.ntiles = ntiles;
+    a.nwg = (ntiles + ftmax - 1) / ftmax;
+    a.y = p.y;
+    const dim3 grid(a.nwg), block(kAllThreads);
+    if (swiglu) {
+      if (ftmax == 5)
+        hipLaunchKernelGGL((linear_allrows_kernel<true, 5, kAllStages>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((linear_allrows_kernel<true, 4, kAllStages>), grid, block, 0, stream, a);
+    } else {
+      if (ftmax == 5)
+        hipLaunchKernelGGL((linear_allrows_kernel<false, 5, kAllStages>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((linear_allrows_kernel<false, 4, kAllStages>), grid, block, 0, stream, a);
+    }
+    return tvh::launch_status();
+  }
   if (!swiglu)
     rc = launch(linear_rows_kernel<false, 6, 64, kRows, 4>, kRows, 4);
   else if (K % kDeepKC == 0 && N % (16 * kWavesWide) == 0)
