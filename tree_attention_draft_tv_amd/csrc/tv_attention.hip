@@ -687,9 +687,9 @@ __device__ __forceinline__ int v_swz(int key) {
 // of the tiles still in flight; the ring's explicit TV_WAIT_VMCNT waits
 // already guarantee that the tile about to be read has landed.
 // A 16-byte store at device scope (sc1): written through the XCD's L2 to
-// memory instead of staying dirty there. Used for the split-KV partials,
-// which only the combine reads: the end of the split kernel then has no L2
-// write-back of ~30 MB to wait for (-2 us per call at C3). The compiler does
+// memory instead of staying dirty there. Used for the fp32 split-KV
+// partials, which only the combine reads: the end of the split kernel then
+// has no L2 write-back of ~30 MB to wait for (-2 us per call at C3). The compiler does
 // not see the store inside the asm, so the asm itself supplies the wait
 // states that a VALU write to the data registers of a preceding store of
 // more than 8 bytes needs (2 on gfx950; s_nop 2 gives 3): the registers are
@@ -1235,9 +1235,11 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
         for (int dp = 0; dp < DT / 2; ++dp) {
           const f32x4_t v0 = o[2 * dp][rt];
           const f32x4_t v1 = o[2 * dp + 1][rt];
-          typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-          store_wt16(dst + 8 * dp, u32x4_t{pack2(v0[0], v0[1]), pack2(v0[2], v0[3]),
-                                           pack2(v1[0], v1[1]), pack2(v1[2], v1[3])});
+          // Plain stores here: written through at device scope, these
+          // 16-byte pieces of a half-size row doubled the counted writes.
+          *reinterpret_cast<uint4*>(dst + 8 * dp) =
+              make_uint4(pack2(v0[0], v0[1]), pack2(v0[2], v0[3]), pack2(v1[0], v1[1]),
+                         pack2(v1[2], v1[3]));
         }
       } else {
         float* dst = p.part_o + prow * D;
