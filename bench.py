@@ -10,10 +10,11 @@ loop rotates over several copies of the inputs so that the 256 MB Infinity
 Cache cannot serve a step from the previous one (cold timing).
 
 Prints one JSON line. ``value`` is verified draft nodes per second for the
-whole step; ``roofline`` reports the attention call's algorithmic HBM
-bandwidth against the 8 TB/s peak, from HIP events recorded on the stream
-the kernels run on; ``cpu_baseline`` times the float64 oracle on a bounded
-sample of the same workload on the host.
+whole step; ``roofline`` reports the attention call against whichever of
+its two bounds binds (matrix-core flops at 2.5 PFLOP/s, or algorithmic HBM
+bytes at 8 TB/s), from HIP events recorded on the stream the kernels run
+on; ``cpu_baseline`` times the float64 oracle on a bounded sample of the
+same workload on the host.
 """
 
 import argparse
@@ -45,7 +46,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200,
-                    help="timed steps (a step is ~75 us: fewer leave the wall clock to jitter)")
+                    help="timed steps (a step is ~85 us: fewer leave the wall clock to jitter)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="C3", help="workload (C1..C5); C3 is the headline")
     ap.add_argument("--sets", type=int, default=0,
