@@ -157,8 +157,8 @@ def test_budget_validation(lib):
 def test_attention_workspace_size(lib):
     f = lib.tv_tree_attention_workspace_size
     assert f(8, 33, 28, 4, 128, 256, 256) == 0          # one chunk: no workspace
-    assert f(1, 9, 8, 2, 64, 128, 0) == 0             # every pair one unit: no workspace
-    assert f(1, 9, 8, 2, 64, 256, 0) > 0              # balanced units may split a pair
+    assert f(1, 9, 8, 2, 64, 0, 0) == 0               # every pair one unit: no workspace
+    assert f(1, 9, 8, 2, 64, 128, 0) > 0              # balanced units may split a pair
     big = f(8, 33, 28, 4, 128, 7650, 512)
     rows = 8 * 4 * 15 * 231
     assert big >= rows * (128 * 4 + 8)

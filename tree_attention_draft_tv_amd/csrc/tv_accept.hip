@@ -154,7 +154,7 @@ __device__ int validate_seq(const int32_t* parent, const int32_t* tokens, int n,
   if (tid == 0) *s_flags = 0;
   __syncthreads();
   if (n < 0 || n > T) return TV_ROW_NNODES;
-  for (int i = tid; i < n; i += blockDim.x) {
+  for (int i = tid; i < n; i += kWalkThreads) {  // the walk's workgroup size
     if (i == 0) continue;
     const int p = parent[static_cast<int64_t>(b) * T + i];
     if (p < 0 || p >= i) atomicOr(s_flags, 1);
@@ -986,13 +986,12 @@ __global__ __launch_bounds__(kWalkThreads) void sample_node_kernel(
   float m0 = -INFINITY;
 #pragma nounroll
   for (int round = 0; round < 2; ++round) {
-    // The row in two halves: the second half's loads are issued once the
-    // first half has landed, so that its transfer overlaps the first
-    // half's terms.
+    // The whole row is requested at once; the reference and the first
+    // half's terms wait only for the first half (loads into registers
+    // complete in issue order), so the second half's transfer overlaps them.
     float lv[kRegSlots];
-    load_blocks<0, kRegSlots / 2>(lrow, V, lv);
-    TV_ACCEPT_WAIT_VMCNT0();
-    load_blocks<kRegSlots / 2, kRegSlots>(lrow, V, lv);
+    load_blocks<0, kRegSlots>(lrow, V, lv);
+    TV_ACCEPT_WAIT_VMCNT(kRegSlots / 2);
     float mr = slot_entry(tid, 0) < V ? lv[0] : -INFINITY;
     if (round == 1)  // the row maximum (a separate pass over the row)
       for (int v = tid; v < V; v += kWalkThreads) mr = fmaxf(mr, lrow[v]);

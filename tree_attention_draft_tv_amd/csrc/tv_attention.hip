@@ -177,12 +177,14 @@ __device__ __forceinline__ int seq_check(const P& p, int b, int& n, int& L, int&
 // n and its start are valid (a bounds error writes nothing). st0 holds the statuses of the first 64 sequences (lane b:
 // sequence b); later blocks of 64 are read in one round before their stores
 // (a load placed after the stores would wait for them: the compiler cannot
-// rule out that they alias the length arrays).
-template <int D, class P>
+// rule out that they alias the length arrays). THREADS is the workgroup
+// size and the grid is p.nw workgroups (reading blockDim would cost a memory
+// round trip at the start of every workgroup).
+template <int D, int THREADS, class P>
 __device__ void finish_non_live(const P& p, int st0, int n0, int s0) {
   constexpr int D4 = D / 4;
-  const int nthreads = gridDim.x * blockDim.x;
-  const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int nthreads = p.nw * THREADS;
+  const int gtid = blockIdx.x * THREADS + threadIdx.x;
   const int lane = threadIdx.x & 63;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     const bool has = b0 + lane < p.B;
@@ -230,7 +232,7 @@ __device__ void finish_non_live(const P& p, int st0, int n0, int s0) {
 // sync, no communication between workgroups); the combine kernel reads the
 // table workgroup 0 writes.
 
-constexpr int kMinUnit = 256;  // smallest balanced unit (keys)
+constexpr int kMinUnit = 128;  // smallest balanced unit (keys)
 
 // Committed length of sequence b if it is live, else -1.
 template <class P>
@@ -280,25 +282,27 @@ __device__ __forceinline__ int block_len(const P& p, int b0, int len0) {
 }
 // Balanced units: the tree block (masked, unpipelined) costs about as much as
 // this many committed keys, so the last unit of a pair, which holds it, gets
-// that many fewer committed keys.
+// that many fewer committed keys (half a unit at most: tree_extra(K)).
 constexpr int kTreeExtra = 128;
+__device__ __forceinline__ int tree_extra(int K) { return min(kTreeExtra, K >> 1); }
 
 // Units of a pair with L committed keys and K keys per unit.
 __device__ __forceinline__ int pair_units(const AttnParams& p, int L, int K) {
-  const int x = p.kunit > 0 ? 0 : kTreeExtra;
+  const int x = p.kunit > 0 ? 0 : tree_extra(K);
   return L == 0 ? 1 : div_fast(L + x + K - 1, K);
 }
 // First committed key of unit c of a pair: c K for fixed chunks; in balanced
-// mode the units split L + kTreeExtra evenly, boundaries rounded down to
-// whole 64-key tiles. Since K >= 2 kTreeExtra, the last unit keeps at least
-// one committed key and every unit at most K + 63 keys.
+// mode the units split L + x evenly (x = tree_extra(K)), boundaries rounded
+// down to whole 64-key tiles. Since K >= 2 x, the last unit keeps at least
+// one committed key (no boundary passes L) and every unit at most K + 63 keys.
 __device__ __forceinline__ int unit_start(const AttnParams& p, int L, int K, int nch, int c) {
   if (p.kunit > 0) return min(c * K, L);
+  const int x = tree_extra(K);
   // c <= nch <= 1024 units per pair, so below 2^22 the product fits 32 bits.
   if (L < (1 << 22) - kTreeExtra)
-    return static_cast<int>(static_cast<uint32_t>(c) * static_cast<uint32_t>(L + kTreeExtra) /
+    return static_cast<int>(static_cast<uint32_t>(c) * static_cast<uint32_t>(L + x) /
                             static_cast<uint32_t>(nch)) & ~63;
-  return static_cast<int>(static_cast<int64_t>(c) * (L + kTreeExtra) / nch) & ~63;
+  return static_cast<int>(static_cast<int64_t>(c) * (L + x) / nch) & ~63;
 }
 
 __device__ __forceinline__ int units_of(const AttnParams& p, int L, int K) {
@@ -1256,7 +1260,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
   };
 
   // Padding outputs first: their stores drain while the first tiles load.
-  finish_non_live<D>(p, st0, n0, s0);
+  finish_non_live<D, kThreads>(p, st0, n0, s0);
   for_each_piece(p, len0, K, sk, stream_k, run_unit);
 }
 
@@ -1387,7 +1391,7 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParamsT
   };
 
   // Padding outputs first: their stores drain while the first tiles load.
-  finish_non_live<D>(p, st0, n0, s0);
+  finish_non_live<D, kThreadsF32>(p, st0, n0, s0);
   for_each_piece(p, len0, K, sk, stream_k, run_unit);
 }
 
@@ -1622,9 +1626,14 @@ int auto_chunk(int B, int T, int Hq, int Hkv, int max_ctx) {
   const int64_t R = static_cast<int64_t>(Hq / Hkv) * T;
   const int64_t pairs = static_cast<int64_t>(B) * Hkv * ((R + kRowsWG - 1) / kRowsWG);
   const int64_t nw = grid_workgroups();
-  auto units = [&](int K) { return pairs * host_chunks(max_ctx, K); };
+  // Units per pair as the device counts them: the tree block weighs
+  // min(kTreeExtra, K / 2) committed keys.
+  auto units = [&](int K) {
+    return max_ctx == 0 ? pairs
+                        : pairs * ((max_ctx + std::min(kTreeExtra, K / 2) + K - 1) / K);
+  };
   int lo = kMinUnit;
-  int hi = std::max(kMinUnit, (max_ctx + 63) / 64 * 64);
+  int hi = std::max(kMinUnit, (max_ctx + kTreeExtra + 63) / 64 * 64);
   if (units(lo) <= nw) return lo;
   if (units(hi) > nw) return hi;
   while (hi - lo > 64) {
