@@ -153,6 +153,15 @@ __device__ __forceinline__ int div_fast(int a, int b) {
   q += static_cast<int>(r >= b) - static_cast<int>(r < 0);
   return q;
 }
+// a / b for 0 <= a < 2^52, 1 <= b < 2^31 (exact): the correctly rounded
+// double quotient is within 1 of the true one; one correction step. (A
+// 64-bit integer division is a long instruction sequence.)
+__device__ __forceinline__ int64_t div64_fast(int64_t a, int64_t b) {
+  int64_t q = static_cast<int64_t>(static_cast<double>(a) / static_cast<double>(b));
+  const int64_t r = a - q * b;
+  q += static_cast<int64_t>(r >= b) - static_cast<int64_t>(r < 0);
+  return q;
+}
 
 // Packed row r -> tree row r / G with the host's multiplier ceil(2^16 / G):
 // exact for r < 2048 and G <= 32, which TV_MAX_TREE * TV_MAX_GROUP keeps.
@@ -302,7 +311,7 @@ __device__ __forceinline__ int unit_start(const AttnParams& p, int L, int K, int
   if (L < (1 << 22) - kTreeExtra)
     return static_cast<int>(static_cast<uint32_t>(c) * static_cast<uint32_t>(L + x) /
                             static_cast<uint32_t>(nch)) & ~63;
-  return static_cast<int>(static_cast<int64_t>(c) * (L + x) / nch) & ~63;
+  return static_cast<int>(div64_fast(static_cast<int64_t>(c) * (L + x), nch)) & ~63;
 }
 
 __device__ __forceinline__ int units_of(const AttnParams& p, int L, int K) {
@@ -347,7 +356,7 @@ __device__ int choose_unit(const P& p, int len0) {
   // units; rounding each pair up adds at most one unit per pair, so a few
   // steps of 64 usually reach the answer.
   const int64_t pair_keys = static_cast<int64_t>(keys) * p.Hkv * p.RG;
-  int lo = static_cast<int>((pair_keys + p.nw - 1) / p.nw);
+  int lo = static_cast<int>(div64_fast(pair_keys + p.nw - 1, p.nw));
   lo = max(kMinUnit, (lo + 63) / 64 * 64);
   if (lo >= hi) return hi;
   // Each candidate's unit count is one wave reduction over the sequences'
@@ -391,13 +400,13 @@ struct SkLine {
 __device__ __forceinline__ int pair_tiles(int L) { return (L + kKB - 1) / kKB + kTreeTiles; }
 
 __device__ __forceinline__ int sk_start(const SkLine& s, int v) {
-  return v >= s.nwa ? s.W : static_cast<int>(static_cast<int64_t>(v) * s.W / s.nwa);
+  return v >= s.nwa ? s.W : static_cast<int>(div64_fast(static_cast<int64_t>(v) * s.W, s.nwa));
 }
 
 // The workgroup whose share holds tile x of the shared part (0 <= x < W):
 // the largest v with sk_start(v) <= x.
 __device__ __forceinline__ int sk_owner(const SkLine& s, int x) {
-  return static_cast<int>((static_cast<int64_t>(x + 1) * s.nwa - 1) / s.W);
+  return static_cast<int>(div64_fast(static_cast<int64_t>(x + 1) * s.nwa - 1, s.W));
 }
 
 // The live sequence b whose tiles hold line tile `key` (by_pair: whose
@@ -443,7 +452,7 @@ __device__ SkLine sk_line(const P& p, int len0) {
   const int total = tv::wave_sum_i32(w);
   const int pairs = per * tv::wave_sum_i32(live);
   SkLine s;
-  s.p0 = pairs / p.nw * p.nw;
+  s.p0 = div_fast(pairs, p.nw) * p.nw;
   s.off = total;
   if (s.p0 < pairs) {
     int b, sb, pb;
@@ -490,12 +499,12 @@ __device__ bool decode_unit(const P& p, int len0, int K, int u, int& b, int& kvh
       const int l = __builtin_ctzll(hit);
       b = b0 + l;
       const int cnt_l = __builtin_amdgcn_readlane(cnt, l);
-      const int per_pair = cnt_l / (p.Hkv * p.RG);
+      const int per_pair = div_fast(cnt_l, p.Hkv * p.RG);
       const int local = u - base - (__builtin_amdgcn_readlane(inc, l) - cnt_l);
       nch = per_pair;
-      const int pair = local / per_pair;
+      const int pair = div_fast(local, per_pair);
       c = local - pair * per_pair;
-      kvh = pair / p.RG;
+      kvh = div_fast(pair, p.RG);
       rg = pair - kvh * p.RG;
       return true;
     }
@@ -584,7 +593,7 @@ __device__ bool sk_piece(const P& p, int len0, const SkLine& s, int v, int x, Pi
     if (b < 0) return false;
     const int L = seq_len(p, b, len0);
     const int wp = pair_tiles(L);
-    const int q = (x - sb) / wp;
+    const int q = div_fast(x - sb, wp);
     const int sp = sb + q * wp;
     const int x1 = min(e - sp, wp);
     next_x = sp + x1;
@@ -597,7 +606,7 @@ __device__ bool sk_piece(const P& p, int len0, const SkLine& s, int v, int x, Pi
     }
     const SkPair pr = sk_pair(s, sp - s.off, wp, pb + q - s.p0);
     pc.b = b;
-    pc.kvh = q / p.RG;
+    pc.kvh = div_fast(q, p.RG);
     pc.rg = q - pc.kvh * p.RG;
     pc.kbeg = kbeg;
     pc.kcut = kcut;
