@@ -1545,9 +1545,8 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
     // Lane k of the row loads the (m, l, scale) of unit c0 + k (and of
     // c0 + k + LPR ... when a round has more units than the row has lanes)
     // and computes its weight; the weights reach the other lanes by
-    // shuffles. The partial rows are loaded unconditionally (units past the
-    // last re-read it, with weight 0), so that all of them are in flight
-    // together.
+    // shuffles. The partial rows of the round's pieces that hold keys are
+    // requested together; the others count as zero rows with weight 0.
     float4 mine[MPL];
     bool valid[MPL];
 #pragma unroll
@@ -1560,12 +1559,14 @@ __global__ __launch_bounds__(kThreadsCombine) void attn_combine_kernel(AttnParam
     Raw v[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      const int kk = held(c0 + k) ? c0 + k : nch - 1;
-      const int64_t off = row_elem + kk * ustride;
-      if constexpr (Q16)
-        v[k] = *reinterpret_cast<const uint4*>(reinterpret_cast<const int16_t*>(p.part_o) + off);
-      else
-        v[k] = *reinterpret_cast<const float4*>(p.part_o + off);
+      const int64_t off = row_elem + (c0 + k) * ustride;
+      v[k] = Raw{};
+      if (held(c0 + k)) {
+        if constexpr (Q16)
+          v[k] = *reinterpret_cast<const uint4*>(reinterpret_cast<const int16_t*>(p.part_o) + off);
+        else
+          v[k] = *reinterpret_cast<const float4*>(p.part_o + off);
+      }
     }
     float m = -INFINITY;
 #pragma unroll
