@@ -380,6 +380,50 @@ def test_greedy_status_codes():
     check_greedy(got, want)
 
 
+def _greedy_shapes(seed):
+    # Same launch shape for every seed; the planted argmax paths differ.
+    return make_custom(seed, 6, 2, 1, 64, 40000, "bf16", [4] * 6, 24, plant_depth=4,
+                       padded_rows=[2])
+
+
+def test_greedy_workspace_reuse():
+    # One workspace of random bytes for calls of two launch shapes in turn:
+    # every call's partials are its own.
+    ws = torch.randint(0, 256, (1 << 22,), dtype=torch.uint8, device=torch.device("cuda:0"))
+    a, b = _greedy_shapes(41), _greedy_shapes(42)
+    other = make_custom(43, 3, 2, 1, 64, 100000, "bf16", [4] * 3, 40, plant_depth=3)
+    for w in (a, b, other, a, b, a):
+        d = upload(w)
+        res = tv.accept_greedy(d["logits"], d["tokens"], d["parent"], d["n_nodes"], workspace=ws)
+        torch.cuda.synchronize()
+        got = tuple(r.cpu().numpy() for r in res)
+        check_greedy(got, oracle.accept_greedy(w.logits, w.tokens, w.parent, w.n_nodes))
+
+
+def test_greedy_graph_replays_with_new_logits():
+    # Replays of one captured call, with new inputs copied in before each.
+    ws = [_greedy_shapes(50 + r) for r in range(4)]
+    d = upload(ws[0])
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g):
+            acc = tv.accept_greedy(d["logits"], d["tokens"], d["parent"], d["n_nodes"])
+    torch.cuda.current_stream().wait_stream(st)
+    for rep in range(8):
+        w = ws[rep % 4]
+        e = upload(w)
+        for key in ("logits", "tokens", "parent", "n_nodes"):
+            d[key].copy_(e[key])
+        acc[0].fill_(-5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = tuple(x.cpu().numpy() for x in acc)
+        check_greedy(got, oracle.accept_greedy(w.logits, w.tokens, w.parent, w.n_nodes))
+
+
 # -------------------------------------------------------------- sampling ---
 
 def test_sample_config_c5():
