@@ -336,9 +336,12 @@ __device__ int total_units(const P& p, int len0, int K) {
 // (at least kMinUnit) that cuts the launch into at most nw units, so that a
 // single pass of the nw workgroups covers it with the least work per unit;
 // else (more pairs than workgroups, or no workspace for partials) one unit
-// per pair: L + kTreeExtra <= K for every sequence.
+// per pair: L + kTreeExtra <= K for every sequence. `stream_k` tells whether
+// the balanced partition leaves more units than workgroups (the stream-K
+// line then takes over); the search has counted them already.
 template <class P>
-__device__ int choose_unit(const P& p, int len0) {
+__device__ int choose_unit(const P& p, int len0, bool& stream_k) {
+  stream_k = false;
   if (p.kunit > 0) return p.kunit;
   // Sequences in lanes (the first 64 from len0, later blocks from memory),
   // reduced across the wave.
@@ -358,13 +361,19 @@ __device__ int choose_unit(const P& p, int len0) {
   const int64_t pair_keys = static_cast<int64_t>(keys) * p.Hkv * p.RG;
   int lo = static_cast<int>(div64_fast(pair_keys + p.nw - 1, p.nw));
   lo = max(kMinUnit, (lo + 63) / 64 * 64);
-  if (lo >= hi) return hi;
+  if (lo >= hi) {
+    stream_k = total_units(p, len0, hi) > p.nw;
+    return hi;
+  }
   // Each candidate's unit count is one wave reduction over the sequences'
   // lanes (no memory for the first 64): a few steps of 64 from the bound,
   // then a bisection.
   for (int step = 0; step < 4 && lo < hi; ++step, lo += 64)
     if (total_units(p, len0, lo) <= p.nw) return lo;
-  if (total_units(p, len0, hi) > p.nw) return hi;
+  if (total_units(p, len0, hi) > p.nw) {
+    stream_k = true;
+    return hi;
+  }
   int bad = lo - 64;  // units(bad) > nw >= units(hi)
   int good = hi;
   while (good - bad > 64) {
@@ -802,9 +811,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int n0, s0, st0;
   const int len0 = lane_len(p, n0, s0, st0);
-  const int K = choose_unit(p, len0);
-  const bool stream_k =
-      p.kunit == 0 && p.part_o != nullptr && total_units(p, len0, K) > p.nw;
+  bool stream_k;
+  const int K = choose_unit(p, len0, stream_k);
   SkLine sk{0, 0, 0, 0};
   if (stream_k) sk = sk_line(p, len0);
   if (p.sched && blockIdx.x == 0 && wave == 0) write_sched(p, len0, K, sk, stream_k);
@@ -878,13 +886,13 @@ __global__ __launch_bounds__(kThreads) void attn_split_bf16_kernel(AttnParamsT<P
       lds_copy16(vbase, row + static_cast<uint32_t>(ld_vch * 16), dV + lds_off);
     }
   };
-  // Tile t becomes readable: wait for all of this thread's copies, publish
-  // with a barrier, then reuse the stage of tile t - 2, which every wave has
-  // finished reading, for tile t + 2. The wait is vmcnt(0), not a partial
-  // count that would leave tile t + 1 in flight: HBM->LDS copies are not
-  // relied on to complete in issue order (a partial count let a tile be
-  // read before all of it had landed). Tile t + 1 was issued a tile earlier,
-  // so it has usually landed by then anyway.
+  // Max-only pass (rare): tile t becomes readable once every copy this
+  // thread has in flight has landed (vmcnt(0), right whatever else is
+  // outstanding); publish with a barrier, then reuse the stage of tile
+  // t - 2, which every wave has finished reading, for tile t + 2. Tile t + 1
+  // was issued a tile earlier, so it has usually landed by then anyway. The
+  // main pass below counts its own copies instead and keeps tile t + 1 in
+  // flight.
   auto enter_tile = [&](int t) __attribute__((always_inline)) {
     TV_WAIT_VMCNT(0);
     lds_barrier();
@@ -1289,9 +1297,8 @@ __global__ __launch_bounds__(kThreadsF32) void attn_split_f32_kernel(AttnParamsT
   const int tid = threadIdx.x;
   int n0, s0, st0;
   const int len0 = lane_len(p, n0, s0, st0);
-  const int K = choose_unit(p, len0);
-  const bool stream_k =
-      p.kunit == 0 && p.part_o != nullptr && total_units(p, len0, K) > p.nw;
+  bool stream_k;
+  const int K = choose_unit(p, len0, stream_k);
   SkLine sk{0, 0, 0, 0};
   if (stream_k) sk = sk_line(p, len0);
   if (p.sched && blockIdx.x == 0 && tid < tv::kWave) write_sched(p, len0, K, sk, stream_k);
