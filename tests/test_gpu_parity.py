@@ -820,6 +820,62 @@ def test_attention_packed_bitwise_equals_padded(name, chunk, parts):
     assert np.abs(l[live] - l_ref[live]).max() <= 1e-4
 
 
+def _random_case(seed, bmax, ctxmax, ndmax):
+    """One seeded draw over the attention call's parameters: head_dim,
+    input type, group size, batch, ragged contexts (some empty), tree size
+    and shape, padded sequences, probability parts, chunking and the packed
+    layout."""
+    rng = np.random.default_rng(seed)
+    D = int(rng.choice([64, 128]))
+    dtype = "f32" if rng.random() < 0.15 else "bf16"
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.integers(1, 8))
+    B = int(rng.integers(1, bmax))
+    ctx = [0 if rng.random() < 0.1 else int(rng.integers(1, ctxmax)) for _ in range(B)]
+    nd = int(rng.integers(0, ndmax))
+    tree = str(rng.choice(["random", "random", "chain", "star"]))
+    padded = [b for b in range(B) if rng.random() < 0.15]
+    parts = int(rng.choice([1, 2, 3, 3])) if dtype == "bf16" else 3
+    chunk = int(rng.choice([0, 0, 0, 64, 128, 512]))
+    packed = bool(rng.random() < 0.3)
+    w = make_custom(seed, B, Hkv * G, Hkv, D, 64, dtype, ctx, nd, tree=tree, padded_rows=padded,
+                    trie_tokens=False)
+    return w, parts, chunk, packed
+
+
+@pytest.mark.parametrize("seed,bmax,ctxmax,ndmax",
+                         [(7000 + i, 7, 2500, 48) for i in range(40)] +
+                         [(9000 + i, 90, 1500, 128) for i in range(12)])
+def test_attention_random_cases(seed, bmax, ctxmax, ndmax):
+    # Seeded random draws over the whole parameter space, up to 89 sequences
+    # (more pairs than workgroups: the stream-K partition) and 128-row trees,
+    # each against the oracle at the bound of its probability parts.
+    w, parts, chunk, packed = _random_case(seed, bmax, ctxmax, ndmax)
+    d = upload(w)
+    mask = tv.build_tree_mask(d["parent"], d["n_nodes"])[0]
+    atol = fast_mode_bound(w) if parts == 1 else ATOL_OUT
+    if not packed:
+        got = run_attention(w, d, mask, chunk_keys=chunk, parts=parts)
+        check_attention(w, got, oracle_attention(w), atol_out=atol,
+                        label="seed %d parts %d chunk %d" % (seed, parts, chunk))
+        return
+    qp, start, rows = _packed_layout(w, 3)
+    o, l, st = _run_packed(w, d, mask, qp, start, chunk=chunk, parts=parts)
+    o_ref, l_ref, st_ref = oracle.tree_attention_packed(
+        qp, w.k, w.v, w.dtype, w.ctx_len, w.n_nodes, w.parent, start, w.T, w.scale,
+        max_ctx=w.max_ctx, kv_capacity=w.kv_capacity)
+    assert np.array_equal(st, st_ref)
+    live = ~np.isnan(l_ref)
+    assert np.all(o[~live] == 12345.0) and np.all(l[~live] == 12345.0)
+    fin = live & np.isfinite(l_ref)
+    assert np.array_equal(l[live & ~fin], l_ref[live & ~fin])
+    err_o = float(np.abs(o[live] - o_ref[live]).max(initial=0.0))
+    err_l = float(np.abs(l[fin] - l_ref[fin]).max(initial=0.0))
+    print("packed seed %d parts %d chunk %d: max|out - oracle| = %.3g, max|lse - oracle| = %.3g"
+          % (seed, parts, chunk, err_o, err_l))
+    assert err_o <= atol and err_l <= 1e-4
+
+
 @pytest.mark.parametrize("dtype,D,chunk", [("f32", 64, 128), ("bf16", 64, 0), ("bf16", 128, 64)])
 def test_attention_packed_ragged_and_statuses(dtype, D, chunk):
     # Ragged trees and contexts, G = 3; one sequence over its context bound
