@@ -474,6 +474,38 @@ def test_sample_vocab_sizes(V):
         assert check_sample(w, got, want) <= 1
 
 
+@pytest.mark.parametrize("seed", range(11000, 11024))
+def test_sample_random_cases(seed):
+    # Seeded draws: batch, tree size and shape, vocabularies on both sides of
+    # the one-round-trip limit, temperature, padded sequences, and draft rows
+    # with zeroed entries or all their mass on the drafted token.
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 13))
+    nd = int(rng.integers(0, 60))
+    V = int(rng.choice([int(rng.integers(1, 50)), int(rng.integers(50, 33000)),
+                        int(rng.integers(32700, 70000))]))
+    tau = float(rng.uniform(0.3, 2.0))
+    tree = str(rng.choice(["random", "random", "star", "chain"]))
+    padded = [b for b in range(B) if rng.random() < 0.15]
+    w = make_custom(seed, B, 2, 1, 64, V, "bf16", [4] * B, nd, mode="sample", tree=tree,
+                    temperature=tau, padded_rows=padded)
+    for b in range(B):
+        for c in range(1, nd + 1):
+            r = rng.random()
+            if r < 0.1:
+                z = int(rng.integers(0, V))
+                if z != w.tokens[b, c]:
+                    w.qdraft[b, c, z] = 0.0
+            elif r < 0.15:
+                w.qdraft[b, c] = 0.0
+                w.qdraft[b, c, w.tokens[b, c]] = 1.0
+    d = upload(w)
+    got = run_sample(w, d)
+    want = oracle.accept_sample(w.logits, w.temperature, w.qdraft, w.u, w.tokens, w.parent,
+                                w.n_nodes)
+    assert check_sample(w, got, want) <= 1
+
+
 def test_sample_unnormalised_draft_keeps_residual():
     """A draft row that dominates the residual everywhere (q = 2 r) leaves a
     zero residual sum, so r is kept; later siblings are tested against it."""
