@@ -65,6 +65,15 @@ def test_trie_siblings_distinct_and_planting():
         assert all(w.parent[b, path[j]] == path[j - 1] for j in range(1, 5))
 
 
+def test_trie_needs_a_token_per_sibling():
+    # 20 children of the root and 19 tokens: no trie exists; the generator
+    # says so instead of drawing forever.
+    with pytest.raises(ValueError, match="more children than vocabulary"):
+        make_custom(7, 1, 2, 1, 16, 19, "bf16", [4], 20, tree="star")
+    w = make_custom(7, 1, 2, 1, 16, 20, "bf16", [4], 20, tree="star")
+    assert sorted(w.tokens[0, 1:].tolist()) == list(range(20))
+
+
 def test_bushy_tree_limits():
     w = make_custom(6, 1, 4, 2, 16, 100, "bf16", [16], 64, max_depth=12, max_children=6)
     par = w.parent[0]

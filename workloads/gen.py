@@ -136,12 +136,15 @@ def _children(parent: np.ndarray, node: int) -> np.ndarray:
 
 
 def _draw_trie_tokens(rng, parent, V):
-    """Tokens with distinct values among siblings (a trie)."""
+    """Tokens with distinct values among siblings (a trie). A node with more
+    children than vocabulary entries has no such tokens: ValueError."""
     T = parent.shape[0]
     tok = np.empty(T, dtype=np.int32)
     tok[0] = rng.integers(V)
     for i in range(1, T):
         taken = {int(tok[c]) for c in range(1, i) if parent[c] == parent[i]}
+        if len(taken) >= V:
+            raise ValueError("a node has more children than vocabulary entries: no trie tokens")
         while True:
             t = int(rng.integers(V))
             if t not in taken:
