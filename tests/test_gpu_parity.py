@@ -660,6 +660,36 @@ def test_linear_batch_invariant_across_tilings():
                               full_s[lo:hi]), (lo, hi)
 
 
+@pytest.mark.parametrize("seed", range(15000, 15016))
+def test_linear_rows_random_shapes(seed):
+    # Seeded shapes (any row count up to 300, K and N any multiple of 64):
+    # the oracle bound, the bits of a random row subset, and the fused SwiGLU
+    # against the rounded product of the two projections.
+    rng = np.random.default_rng(seed)
+    M = int(rng.choice([int(rng.integers(1, 20)), int(rng.integers(20, 300))]))
+    K = 64 * int(rng.integers(1, 65))
+    N = 64 * int(rng.integers(1, 130))
+    x, xb = _bf16_dev(rng.normal(size=(M, K)))
+    w, wb = _bf16_dev(rng.normal(size=(N, K)) / np.sqrt(K))
+    y = tv.linear_rows(x, w)
+    torch.cuda.synchronize()
+    yg = y.float().cpu().numpy().astype(np.float64)
+    exact, _ = oracle.linear_rows(xb, wb)
+    tol = 2.0 ** -8 * np.abs(exact) + _linear_bound(xb, wb, K) + 1e-30
+    assert (np.abs(yg - exact) <= tol).all(), np.abs(yg - exact).max()
+    lo = int(rng.integers(0, M))
+    hi = int(rng.integers(lo + 1, M + 1))
+    part = tv.linear_rows(x[lo:hi].contiguous(), w).cpu().view(torch.int16).numpy()
+    assert np.array_equal(part, y.cpu().view(torch.int16).numpy()[lo:hi]), (lo, hi)
+    if rng.random() < 0.5:
+        wu, _ = _bf16_dev(rng.normal(size=(N, K)) / np.sqrt(K))
+        ys = tv.linear_swiglu_rows(x, w, wu).float().cpu().numpy().astype(np.float64)
+        u = tv.linear_rows(x, wu).float().cpu().numpy().astype(np.float64)
+        ref = oracle.round_bf16(oracle.silu(yg) * u)
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+        assert (np.abs(ys - ref) <= ulp).all()
+
+
 @pytest.mark.parametrize("M,K,N", [(9, 64, 64), (100, 448, 320), (264, 3584, 1024),
                                    (264, 3584, 18944)])
 def test_linear_swiglu_rows(M, K, N):
