@@ -756,6 +756,36 @@ def test_commit_after_greedy_acceptance(name):
     assert not st_c.any()
 
 
+@pytest.mark.parametrize("seed", range(17000, 17012))
+def test_commit_random_paths(seed):
+    # Seeded trees, contexts and element types; each live sequence accepts the
+    # root-to-node path of a random node (any depth, the root alone included).
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 9))
+    dtype = "f32" if rng.random() < 0.3 else "bf16"
+    D = int(rng.choice([64, 128]))
+    ctx = [int(rng.integers(0, 700)) for _ in range(B)]
+    nd = int(rng.integers(0, 100))
+    w = make_custom(seed, B, 4, 2, D, 50, dtype, ctx, nd, trie_tokens=False,
+                    padded_rows=[b for b in range(B) if rng.random() < 0.15])
+    T = w.T
+    path = np.full((B, T), -1, np.int32)
+    acc = np.zeros(B, np.int32)
+    for b in range(B):
+        n = int(w.n_nodes[b])
+        if n == 0:
+            continue
+        node = int(rng.integers(0, n))
+        chain = [node]
+        while chain[-1] != 0:
+            chain.append(int(w.parent[b, chain[-1]]))
+        chain = chain[::-1]
+        path[b, :len(chain)] = chain
+        acc[b] = len(chain) - 1
+    st = _commit_case(w, w.k, w.v, acc, path)
+    assert not st.any()
+
+
 def test_commit_layers_nhd_fp32_and_long_paths():
     # Three layers of an fp32 cache laid out [layer][B][capacity][Hkv][D]
     # (NHD) and seen through strides; a chain of 128 rows whose path skips
