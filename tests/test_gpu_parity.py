@@ -589,6 +589,34 @@ def test_attention_draft_blocks(mode, chunk):
     check_attention(w, got, want, label="block mode %d" % mode)
 
 
+@pytest.mark.parametrize("seed", range(19000, 19012))
+def test_attention_draft_blocks_random(seed):
+    # Seeded draft blocks: block length, batch, ragged contexts (some empty),
+    # head grouping, head_dim, causal or bidirectional, probability parts and
+    # chunking, against the oracle's masked attention.
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 7))
+    nd = int(rng.integers(0, 40))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.integers(1, 8))
+    D = int(rng.choice([64, 128]))
+    ctx = [0 if rng.random() < 0.2 else int(rng.integers(1, 3000)) for _ in range(B)]
+    mode = int(rng.integers(0, 2))
+    parts = int(rng.choice([2, 3]))
+    chunk = int(rng.choice([0, 0, 64, 256]))
+    w = make_custom(seed, B, Hkv * G, Hkv, D, 50, "bf16", ctx, nd, tree="chain",
+                    trie_tokens=False, padded_rows=[b for b in range(B) if rng.random() < 0.15])
+    d = upload(w)
+    mask, pos, st = tv.build_block_mask(d["n_nodes"], w.T, mode)
+    torch.cuda.synchronize()
+    m_host = mask.cpu().numpy().view(np.uint32)
+    got = run_attention(w, d, mask, chunk_keys=chunk, parts=parts)
+    want = oracle.masked_attention(w.q, w.k, w.v, w.dtype, w.ctx_len, w.n_nodes, m_host, w.scale,
+                                   max_ctx=w.max_ctx, kv_capacity=w.kv_capacity)
+    check_attention(w, got, want, label="block seed %d mode %d parts %d chunk %d"
+                    % (seed, mode, parts, chunk))
+
+
 # ------------------------------------------------------ few-row projections ---
 
 def _bf16_dev(a):
